@@ -1,0 +1,221 @@
+"""ctypes wrapper around the C oracle (``qmv_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: only the test suite, the smoke check and the
+bench's CPU-baseline leg may import this module.  It knows nothing of the
+HIP library and never imports it.
+
+Every function takes and returns host numpy arrays.  The arithmetic lives in
+the C file; this module only marshals buffers.  Rules and citations are in
+the C file's comments (Legacy-ISA ML Inference Runtime -- Design Spec,
+sections 4, 5 and 7).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+QK = 32
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qmv_oracle.c")
+_LIB = os.path.join(_HERE, "libqmv_oracle.so")
+
+# -ffp-contract=off: no multiply-add is ever fused, each float op rounds once.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-fno-tree-vectorize"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into a shared object next to its source."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Lib:
+    """Typed handle on one build of the oracle shared object."""
+
+    def __init__(self, path: str):
+        self.path = path
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        sigs = {
+            "orc_quantize_q8": [P, i64, P, P],
+            "orc_quantize_q4": [P, i64, P, P],
+            "orc_block_sums_q8": [P, i32, P, i32, i32, P],
+            "orc_block_sums_q4": [P, i32, P, i32, i32, P],
+            "orc_matvec_q8": [P, P, P, i32, P, P, i32, i32],
+            "orc_matvec_q4": [P, P, P, i32, P, P, i32, i32],
+            "orc_gemm_q8": [P, P, P, i32, i32, P, P, i32, i32, i32],
+            "orc_gemm_q4": [P, P, P, i32, i32, P, P, i32, i32, i32],
+            "orc_tol_abs": [ctypes.c_int, P, P, i32, P, P, i32, i32, P],
+        }
+        for name, args in sigs.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = None
+            setattr(self, name, f)
+
+
+_lib = None
+_override = None
+
+
+def lib() -> _Lib:
+    """The oracle build in use (the committed source, unless a test has
+    swapped in another build with use_build())."""
+    global _lib
+    if _override is not None:
+        return _override
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _Lib(_LIB)
+    return _lib
+
+
+def build_variant(src_text: str, out_path: str) -> str:
+    """Compile an edited copy of the oracle source (used by the tests that
+    plant a mistake in the oracle to show the pins catch it)."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", *CFLAGS, src, "-o", out_path, "-lm"])
+    return out_path
+
+
+class use_build:
+    """Context manager: route every oracle call through another build."""
+
+    def __init__(self, path: str):
+        self.handle = _Lib(path)
+
+    def __enter__(self):
+        global _override
+        self.prev = _override
+        _override = self.handle
+        return self.handle
+
+    def __exit__(self, *exc):
+        global _override
+        _override = self.prev
+        return False
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def quantize_q8(x):
+    """Q8_0 quantization of a float32 array whose size is a multiple of 32.
+    Returns (q int8 of x.shape, d float32 of shape x.shape[:-1] + (n/32,))."""
+    x = _f32(x)
+    assert x.size % QK == 0 and x.shape[-1] % QK == 0
+    q = np.empty(x.shape, np.int8)
+    d = np.empty(x.shape[:-1] + (x.shape[-1] // QK,), np.float32)
+    lib().orc_quantize_q8(_p(x), x.size, _p(q), _p(d))
+    return q, d
+
+
+def quantize_q4(x):
+    """Q4_0 quantization of a float32 array (last dim multiple of 32).
+    Returns (q uint8 of shape [..., n/2], d float32 [..., n/32])."""
+    x = _f32(x)
+    assert x.shape[-1] % QK == 0
+    q = np.empty(x.shape[:-1] + (x.shape[-1] // 2,), np.uint8)
+    d = np.empty(x.shape[:-1] + (x.shape[-1] // QK,), np.float32)
+    lib().orc_quantize_q4(_p(x), x.size, _p(q), _p(d))
+    return q, d
+
+
+def _check_w(qtype, wq, wd):
+    rows = wd.shape[0]
+    nb = wd.shape[1]
+    cols = nb * QK
+    if qtype == 8:
+        assert wq.dtype == np.int8 and wq.shape == (rows, cols)
+    elif qtype == 4:
+        assert wq.dtype == np.uint8 and wq.shape == (rows, cols // 2)
+    else:
+        raise ValueError("qtype must be 4 or 8")
+    assert wd.dtype == np.float32
+    return rows, cols
+
+
+def block_sums(qtype, wq, xq, r0=None, r1=None):
+    """int32 block sums sumi[r - r0, b] for rows [r0, r1)."""
+    wq = np.ascontiguousarray(wq)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    rows = wq.shape[0]
+    cols = xq.shape[-1]
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    out = np.zeros((r1 - r0, cols // QK), np.int32)
+    f = lib().orc_block_sums_q8 if qtype == 8 else lib().orc_block_sums_q4
+    f(_p(wq), cols, _p(xq), r0, r1, _p(out))
+    return out
+
+
+def matvec(qtype, wq, wd, xq, xd, r0=None, r1=None, y=None):
+    """y[r] for r in [r0, r1); other entries of y are left as given
+    (zeros by default)."""
+    wq = np.ascontiguousarray(wq)
+    wd = _f32(wd)
+    rows, cols = _check_w(qtype, wq, wd)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    xd = _f32(xd).reshape(-1)
+    assert xq.size == cols and xd.size == cols // QK
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    if y is None:
+        y = np.zeros(rows, np.float32)
+    f = lib().orc_matvec_q8 if qtype == 8 else lib().orc_matvec_q4
+    f(_p(y), _p(wq), _p(wd), cols, _p(xq), _p(xd), r0, r1)
+    return y
+
+
+def gemm(qtype, wq, wd, xq, xd, r0=None, r1=None, Y=None):
+    """Y[m, r] for every row m of X and r in [r0, r1)."""
+    wq = np.ascontiguousarray(wq)
+    wd = _f32(wd)
+    rows, cols = _check_w(qtype, wq, wd)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    xd = _f32(xd)
+    m = xq.shape[0]
+    assert xq.shape == (m, cols) and xd.shape == (m, cols // QK)
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    if Y is None:
+        Y = np.zeros((m, rows), np.float32)
+    f = lib().orc_gemm_q8 if qtype == 8 else lib().orc_gemm_q4
+    f(_p(Y), _p(wq), _p(wd), rows, cols, _p(xq), _p(xd), m, r0, r1)
+    return Y
+
+
+def tol_abs(qtype, wq, wd, xq, xd, r0=None, r1=None):
+    """A(r) = sum_b |sumi * dw * dx| in float64, for r in [r0, r1)."""
+    wq = np.ascontiguousarray(wq)
+    wd = _f32(wd)
+    rows, cols = _check_w(qtype, wq, wd)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    xd = _f32(xd).reshape(-1)
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    out = np.zeros(r1 - r0, np.float64)
+    lib().orc_tol_abs(qtype, _p(wq), _p(wd), cols, _p(xq), _p(xd), r0, r1, _p(out))
+    return out
+
+
+def tolerance(qtype, wq, wd, xq, xd, r0=None, r1=None):
+    """Allowed |y - y_ref| per row: 1e-5 * A(r) + 1e-6."""
+    return 1e-5 * tol_abs(qtype, wq, wd, xq, xd, r0, r1) + 1e-6

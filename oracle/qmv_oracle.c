@@ -1,0 +1,269 @@
+/*
+ * qmv_oracle.c -- plain, slow, obviously-correct CPU oracle for the
+ * block-quantized weight x activation product of LLM decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the bench's CPU
+ * baseline leg use it.  It shares no source, header, table or helper with
+ * the HIP library; the only thing the two have in common is the byte layout
+ * of the formats, which both take from the design spec below.
+ *
+ * Source of every rule here: "Legacy-ISA ML Inference Runtime -- Design
+ * Spec" (jonpark0.github.io/krafla), sections 4 (Quantization Formats),
+ * 5 (Kernel Interface) and 7 (Testing, Verification, Benchmarks).
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (no FMA is ever
+ * formed; every float operation rounds to nearest-even in binary32).
+ *
+ * Parity status per function (what pins it is listed in the test suite):
+ *   orc_quantize_q8     pinned (closed forms, detector vectors, invariants,
+ *                       textbook rounding at unit scale, round-trip bound)
+ *   orc_quantize_q4     pinned (nibble layout, closed forms, round-trip)
+ *   orc_block_sums_*    pinned (closed forms, int64 brute force)
+ *   orc_matvec_*        pinned (fp64 brute force within the error bound,
+ *                       exact sums at unit scale, sign/power-of-two/row
+ *                       permutation invariants); its individual fp32
+ *                       roundings are defined only by this order of
+ *                       operations: "parity unpinned" beyond the bound.
+ *   orc_gemm_*          pinned (M=1 slice and per-row equality with matvec)
+ *   orc_tol_abs         pinned (closed forms)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define QK 32 /* block length, spec section 4 */
+
+/* ------------------------------------------------------------------------
+ * Q8_0 quantization (spec section 4 "Q8 quantization" bullet, and the
+ * section 5 rounding rule).  Per block of 32 consecutive values:
+ *   amax = max |x_i|,   d = amax / 127,   id = 127 / amax  (0 when amax=0),
+ *   q_i  = trunc(x_i * id + copysign(0.5, x_i))   (half away from zero),
+ *   q_i clamped to [-127, 127];  amax = 0 gives d = 0 and every q_i = 0.
+ * Each of the two float operations on x_i rounds separately (contraction
+ * is off for this translation unit).  n must be a multiple of 32.
+ * ---------------------------------------------------------------------- */
+void orc_quantize_q8(const float *x, int64_t n, int8_t *q, float *d)
+{
+    for (int64_t b = 0; b < n / QK; ++b) {
+        const float *xb = x + b * QK;
+        float amax = 0.0f;
+        for (int i = 0; i < QK; ++i) {
+            float a = fabsf(xb[i]);
+            if (a > amax)
+                amax = a;
+        }
+        float db = amax / 127.0f;
+        float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+        for (int i = 0; i < QK; ++i) {
+            float v = xb[i] * id;
+            float t = v + copysignf(0.5f, xb[i]);
+            int qi = (int)truncf(t);
+            if (qi > 127)
+                qi = 127;
+            if (qi < -127)
+                qi = -127;
+            q[b * QK + i] = (int8_t)qi;
+        }
+        d[b] = db;
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Q4_0 quantization of weights.  The spec fixes only the storage (section
+ * 4 table: 16 bytes per block, byte j holds element j in its low nibble and
+ * element j+16 in its high nibble, value = nibble - 8 in [-8, 7]) and that
+ * quantization is symmetric.  The plain symmetric reading used here mirrors
+ * the Q8_0 rule with 7 in place of 127:
+ *   d = amax / 7,  id = 7 / amax (0 when amax = 0),
+ *   v_i = clamp(trunc(x_i * id + copysign(0.5, x_i)), -8, 7),
+ *   nibble_i = v_i + 8.
+ * q receives n/2 bytes, d receives n/32 scales.
+ * ---------------------------------------------------------------------- */
+void orc_quantize_q4(const float *x, int64_t n, uint8_t *q, float *d)
+{
+    for (int64_t b = 0; b < n / QK; ++b) {
+        const float *xb = x + b * QK;
+        float amax = 0.0f;
+        for (int i = 0; i < QK; ++i) {
+            float a = fabsf(xb[i]);
+            if (a > amax)
+                amax = a;
+        }
+        float db = amax / 7.0f;
+        float id = (amax != 0.0f) ? 7.0f / amax : 0.0f;
+        int nib[QK];
+        for (int i = 0; i < QK; ++i) {
+            float v = xb[i] * id;
+            float t = v + copysignf(0.5f, xb[i]);
+            int qi = (int)truncf(t);
+            if (qi > 7)
+                qi = 7;
+            if (qi < -8)
+                qi = -8;
+            nib[i] = qi + 8;
+        }
+        for (int j = 0; j < QK / 2; ++j)
+            q[b * (QK / 2) + j] = (uint8_t)(nib[j] | (nib[j + QK / 2] << 4));
+        d[b] = db;
+    }
+}
+
+/* Weight element i (0..31) of a Q4_0 block, as a signed value (section 4
+ * table and the section 5 note on Q4 kernels: mask 0x0F / shift 4, then
+ * subtract 8). */
+static int q4_elem(const uint8_t *blk, int i)
+{
+    int nib = (i < QK / 2) ? (blk[i] & 0x0F) : (blk[i - QK / 2] >> 4);
+    return nib - 8;
+}
+
+/* ------------------------------------------------------------------------
+ * Integer block dot products (section 4 "Integer dot per block"):
+ *   sumi(r, b) = sum over i < 32 of w(r, 32b+i) * qx(32b+i), in int32.
+ * out has (r1 - r0) * nb entries, row-major, nb = cols / 32.
+ * ---------------------------------------------------------------------- */
+void orc_block_sums_q8(const int8_t *wq, int32_t cols, const int8_t *xq,
+                       int32_t r0, int32_t r1, int32_t *out)
+{
+    int32_t nb = cols / QK;
+    for (int32_t r = r0; r < r1; ++r)
+        for (int32_t b = 0; b < nb; ++b) {
+            const int8_t *w = wq + (int64_t)r * cols + (int64_t)b * QK;
+            const int8_t *xv = xq + (int64_t)b * QK;
+            int32_t s = 0;
+            for (int i = 0; i < QK; ++i)
+                s += (int32_t)w[i] * (int32_t)xv[i];
+            out[(int64_t)(r - r0) * nb + b] = s;
+        }
+}
+
+void orc_block_sums_q4(const uint8_t *wq, int32_t cols, const int8_t *xq,
+                       int32_t r0, int32_t r1, int32_t *out)
+{
+    int32_t nb = cols / QK;
+    for (int32_t r = r0; r < r1; ++r)
+        for (int32_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = wq + (int64_t)r * (cols / 2) + (int64_t)b * (QK / 2);
+            const int8_t *xv = xq + (int64_t)b * QK;
+            int32_t s = 0;
+            for (int i = 0; i < QK; ++i)
+                s += (int32_t)q4_elem(blk, i) * (int32_t)xv[i];
+            out[(int64_t)(r - r0) * nb + b] = s;
+        }
+}
+
+/* ------------------------------------------------------------------------
+ * Matrix-vector product (section 5 kernel interface: rows [r0, r1) of W
+ * times the Q8_0 activation; section 4 accumulation rule):
+ *   s = 0;  for each block b in ascending order:
+ *       s = s + ((float)sumi * dw[r, b]) * dx[b]
+ *   y[r] = s            (y is indexed by the absolute row r)
+ * Rows outside [r0, r1) are not written.
+ * ---------------------------------------------------------------------- */
+static float row_q8(const int8_t *wq, const float *wd, int32_t cols,
+                    const int8_t *xq, const float *xd, int32_t r)
+{
+    int32_t nb = cols / QK;
+    float s = 0.0f;
+    for (int32_t b = 0; b < nb; ++b) {
+        const int8_t *w = wq + (int64_t)r * cols + (int64_t)b * QK;
+        const int8_t *xv = xq + (int64_t)b * QK;
+        int32_t sumi = 0;
+        for (int i = 0; i < QK; ++i)
+            sumi += (int32_t)w[i] * (int32_t)xv[i];
+        float t = (float)sumi * wd[(int64_t)r * nb + b];
+        t = t * xd[b];
+        s = s + t;
+    }
+    return s;
+}
+
+static float row_q4(const uint8_t *wq, const float *wd, int32_t cols,
+                    const int8_t *xq, const float *xd, int32_t r)
+{
+    int32_t nb = cols / QK;
+    float s = 0.0f;
+    for (int32_t b = 0; b < nb; ++b) {
+        const uint8_t *blk = wq + (int64_t)r * (cols / 2) + (int64_t)b * (QK / 2);
+        const int8_t *xv = xq + (int64_t)b * QK;
+        int32_t sumi = 0;
+        for (int i = 0; i < QK; ++i)
+            sumi += (int32_t)q4_elem(blk, i) * (int32_t)xv[i];
+        float t = (float)sumi * wd[(int64_t)r * nb + b];
+        t = t * xd[b];
+        s = s + t;
+    }
+    return s;
+}
+
+void orc_matvec_q8(float *y, const int8_t *wq, const float *wd, int32_t cols,
+                   const int8_t *xq, const float *xd, int32_t r0, int32_t r1)
+{
+    for (int32_t r = r0; r < r1; ++r)
+        y[r] = row_q8(wq, wd, cols, xq, xd, r);
+}
+
+void orc_matvec_q4(float *y, const uint8_t *wq, const float *wd, int32_t cols,
+                   const int8_t *xq, const float *xd, int32_t r0, int32_t r1)
+{
+    for (int32_t r = r0; r < r1; ++r)
+        y[r] = row_q4(wq, wd, cols, xq, xd, r);
+}
+
+/* ------------------------------------------------------------------------
+ * Several activation rows at once: X is M rows of Q8_0 (each row quantized
+ * on its own, cols/32 scales per row); Y[m * rows + r] is the matvec of row
+ * m of X, for r in [r0, r1).  The spec defines the single-row product only;
+ * this is that product applied to each row of X.
+ * ---------------------------------------------------------------------- */
+void orc_gemm_q8(float *Y, const int8_t *wq, const float *wd, int32_t rows,
+                 int32_t cols, const int8_t *xq, const float *xd, int32_t m,
+                 int32_t r0, int32_t r1)
+{
+    int32_t nb = cols / QK;
+    for (int32_t i = 0; i < m; ++i)
+        orc_matvec_q8(Y + (int64_t)i * rows, wq, wd, cols,
+                      xq + (int64_t)i * cols, xd + (int64_t)i * nb, r0, r1);
+}
+
+void orc_gemm_q4(float *Y, const uint8_t *wq, const float *wd, int32_t rows,
+                 int32_t cols, const int8_t *xq, const float *xd, int32_t m,
+                 int32_t r0, int32_t r1)
+{
+    int32_t nb = cols / QK;
+    for (int32_t i = 0; i < m; ++i)
+        orc_matvec_q4(Y + (int64_t)i * rows, wq, wd, cols,
+                      xq + (int64_t)i * cols, xd + (int64_t)i * nb, r0, r1);
+}
+
+/* ------------------------------------------------------------------------
+ * Tolerance aid: A(r) = sum over blocks of |sumi * dw * dx| in binary64,
+ * the scale against which an fp32 result of any summation order is judged
+ * (|y - y_ref| <= 1e-5 * A + 1e-6).  type is 8 (Q8_0) or 4 (Q4_0).
+ * out[r - r0] receives A(r).
+ * ---------------------------------------------------------------------- */
+void orc_tol_abs(int type, const void *wq, const float *wd, int32_t cols,
+                 const int8_t *xq, const float *xd, int32_t r0, int32_t r1,
+                 double *out)
+{
+    int32_t nb = cols / QK;
+    for (int32_t r = r0; r < r1; ++r) {
+        double a = 0.0;
+        for (int32_t b = 0; b < nb; ++b) {
+            const int8_t *xv = xq + (int64_t)b * QK;
+            int64_t sumi = 0;
+            if (type == 8) {
+                const int8_t *w = (const int8_t *)wq + (int64_t)r * cols + (int64_t)b * QK;
+                for (int i = 0; i < QK; ++i)
+                    sumi += (int64_t)w[i] * xv[i];
+            } else {
+                const uint8_t *blk = (const uint8_t *)wq + (int64_t)r * (cols / 2) + (int64_t)b * (QK / 2);
+                for (int i = 0; i < QK; ++i)
+                    sumi += (int64_t)q4_elem(blk, i) * xv[i];
+            }
+            a += fabs((double)sumi * (double)wd[(int64_t)r * nb + b] * (double)xd[b]);
+        }
+        out[r - r0] = a;
+    }
+}

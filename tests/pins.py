@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle against facts fixed by the design spec and by
+mathematics -- never against the oracle itself.
+
+Each check raises AssertionError when the oracle in use (oracle.oracle.lib(),
+which a test may swap for a build with a planted mistake) disagrees with:
+  * closed forms the spec states (zero block, the +-127 clamp, the nibble
+    layout, the largest block sum),
+  * textbook rounding (Python's decimal ROUND_HALF_UP, i.e. half away from
+    zero) where the spec's rule reduces to it exactly,
+  * detector vectors whose expected values are derived by hand,
+  * exact invariants (sign symmetry, powers of two, row permutations,
+    row sub-ranges),
+  * brute force: int64 block sums and float64 dequantized dot products
+    (numpy), with the spec's tolerance.
+
+Rules: "Legacy-ISA ML Inference Runtime -- Design Spec", section 4
+(Quantization Formats), section 5 (Kernel Interface, rounding bullet) and
+section 7 (Testing: test_kernels / test_quant).
+"""
+from __future__ import annotations
+
+import decimal
+import json
+import os
+
+import numpy as np
+
+from oracle import oracle as orc
+
+QK = 32
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32_from_bits(h) -> np.float32:
+    return np.array([int(h, 16) if isinstance(h, str) else h], np.uint32).view(np.float32)[0]
+
+
+def half_away(x: float) -> int:
+    """Textbook round-half-away-from-zero of the exact binary value x."""
+    return int(decimal.Decimal(float(x)).quantize(decimal.Decimal(1), rounding=decimal.ROUND_HALF_UP))
+
+
+# ---------------------------------------------------------------------------
+# Independent numpy readers of the storage layout (section 4 table).
+# ---------------------------------------------------------------------------
+
+def q4_values(q: np.ndarray) -> np.ndarray:
+    """[rows, K/2] uint8 -> [rows, K] int64 values nibble - 8, element j of a
+    block from the low nibble of byte j (j < 16), element j from the high
+    nibble of byte j - 16 (j >= 16)."""
+    rows = q.shape[0]
+    b = q.reshape(rows, -1, 16).astype(np.int64)
+    lo = b & 0x0F
+    hi = b >> 4
+    return (np.concatenate([lo, hi], axis=2) - 8).reshape(rows, -1)
+
+
+def w_values(qtype, q):
+    return q.astype(np.int64) if qtype == 8 else q4_values(q)
+
+
+def brute_matvec64(qtype, wq, wd, xq, xd):
+    """float64 sum over k of (w_k * dw) * (qx_k * dx): the dequantized dot."""
+    w = w_values(qtype, wq).astype(np.float64)
+    rows, k = w.shape
+    wdeq = (w.reshape(rows, k // QK, QK) * wd.astype(np.float64)[:, :, None]).reshape(rows, k)
+    xdeq = (xq.astype(np.float64).reshape(-1, QK) * xd.astype(np.float64).reshape(-1)[:, None]).reshape(-1)
+    return wdeq @ xdeq
+
+
+def brute_abs_terms64(qtype, wq, wd, xq, xd):
+    """float64 A(r) = sum_b |sumi * dw * dx| from int64 brute-force sums."""
+    w = w_values(qtype, wq)
+    rows, k = w.shape
+    s = (w.reshape(rows, k // QK, QK) * xq.astype(np.int64).reshape(1, k // QK, QK)).sum(axis=2)
+    return np.abs(s.astype(np.float64) * wd.astype(np.float64) * xd.astype(np.float64).reshape(1, -1)).sum(axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Q8_0 quantization pins
+# ---------------------------------------------------------------------------
+
+def check_q8_zero_block():
+    x = np.zeros(64, np.float32)
+    x[32:] = -0.0
+    q, d = orc.quantize_q8(x)
+    assert np.all(q == 0) and np.all(d == 0.0), "zero block must give d = 0 and q = 0"
+
+
+def check_q8_equal_block():
+    for c in (0.37, 1.0, 3.0e-3, 1234.5):
+        c32 = np.float32(c)
+        x = np.full(32, c32, np.float32)
+        q, d = orc.quantize_q8(x)
+        assert np.all(q == 127), "a block of equal positive values quantizes to 127"
+        assert d[0] == c32 / np.float32(127.0), "d = amax / 127 (IEEE binary32 division)"
+        q, d = orc.quantize_q8(-x)
+        assert np.all(q == -127) and d[0] == c32 / np.float32(127.0)
+
+
+def check_q8_clamp_and_range():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(32 * 512).astype(np.float32) * np.float32(3.0)
+    x[::97] *= np.float32(50.0)
+    q, d = orc.quantize_q8(x)
+    assert q.min() >= -127 and q.max() <= 127, "quants clamped to [-127, 127]"
+    # the element of largest magnitude in each block maps to +-127
+    xb = x.reshape(-1, QK)
+    qb = q.reshape(-1, QK)
+    i = np.argmax(np.abs(xb), axis=1)
+    top = qb[np.arange(len(i)), i]
+    assert np.all(np.abs(top) == 127), "amax element maps to +-127"
+    assert np.all(np.sign(top) == np.sign(xb[np.arange(len(i)), i]))
+
+
+def check_q8_unit_scale_textbook():
+    # amax = 127 makes id = 127/127 = 1 and d = 1 exactly, so q = trunc(x + copysign(0.5, x));
+    # for x on a 1/8 grid the addition is exact and this is textbook half-away rounding.
+    k = np.arange(-1016, 1017, dtype=np.int64)
+    vals = (k / 8.0).astype(np.float32)
+    vals = vals[np.abs(vals) <= 127]
+    pad = (-len(vals)) % 31
+    vals = np.concatenate([vals, np.zeros(pad, np.float32)])
+    blocks = vals.reshape(-1, 31)
+    x = np.concatenate([np.full((len(blocks), 1), 127.0, np.float32), blocks], axis=1)
+    q, d = orc.quantize_q8(x.reshape(-1))
+    assert np.all(d == 1.0)
+    expect = np.array([[half_away(v) for v in row] for row in x], np.int64)
+    assert np.array_equal(q.reshape(x.shape).astype(np.int64), expect), "unit-scale rounding is half away from zero"
+    # random values not within 2^-20 of a half-integer also round textbook-style
+    rng = np.random.default_rng(12)
+    r = rng.uniform(-126.9, 126.9, size=(64, 31)).astype(np.float32)
+    frac = np.abs(np.abs(r.astype(np.float64)) - np.floor(np.abs(r.astype(np.float64))) - 0.5)
+    r[frac < 2.0 ** -20] = 0.25
+    x = np.concatenate([np.full((64, 1), 127.0, np.float32), r], axis=1)
+    q, _ = orc.quantize_q8(x.reshape(-1))
+    expect = np.array([[half_away(v) for v in row] for row in x], np.int64)
+    assert np.array_equal(q.reshape(x.shape).astype(np.int64), expect)
+
+
+def check_q8_ties():
+    x = np.zeros(32, np.float32)
+    x[0] = 127.0
+    x[1:7] = [2.5, -2.5, 0.5, -0.5, 1.5, 126.5]
+    q, _ = orc.quantize_q8(x)
+    assert list(q[1:7]) == [3, -3, 1, -1, 2, 127], "ties go away from zero"
+
+
+def check_q8_detectors():
+    for case in golden("q8_rounding_detectors.json")["cases"]:
+        amax = f32_from_bits(case["amax_bits"])
+        xv = f32_from_bits(case["x_bits"])
+        x = np.zeros(32, np.float32)
+        x[0] = amax
+        x[5] = xv
+        x[9] = -xv
+        q, _ = orc.quantize_q8(x)
+        assert q[5] == case["q"] and q[9] == -case["q"], case["why"]
+
+
+def check_q8_invariants():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal(32 * 256).astype(np.float32)
+    q, d = orc.quantize_q8(x)
+    qn, dn = orc.quantize_q8(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d), "q(-x) = -q(x), d(-x) = d(x)"
+    for k in (-7, -1, 1, 5):
+        s = np.float32(2.0 ** k)
+        qs, ds = orc.quantize_q8(x * s)
+        assert np.array_equal(qs, q) and np.array_equal(ds, d * s), "power-of-two scaling"
+
+
+def check_q8_roundtrip():
+    # section 7, test_quant: quantize -> dequantize error <= d/2 per element
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal(32 * 1024).astype(np.float32)
+    x[::50] *= np.float32(20.0)
+    q, d = orc.quantize_q8(x)
+    xb = x.reshape(-1, QK).astype(np.float64)
+    deq = q.reshape(-1, QK).astype(np.float64) * d.astype(np.float64)[:, None]
+    err = np.abs(deq - xb)
+    amax = np.abs(xb).max(axis=1)
+    # d/2 plus a few binary32 roundings of the amax-sized intermediate values
+    bound = d.astype(np.float64)[:, None] / 2 + 4 * amax[:, None] * 2.0 ** -24
+    assert np.all(err <= bound), "round trip within d/2"
+
+
+# ---------------------------------------------------------------------------
+# Q4_0 quantization pins
+# ---------------------------------------------------------------------------
+
+def check_q4_layout():
+    spec = golden("spec_constants.json")["q4_0"]
+    v = np.array([(i % 15) - 7 for i in range(32)], np.int64)  # -7..7, each element distinct within a half
+    v[3] = 7
+    c = np.float32(0.125)
+    x = (v * 0.125).astype(np.float32)        # amax = 7c exactly, id = 7/amax = 8, x*id = v exactly
+    q, d = orc.quantize_q4(x)
+    assert q.shape == (spec["bytes_per_block"],)
+    assert d[0] == np.float32(7 * c) / np.float32(7.0)
+    lo, hi = spec["low_nibble_elems"], spec["high_nibble_elems"]
+    for j in range(16):
+        assert (q[j] & 0x0F) == v[lo[0] + j] + spec["offset"], "low nibble of byte j holds element j"
+        assert (q[j] >> 4) == v[hi[0] + j] + spec["offset"], "high nibble of byte j holds element j+16"
+
+
+def check_q4_closed_forms():
+    x = np.zeros(64, np.float32)
+    x[32:] = 0.3
+    q, d = orc.quantize_q4(x)
+    assert np.all(q[:16] == 0x88) and d[0] == 0.0, "zero block: nibble 8 (value 0), d = 0"
+    assert np.all(q[16:] == 0xFF) and d[1] == np.float32(0.3) / np.float32(7.0), "equal block: value 7"
+    q, d = orc.quantize_q4(-x)
+    assert np.all(q[16:] == 0x11), "equal negative block: value -7 (nibble 1)"
+
+
+def check_q4_roundtrip():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal(32 * 512).astype(np.float32)
+    q, d = orc.quantize_q4(x)
+    vals = q4_values(q.reshape(1, -1)).reshape(-1, QK)
+    assert vals.min() >= -8 and vals.max() <= 7
+    deq = vals.astype(np.float64) * d.astype(np.float64)[:, None]
+    xb = x.reshape(-1, QK).astype(np.float64)
+    amax = np.abs(xb).max(axis=1)
+    bound = d.astype(np.float64)[:, None] / 2 + 4 * amax[:, None] * 2.0 ** -24
+    assert np.all(np.abs(deq - xb) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# Block sums
+# ---------------------------------------------------------------------------
+
+def check_block_sum_closed_forms():
+    spec = golden("spec_constants.json")
+    wq = np.full((1, 32), 127, np.int8)
+    xq = np.full(32, 127, np.int8)
+    s = orc.block_sums(8, wq, xq)
+    assert s[0, 0] == spec["max_abs_block_sum_q8"] == 32 * 127 * 127
+    s = orc.block_sums(8, wq, -xq)
+    assert s[0, 0] == -spec["max_abs_block_sum_q8"]
+    w4 = np.zeros((1, 16), np.uint8)           # every nibble 0 -> value -8
+    s = orc.block_sums(4, w4, np.full(32, -127, np.int8))
+    assert s[0, 0] == 32 * 8 * 127
+    w4 = np.full((1, 16), 0x0F, np.uint8)      # low nibbles 15 (+7), high nibbles 0 (-8)
+    xq = np.concatenate([np.ones(16, np.int8), np.full(16, 2, np.int8)])
+    s = orc.block_sums(4, w4, xq)
+    assert s[0, 0] == 16 * 7 * 1 + 16 * (-8) * 2
+
+
+def check_block_sums_brute():
+    rng = np.random.default_rng(16)
+    for qtype in (8, 4):
+        rows, k = 7, 32 * 9
+        if qtype == 8:
+            wq = rng.integers(-128, 128, size=(rows, k), dtype=np.int16).astype(np.int8)
+        else:
+            wq = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+        xq = rng.integers(-128, 128, size=k, dtype=np.int16).astype(np.int8)
+        got = orc.block_sums(qtype, wq, xq)
+        w = w_values(qtype, wq).reshape(rows, k // QK, QK)
+        want = (w * xq.astype(np.int64).reshape(1, k // QK, QK)).sum(axis=2)
+        assert np.array_equal(got.astype(np.int64), want)
+        got = orc.block_sums(qtype, wq, xq, 2, 5)
+        assert np.array_equal(got.astype(np.int64), want[2:5])
+
+
+# ---------------------------------------------------------------------------
+# Matvec / gemm
+# ---------------------------------------------------------------------------
+
+def _tiny_problem(rng, qtype, rows, k):
+    if qtype == 8:
+        wq = rng.integers(-127, 128, size=(rows, k), dtype=np.int16).astype(np.int8)
+    else:
+        wq = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    wd = (np.exp2(rng.uniform(-8, 0, size=(rows, k // QK))) * rng.uniform(0.5, 2, size=(rows, k // QK))).astype(np.float32)
+    x = rng.standard_normal(k).astype(np.float32)
+    xq, xd = orc.quantize_q8(x)
+    return wq, wd, xq, xd
+
+
+def check_matvec_brute64():
+    rng = np.random.default_rng(17)
+    for qtype in (8, 4):
+        for rows, k in ((1, 32), (5, 64), (13, 32 * 11), (4, 32 * 40)):
+            wq, wd, xq, xd = _tiny_problem(rng, qtype, rows, k)
+            y = orc.matvec(qtype, wq, wd, xq, xd)
+            y64 = brute_matvec64(qtype, wq, wd, xq, xd)
+            a64 = brute_abs_terms64(qtype, wq, wd, xq, xd)
+            assert np.all(np.abs(y.astype(np.float64) - y64) <= 1e-5 * a64 + 1e-6), "fp64 brute force"
+            assert np.allclose(orc.tol_abs(qtype, wq, wd, xq, xd), a64, rtol=1e-12, atol=0), "A(r)"
+
+
+def check_matvec_unit_scales():
+    # dw = dx = 1: y[r] = sum_b sumi exactly while |sum| < 2^24
+    rng = np.random.default_rng(18)
+    for qtype in (8, 4):
+        rows, k = 9, 32 * 16
+        wq, _, xq, _ = _tiny_problem(rng, qtype, rows, k)
+        ones_w = np.ones((rows, k // QK), np.float32)
+        ones_x = np.ones(k // QK, np.float32)
+        y = orc.matvec(qtype, wq, ones_w, xq, ones_x)
+        want = (w_values(qtype, wq) * xq.astype(np.int64)[None, :]).sum(axis=1)
+        assert np.all(np.abs(want) < 2 ** 24)
+        assert np.array_equal(y.astype(np.int64), want)
+        # one-hot dx isolates one block's sum at any K
+        for b in (0, k // QK - 1, 5):
+            oh = np.zeros(k // QK, np.float32)
+            oh[b] = 1.0
+            y = orc.matvec(qtype, wq, ones_w, xq, oh)
+            wb = w_values(qtype, wq)[:, b * QK:(b + 1) * QK]
+            assert np.array_equal(y.astype(np.int64), (wb * xq[b * QK:(b + 1) * QK].astype(np.int64)).sum(axis=1))
+
+
+def check_matvec_invariants():
+    rng = np.random.default_rng(19)
+    for qtype in (8, 4):
+        rows, k = 11, 32 * 7
+        wq, wd, xq, xd = _tiny_problem(rng, qtype, rows, k)
+        y = orc.matvec(qtype, wq, wd, xq, xd)
+        yn = orc.matvec(qtype, wq, wd, (-xq.astype(np.int16)).astype(np.int8), xd)
+        assert np.array_equal(yn, -y), "y(-x) = -y(x)"
+        ys = orc.matvec(qtype, wq, wd, xq, xd * np.float32(0.25))
+        assert np.array_equal(ys, y * np.float32(0.25)), "y(x * 2^-2) = y(x) * 2^-2"
+        perm = rng.permutation(rows)
+        yp = orc.matvec(qtype, wq[perm], wd[perm], xq, xd)
+        assert np.array_equal(yp, y[perm]), "row permutation"
+        sentinel = np.full(rows, np.float32(-7.5))
+        ysub = orc.matvec(qtype, wq, wd, xq, xd, 3, 8, y=sentinel.copy())
+        assert np.array_equal(ysub[3:8], y[3:8]), "rows [r0, r1) match the full run"
+        assert np.all(ysub[:3] == -7.5) and np.all(ysub[8:] == -7.5), "rows outside [r0, r1) untouched"
+        ye = orc.matvec(qtype, wq, wd, xq, xd, 4, 4, y=sentinel.copy())
+        assert np.all(ye == -7.5), "empty range writes nothing"
+
+
+def check_gemm_rows():
+    rng = np.random.default_rng(20)
+    for qtype in (8, 4):
+        rows, k, m = 6, 32 * 5, 3
+        wq, wd, _, _ = _tiny_problem(rng, qtype, rows, k)
+        X = rng.standard_normal((m, k)).astype(np.float32)
+        xq, xd = orc.quantize_q8(X)
+        # per-row quantization of X equals quantizing the flattened M*K array
+        xq1, xd1 = orc.quantize_q8(X.reshape(-1))
+        assert np.array_equal(xq1.reshape(m, k), xq) and np.array_equal(xd1.reshape(m, -1), xd)
+        Y = orc.gemm(qtype, wq, wd, xq, xd)
+        for i in range(m):
+            assert np.array_equal(Y[i], orc.matvec(qtype, wq, wd, xq[i], xd[i]))
+            y64 = brute_matvec64(qtype, wq, wd, xq[i], xd[i])
+            a64 = brute_abs_terms64(qtype, wq, wd, xq[i], xd[i])
+            assert np.all(np.abs(Y[i].astype(np.float64) - y64) <= 1e-5 * a64 + 1e-6)
+
+
+ALL_CHECKS = [
+    check_q8_zero_block, check_q8_equal_block, check_q8_clamp_and_range,
+    check_q8_unit_scale_textbook, check_q8_ties, check_q8_detectors,
+    check_q8_invariants, check_q8_roundtrip,
+    check_q4_layout, check_q4_closed_forms, check_q4_roundtrip,
+    check_block_sum_closed_forms, check_block_sums_brute,
+    check_matvec_brute64, check_matvec_unit_scales, check_matvec_invariants,
+    check_gemm_rows,
+]
+
+
+def failing_checks():
+    """Names of the checks that fail against the oracle build in use."""
+    bad = []
+    for c in ALL_CHECKS:
+        try:
+            c()
+        except AssertionError:
+            bad.append(c.__name__)
+    return bad

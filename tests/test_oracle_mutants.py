@@ -1,0 +1,61 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and show
+that the pins catch every one of them.  A mutant that passes every pin
+would mean the pins cannot tell that mistake from the spec's rule."""
+import os
+
+import pytest
+
+import pins
+from oracle import oracle as orc
+
+SRC = os.path.join(os.path.dirname(orc.__file__), "qmv_oracle.c")
+
+# (name, text in the source, replacement, occurrence to replace or None = all)
+# Not listed: widening the Q8 clamp to -128.  For finite input |x * id| is at
+# most 127 * (1 + 2^-23)^2, so trunc(x * id +- 0.5) never leaves [-127, 127]
+# and that edit cannot change any output (an equivalent mutant).
+MUTANTS = [
+    ("round_by_division", "float v = xb[i] * id;\n            float t = v + copysignf(0.5f, xb[i]);\n            int qi = (int)truncf(t);\n            if (qi > 127)",
+     "float v = xb[i] / db;\n            float t = v + copysignf(0.5f, xb[i]);\n            int qi = (int)truncf(t);\n            if (qi > 127)", 1),
+    ("id_from_d", "float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;", "float id = (amax != 0.0f) ? 1.0f / db : 0.0f;", 1),
+    ("fused_multiply_add", "float v = xb[i] * id;\n            float t = v + copysignf(0.5f, xb[i]);\n            int qi = (int)truncf(t);\n            if (qi > 127)",
+     "float t = fmaf(xb[i], id, copysignf(0.5f, xb[i]));\n            int qi = (int)truncf(t);\n            if (qi > 127)", 1),
+    ("round_half_even", "int qi = (int)truncf(t);\n            if (qi > 127)", "int qi = (int)rintf(v);\n            (void)t;\n            if (qi > 127)", 1),
+    ("truncate_only", "float t = v + copysignf(0.5f, xb[i]);\n            int qi = (int)truncf(t);\n            if (qi > 127)",
+     "float t = v;\n            int qi = (int)truncf(t);\n            if (qi > 127)", 1),
+    ("scale_128", "float db = amax / 127.0f;", "float db = amax / 128.0f;", 1),
+    ("signed_max", "float a = fabsf(xb[i]);\n            if (a > amax)\n                amax = a;\n        }\n        float db = amax / 127.0f;",
+     "float a = xb[i];\n            if (a > amax)\n                amax = a;\n        }\n        float db = amax / 127.0f;", 1),
+    ("q4_nibbles_swapped", "(i < QK / 2) ? (blk[i] & 0x0F) : (blk[i - QK / 2] >> 4)", "(i < QK / 2) ? (blk[i] >> 4) : (blk[i - QK / 2] & 0x0F)", 1),
+    ("q4_interleaved", "(i < QK / 2) ? (blk[i] & 0x0F) : (blk[i - QK / 2] >> 4)", "(i % 2 == 0) ? (blk[i / 2] & 0x0F) : (blk[i / 2] >> 4)", 1),
+    ("q4_offset_7", "return nib - 8;", "return nib - 7;", 1),
+    ("q4_pack_interleaved", "q[b * (QK / 2) + j] = (uint8_t)(nib[j] | (nib[j + QK / 2] << 4));",
+     "q[b * (QK / 2) + j] = (uint8_t)(nib[2 * j] | (nib[2 * j + 1] << 4));", 1),
+    ("q4_scale_8", "float db = amax / 7.0f;", "float db = amax / 8.0f;", 1),
+    ("drop_last_block", "for (int32_t b = 0; b < nb; ++b) {\n        const int8_t *w = wq + (int64_t)r * cols + (int64_t)b * QK;\n        const int8_t *xv = xq + (int64_t)b * QK;\n        int32_t sumi = 0;",
+     "for (int32_t b = 0; b < nb - 1; ++b) {\n        const int8_t *w = wq + (int64_t)r * cols + (int64_t)b * QK;\n        const int8_t *xv = xq + (int64_t)b * QK;\n        int32_t sumi = 0;", 1),
+    ("dx_wrong_index", "t = t * xd[b];", "t = t * xd[r % nb];", None),
+    ("dw_transposed", "float t = (float)sumi * wd[(int64_t)r * nb + b];", "float t = (float)sumi * wd[(int64_t)b * nb + r % nb];", None),
+    ("drop_dx", "t = t * xd[b];", "t = t * 1.0f;", None),
+    ("acc_overwrite", "s = s + t;", "s = t;", None),
+    ("sum_sign", "sumi += (int32_t)q4_elem(blk, i) * (int32_t)xv[i];", "sumi -= (int32_t)q4_elem(blk, i) * (int32_t)xv[i];", None),
+    ("y_relative_index", "y[r] = row_q8(wq, wd, cols, xq, xd, r);", "y[r - r0] = row_q8(wq, wd, cols, xq, xd, r);", 1),
+    ("gemm_x_stride", "xq + (int64_t)i * cols, xd + (int64_t)i * nb, r0, r1);", "xq + (int64_t)i * cols, xd, r0, r1);", None),
+]
+
+
+def _apply(src, old, new, count):
+    assert old in src, "mutation site not found"
+    return src.replace(old, new) if count is None else src.replace(old, new, count)
+
+
+@pytest.mark.parametrize("name,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new, count):
+    with open(SRC) as f:
+        src = f.read()
+    mutated = _apply(src, old, new, count)
+    assert mutated != src
+    so = orc.build_variant(mutated, str(tmp_path / f"mut_{name}.so"))
+    with orc.use_build(so):
+        failed = pins.failing_checks()
+    assert failed, f"no pin catches the planted mistake '{name}'"
