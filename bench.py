@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Bench of the block-quantized decode product on one MI355X.
+
+Default workload: the Llama-7B-shaped FFN stack, Q4_0, M = 1 -- 8 layers of
+(W_up 11008 x 4096, W_down 4096 x 11008), 450,887,680 weight bytes per step,
+more than the 256 MB last-level cache, so every step streams its weights
+from HBM.  One step = the whole path once: for each of the 16 matrices, the
+fused kernel quantizes that matrix's float32 activation to Q8_0 on chip and
+streams the matrix (qmv_matvec_q4_fx).
+
+Printed: one JSON line with the metric (weight GB/s = quant + scale bytes
+per step / step time), the roofline of the dominant kernel (HIP events
+around each of its launches in the timed region) and the CPU oracle timed
+on a bounded sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix peak, vendor figure
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_ffn_stack_q4")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_decode_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if
+    they were taken on the kernel sources as they are now; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by weight rows across GPUs, but nothing here launches a second GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_quantized_decode_amd import qmv, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    assert wl.ms[0] == 1 and len(wl.qtypes) == 1, "the bench times the M = 1 fused path"
+    qtype = wl.qtypes[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qmv.qmv_device_check()
+
+    # ---- inputs, resident in HBM before timing starts
+    t_setup = time.time()
+    mats = []
+    acts = {}
+    for mt in wl.matrices:
+        w = torch.from_numpy(synth.weight(wl, mt.name)).to(dev)
+        q, d = qmv.qmv_quantize_weights(w, qtype)
+        del w
+        if mt.act not in acts:
+            acts[mt.act] = torch.from_numpy(synth.activation(wl, mt.act, 1).reshape(-1)).to(dev)
+        y = torch.zeros(mt.rows, dtype=torch.float32, device=dev)
+        mats.append((mt, q, d, acts[mt.act], y))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    setup_s = time.time() - t_setup
+    fx = qmv.qmv_matvec_q4_fx if qtype == 4 else qmv.qmv_matvec_q8_fx
+
+    weight_bytes = wl.weight_bytes(qtype)                      # q + d per step
+    algo_bytes = [q.numel() + d.numel() * 4 + 4 * mt.cols + 4 * mt.rows for mt, q, d, _, _ in mats]
+
+    def step(events=None):
+        for i, (mt, q, d, x, y) in enumerate(mats):
+            if events is not None:
+                events[i][0].record()
+            fx(q, d, x, y=y)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kernel = qmv.last_kernel()
+
+    # ---- timed region: K steps, HIP events around every launch on the launch stream
+    stream = torch.cuda.current_stream()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in mats]
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    launch_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])   # [steps, matrices]
+    avg_launch_us = float(launch_ms.mean()) * 1e3
+    avg_algo_bytes = float(np.mean(algo_bytes))
+    achieved_gbs = avg_algo_bytes / (avg_launch_us * 1e-6) / 1e9
+    per_matrix_us = {}
+    for i, (mt, *_rest) in enumerate(mats):
+        key = mt.name.split(".")[0]
+        per_matrix_us.setdefault(key, []).append(float(launch_ms[:, i].mean()) * 1e3)
+
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    sha = kernel_source_sha()
+    traffic = load_traffic(kernel, sha)
+
+    # ---- CPU oracle baseline on a bounded sample (and a parity spot-check)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, qtype, mats, args.cpu_seconds)
+
+    line = {
+        "metric": "M=1 matvec weight GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 x q8_0 -> i32 block sums, f32 accumulate" if qtype == 4 else "q8_0 x q8_0 -> i32 block sums, f32 accumulate",
+        "data": "synthetic (seeded numpy draws, shapes of the named model; no trained weights)",
+        "config": {
+            "workload": wl.name,
+            "shapes": "8 x (W_up 11008x4096, W_down 4096x11008)" if wl.name.startswith("llama7b") else
+                      ", ".join(f"{mt.name} {mt.rows}x{mt.cols}" for mt in wl.matrices),
+            "m": 1,
+            "weight_bytes_per_step": weight_bytes,
+            "launches_per_step": len(mats),
+            "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "kernel": kernel,
+            "kernel_avg_us": {k: round(float(np.mean(v)), 3) for k, v in per_matrix_us.items()},
+            "setup_s": round(setup_s, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": round(avg_algo_bytes),
+            "avg_launch_us": round(avg_launch_us, 3),
+            "kernel_source_sha": sha,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if cpu is not None and not cpu.get("parity_ok", True):
+        sys.exit(1)
+
+
+def cpu_baseline(wl, qtype, mats, target_s):
+    """Time the CPU oracle (plain C, as committed) on the same workload: the
+    oracle quantizes each matrix's activation and multiplies all matrices of
+    the step, rows split over the host cores by the oracle's own row-range
+    contract (ctypes drops the GIL inside each call).  Whole steps are
+    repeated until about target_s seconds have passed.  The GPU outputs of
+    the last timed GPU step are checked against the oracle's within the
+    tolerance on every row."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    from block_quantized_decode_amd import synth
+    from oracle import oracle as orc
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    prepared = []
+    xs = {}
+    for mt, q, d, x, y in mats:
+        w = synth.weight(wl, mt.name)
+        wq, wd = (orc.quantize_q4(w) if qtype == 4 else orc.quantize_q8(w))
+        del w
+        if mt.act not in xs:
+            xs[mt.act] = synth.activation(wl, mt.act, 1).reshape(-1)
+        prepared.append((mt, wq, wd, xs[mt.act], y.cpu().numpy(), np.zeros(mt.rows, np.float32)))
+
+    pool = cf.ThreadPoolExecutor(cores)
+
+    def oracle_step():
+        for mt, wq, wd, xh, _, out in prepared:
+            xq, xd = orc.quantize_q8(xh)
+            bounds = np.linspace(0, mt.rows, cores + 1).astype(int)
+            list(pool.map(lambda i: orc.matvec(qtype, wq, wd, xq, xd, int(bounds[i]), int(bounds[i + 1]), y=out),
+                          range(cores)))
+
+    passes = 0
+    t = time.perf_counter()
+    while True:
+        oracle_step()
+        passes += 1
+        el = time.perf_counter() - t
+        if el >= target_s:
+            break
+    pool.shutdown()
+    parity_ok = True
+    worst = 0.0
+    for mt, wq, wd, xh, ygpu, out in prepared:
+        xq, xd = orc.quantize_q8(xh)
+        tol = orc.tolerance(qtype, wq, wd, xq, xd)
+        err = np.abs(ygpu.astype(np.float64) - out.astype(np.float64))
+        worst = max(worst, float((err / tol).max()))
+        parity_ok &= bool(np.all(err <= tol))
+    wbytes = wl.weight_bytes(qtype)
+    return {
+        "value": round(wbytes * passes / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"the full step ({len(prepared)} matrices, {wbytes} weight bytes, activation quantization "
+                  f"included) repeated {passes} times in {el:.1f} s, rows split over {cores} threads",
+        "parity_ok": parity_ok,
+        "parity_max_err_over_tol": round(worst, 4),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+// device_common.h -- device helpers shared by the libqmv kernels (gfx950).
+//
+// Quantization rule: Legacy-ISA ML Inference Runtime -- Design Spec,
+// section 4 ("Q8 quantization": d = max|x| / 127, all-zero block -> d = 0)
+// and section 5 (rounding bullet: q = trunc(x * id + copysign(0.5, x)),
+// id = 127 / amax, no floating-point contraction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+constexpr int QK = 32;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// One element: v = x * id, t = v + copysign(0.5, x), q = trunc(t), each
+// float operation rounded on its own (contraction off in this scope), then
+// clamped to [lo, hi].  fp32 division elsewhere is the IEEE correctly
+// rounded sequence (hipcc default), never a reciprocal approximation.
+__device__ __forceinline__ int quant_round(float x, float id, int lo, int hi) {
+#pragma clang fp contract(off)
+    float v = x * id;
+    float t = v + copysignf(0.5f, x);
+    int q = (int)truncf(t);
+    return min(max(q, lo), hi);
+}
+
+// Cross-lane moves within an aligned group of 8 lanes, one DPP instruction
+// each: swap neighbours (quad_perm [1,0,3,2]), swap pairs (quad_perm
+// [2,3,0,1]), and mirror the 8 lanes (row_half_mirror, lane i <-> 7 - i).
+// After the two quad steps every lane of a quad holds the quad's value, so
+// the mirror step combines the two quads of the group.
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+// row_shl:4 -- lane i receives lane i + 4 (within a row of 16 lanes).
+__device__ __forceinline__ int dpp_down4(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false); }
+
+__device__ __forceinline__ float group8_max(float a) {
+    a = fmaxf(a, __int_as_float(dpp_xor1(__float_as_int(a))));
+    a = fmaxf(a, __int_as_float(dpp_xor2(__float_as_int(a))));
+    a = fmaxf(a, __int_as_float(dpp_mirror8(__float_as_int(a))));
+    return a;
+}
+
+__device__ __forceinline__ int group8_sum(int s) {
+    s += dpp_xor1(s);
+    s += dpp_xor2(s);
+    s += dpp_mirror8(s);
+    return s;
+}
+
+// Largest |x| of a 32-element block spread over an aligned group of 8 lanes,
+// 4 elements per lane (lane c of the group holds elements 4c..4c+3).  All 8
+// lanes of the group must be active.  The maximum is exact, so its
+// evaluation order does not matter.
+__device__ __forceinline__ float block_amax8(float4 v) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    return group8_max(a);
+}
+
+__device__ __forceinline__ int pack4(int a, int b, int c, int d) {
+    return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((unsigned)(d & 0xFF) << 24);
+}
+
+// Q8_0 quantization of one block held by an aligned group of 8 lanes.
+// Returns this lane's 4 quants packed little-endian (element 4c in the low
+// byte); d receives the block scale and qsum the sum of the block's 32
+// quants (both identical in all 8 lanes).
+__device__ __forceinline__ int quant_q8_group8(float4 v, float &d, int &qsum) {
+    float amax = block_amax8(v);
+    d = amax / 127.0f;
+    float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+    int q0 = quant_round(v.x, id, -127, 127);
+    int q1 = quant_round(v.y, id, -127, 127);
+    int q2 = quant_round(v.z, id, -127, 127);
+    int q3 = quant_round(v.w, id, -127, 127);
+    qsum = group8_sum(q0 + q1 + q2 + q3);
+    return pack4(q0, q1, q2, q3);
+}
+
+// Q8_0 quantization of one whole 32-element block held by one lane (the
+// same arithmetic as quant_q8_group8, hence the same bits): the 32 quants
+// are returned packed little-endian in lo (elements 0..15) and hi
+// (elements 16..31), with the block scale d and the sum of the quants.
+__device__ __forceinline__ void quant_q8_lane(const float4 (&v)[8], v4i &lo, v4i &hi, float &d, int &qsum) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    d = amax / 127.0f;
+    const float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+    int w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        w[i] = pack4(quant_round(v[i].x, id, -127, 127), quant_round(v[i].y, id, -127, 127),
+                     quant_round(v[i].z, id, -127, 127), quant_round(v[i].w, id, -127, 127));
+    lo = (v4i){w[0], w[1], w[2], w[3]};
+    hi = (v4i){w[4], w[5], w[6], w[7]};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = __builtin_amdgcn_sdot4(w[i], 0x01010101, s, false);
+    qsum = s;
+}
+
+// Q4_0 weight quantization of one block held by an aligned group of 8
+// lanes: d = amax / 7, value = clamp(trunc(x * (7 / amax) + copysign(0.5,
+// x)), -8, 7), nibble = value + 8.  Returns this lane's 4 nibbles, one per
+// byte (element 4c in the low byte).
+__device__ __forceinline__ int quant_q4_group8(float4 v, float &d) {
+    float amax = block_amax8(v);
+    d = amax / 7.0f;
+    float id = (amax != 0.0f) ? 7.0f / amax : 0.0f;
+    int n0 = quant_round(v.x, id, -8, 7) + 8;
+    int n1 = quant_round(v.y, id, -8, 7) + 8;
+    int n2 = quant_round(v.z, id, -8, 7) + 8;
+    int n3 = quant_round(v.w, id, -8, 7) + 8;
+    return pack4(n0, n1, n2, n3);
+}
+
+// v_dot4_i32_i8: c + sum of the four signed byte products of a and b.
+__device__ __forceinline__ int dot4(int a, int b, int c) {
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Transposing wave reduction of NV per-lane partial sums (NV a power of two,
+// at most 64).  At each butterfly step with lane offset o, a lane keeps half
+// of its values (the upper half if bit o of its lane id is set), sends the
+// other half to lane ^ o and adds what it receives; once one value is left
+// the remaining steps are plain butterfly sums.  On return every lane holds
+// the wave-wide total of value index reduce_index<NV>(lane).
+template <int NV>
+__device__ __forceinline__ float wave_reduce_transpose(float (&a)[NV]) {
+    static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of two <= 64");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        const int o = 32 >> s;
+        const int n = NV >> s;  // values still held
+        if (n > 1) {
+            const bool up = (lane & o) != 0;
+#pragma unroll
+            for (int i = 0; i < n / 2; ++i) {
+                float lo = a[i], hi = a[i + n / 2];
+                // opaque to the optimizer: otherwise the selects below are
+                // folded into one load from a lane-dependent address, which
+                // would push the whole array out of registers into scratch
+                asm volatile("" : "+v"(lo), "+v"(hi));
+                float keep = up ? hi : lo;
+                float send = up ? lo : hi;
+                a[i] = keep + __shfl_xor(send, o);
+            }
+        } else {
+            a[0] += __shfl_xor(a[0], o);
+        }
+    }
+    return a[0];
+}
+
+// Value index whose total wave_reduce_transpose<NV> leaves in `lane`.
+template <int NV>
+__device__ __forceinline__ int reduce_index(int lane) {
+    int idx = 0;
+#pragma unroll
+    for (int s = 0; (NV >> (s + 1)) >= 1; ++s)
+        idx += ((lane >> (5 - s)) & 1) * (NV >> (s + 1));
+    return idx;
+}
+
+// Lanes that hold a distinct total after wave_reduce_transpose<NV>: those
+// whose lane-id bits below the top log2(NV) bits are zero.
+template <int NV>
+__device__ __forceinline__ bool reduce_owner(int lane) {
+    return (lane & ((64 / NV) - 1)) == 0;
+}
+
+}  // namespace qmv

@@ -1,0 +1,36 @@
+// launch.h -- internal interface between the C ABI (qmv_api.cpp) and the
+// kernel translation units.  Not installed, not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+// Arguments of the weight-streaming product for M = 1 .. 8 activation rows.
+struct RowsArgs {
+    int qtype;                 // 4 or 8
+    float *y;                  // M x rows, row-major
+    const int8_t *wq;
+    const float *wd;
+    int32_t rows, K;
+    int32_t M;                 // activation rows (1 when x is given)
+    const float *x;            // float32 activation (fused quantization), or null
+    const int8_t *xq;          // Q8_0 activation quants (when x is null)
+    const float *xd;           // Q8_0 activation scales (when x is null)
+    int8_t *xq_out;            // optional copy of the fused quantization
+    float *xd_out;
+    int32_t r0, r1;
+    int max_groups;            // cap on the workgroup count
+};
+
+hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name);
+
+// Q8_0 quantization of nblk blocks of 32 floats (activations or weights).
+hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,
+                           const char **name);
+// Q4_0 quantization of nblk blocks of 32 floats (weights).
+hipError_t launch_quant_q4(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,
+                           const char **name);
+
+}  // namespace qmv

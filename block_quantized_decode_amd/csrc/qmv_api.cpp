@@ -1,0 +1,262 @@
+// qmv_api.cpp -- the C ABI of libqmv (declared in include/qmv.h).
+//
+// Every entry point validates its arguments on the host before anything is
+// enqueued (status convention of the Legacy-ISA ML Inference Runtime --
+// Design Spec, section 6 "Error handling": return a status, never abort;
+// shape checks of the loader such as K % 32 == 0 move to call entry), then
+// checks once per device that the device is a gfx950 (the spec's
+// instruction-set guard, section 6, turned into a device-architecture
+// guard), then launches on the caller's stream.  There is no fallback path:
+// a call either runs the gfx950 kernels or returns an error.
+#include "qmv.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unchecked, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch[kMaxDevices];
+int g_num_cu[kMaxDevices];
+
+thread_local const char *t_last_kernel = "";
+
+bool diag_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("QMV_DIAG");
+        v = (e != nullptr && e[0] != '\0' && e[0] != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+qmv_status device_check(int *dev_out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return QMV_E_DEVICE;
+    }
+    int st = g_arch[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return QMV_E_DEVICE;
+        }
+        st = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_num_cu[dev] = p.multiProcessorCount;
+        g_arch[dev].store(st, std::memory_order_release);
+        if (diag_enabled())
+            fprintf(stderr, "[qmv] device %d: %s, %d CUs -> %s\n", dev, p.gcnArchName, p.multiProcessorCount,
+                    st == 1 ? "ok" : "QMV_E_ARCH");
+    }
+    if (dev_out) *dev_out = dev;
+    return st == 1 ? QMV_OK : QMV_E_ARCH;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+qmv_status finish(hipError_t e, const char *name, long grid_hint) {
+    if (e != hipSuccess) return QMV_E_DEVICE;
+    t_last_kernel = name;
+    if (diag_enabled()) fprintf(stderr, "[qmv] launch %s (%ld)\n", name, grid_hint);
+    return QMV_OK;
+}
+
+#ifndef QMV_GROUPS_PER_CU
+#define QMV_GROUPS_PER_CU 1
+#endif
+
+// Upper bound on the workgroup count of the row-streaming kernels: one
+// workgroup per compute unit, whose wavefronts loop over row quads.  Every
+// workgroup stages the whole activation, so more workgroups only multiply
+// the activation traffic that every CU pulls through L2 at the same time.
+int groups_cap(int dev) {
+    int cu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+    return cu * QMV_GROUPS_PER_CU;
+}
+
+qmv_status check_weight(const qmv_qtensor *W, int want_type) {
+    if (W == nullptr || W->q == nullptr || W->d == nullptr) return QMV_E_ARG;
+    if (W->type != QMV_Q4_0 && W->type != QMV_Q8_0) return QMV_E_FORMAT;
+    if (want_type != 0 && W->type != want_type) return QMV_E_FORMAT;
+    if (W->rows < 0 || W->cols <= 0 || (W->cols % QMV_QK) != 0) return QMV_E_SHAPE;
+    return QMV_OK;
+}
+
+qmv_status check_range(const qmv_qtensor *W, int32_t r0, int32_t r1) {
+    if (r0 < 0 || r1 > W->rows || r0 > r1) return QMV_E_SHAPE;
+    return QMV_OK;
+}
+
+qmv_status check_weight_align(const qmv_qtensor *W) {
+    if (!aligned(W->q, 16) || !aligned(W->d, 4)) return QMV_E_ARG;
+    return QMV_OK;
+}
+
+qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, const float *x,
+                       const int8_t *xq, const float *xd, qmv_qact *xq_out, int32_t r0, int32_t r1,
+                       void *stream) {
+    if (y == nullptr) return QMV_E_ARG;
+    qmv_status st = check_weight(W, qtype);
+    if (st != QMV_OK) return st;
+    if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
+    const int64_t nb = W->cols / QMV_QK;
+    if (40 * nb * (int64_t)M > QMV_LDS_BYTES) return QMV_E_SHAPE;
+    if ((st = check_weight_align(W)) != QMV_OK) return st;
+    if (!aligned(y, 4)) return QMV_E_ARG;
+    if (x != nullptr && !aligned(x, 16)) return QMV_E_ARG;
+    if (xq != nullptr && (!aligned(xq, 16) || !aligned(xd, 4))) return QMV_E_ARG;
+    if (xq_out != nullptr && (!aligned(xq_out->q, 16) || !aligned(xq_out->d, 4))) return QMV_E_ARG;
+    int dev = -1;
+    if ((st = device_check(&dev)) != QMV_OK) return st;
+    if (xq_out != nullptr) xq_out->n = W->cols;
+    if (r0 == r1) return QMV_OK;
+    qmv::RowsArgs a;
+    a.qtype = qtype;
+    a.y = y;
+    a.wq = W->q;
+    a.wd = W->d;
+    a.rows = W->rows;
+    a.K = W->cols;
+    a.M = M;
+    a.x = x;
+    a.xq = xq;
+    a.xd = xd;
+    a.xq_out = xq_out ? xq_out->q : nullptr;
+    a.xd_out = xq_out ? xq_out->d : nullptr;
+    a.r0 = r0;
+    a.r1 = r1;
+    a.max_groups = groups_cap(dev);
+    const char *name = "";
+    hipError_t e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (r1 - r0 + 15) / 16);
+}
+
+qmv_status matvec_pre(int qtype, float *y, const qmv_qtensor *W, const qmv_qact *x, int32_t r0,
+                      int32_t r1, void *stream) {
+    if (x == nullptr || x->q == nullptr || x->d == nullptr) return QMV_E_ARG;
+    qmv_status st = check_weight(W, qtype);
+    if (st != QMV_OK) return st;
+    if (x->n != W->cols) return QMV_E_SHAPE;
+    return rows_common(qtype, y, W, 1, nullptr, x->q, x->d, nullptr, r0, r1, stream);
+}
+
+qmv_status matvec_fx(int qtype, float *y, const qmv_qtensor *W, const float *x, qmv_qact *xq,
+                     int32_t r0, int32_t r1, void *stream) {
+    if (x == nullptr) return QMV_E_ARG;
+    if (xq != nullptr && (xq->q == nullptr || xq->d == nullptr)) return QMV_E_ARG;
+    return rows_common(qtype, y, W, 1, x, nullptr, nullptr, xq, r0, r1, stream);
+}
+
+qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
+                void *stream) {
+    if (X == nullptr || X->q == nullptr || X->d == nullptr || Y == nullptr) return QMV_E_ARG;
+    qmv_status st = check_weight(W, qtype);
+    if (st != QMV_OK) return st;
+    if (X->type != QMV_Q8_0) return QMV_E_FORMAT;
+    if (X->rows < 1 || X->cols != W->cols) return QMV_E_SHAPE;
+    if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
+    if (!aligned(X->q, 16) || !aligned(X->d, 4)) return QMV_E_ARG;
+    // Dot-product path, up to 8 activation rows per pass over the weights.
+    for (int32_t m0 = 0; m0 < X->rows; m0 += 8) {
+        const int32_t mc = (X->rows - m0) < 8 ? (X->rows - m0) : 8;
+        st = rows_common(qtype, Y + (size_t)m0 * W->rows, W, mc, nullptr, X->q + (size_t)m0 * X->cols,
+                         X->d + (size_t)m0 * (X->cols / QMV_QK), nullptr, r0, r1, stream);
+        if (st != QMV_OK) return st;
+    }
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmv_status qmv_device_check(void) { return device_check(nullptr); }
+
+qmv_status qmv_quantize_q8(qmv_qact *out, const float *x, int64_t k, void *stream) {
+    if (out == nullptr) return QMV_E_ARG;
+    if (k < 0 || (k % QMV_QK) != 0 || k > INT32_MAX) return QMV_E_SHAPE;
+    if (k == 0) {  // nothing to quantize: data pointers may be null
+        out->n = 0;
+        return QMV_OK;
+    }
+    if (out->q == nullptr || out->d == nullptr || x == nullptr) return QMV_E_ARG;
+    if (!aligned(x, 16) || !aligned(out->q, 16) || !aligned(out->d, 4)) return QMV_E_ARG;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    out->n = (int32_t)k;
+    const char *name = "";
+    hipError_t e = qmv::launch_quant_q8(out->q, out->d, x, k / QMV_QK, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)(k / QMV_QK));
+}
+
+qmv_status qmv_quantize_weights(const qmv_qtensor *W, const float *w, void *stream) {
+    if (w == nullptr) return QMV_E_ARG;
+    qmv_status st = check_weight(W, 0);
+    if (st != QMV_OK) return st;
+    if (!aligned(w, 16)) return QMV_E_ARG;
+    if ((st = check_weight_align(W)) != QMV_OK) return st;
+    if ((st = device_check(nullptr)) != QMV_OK) return st;
+    const int64_t nblk = (int64_t)W->rows * (W->cols / QMV_QK);
+    if (nblk == 0) return QMV_OK;
+    const char *name = "";
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = W->type == QMV_Q8_0 ? qmv::launch_quant_q8(W->q, W->d, w, nblk, s, &name)
+                                       : qmv::launch_quant_q4(W->q, W->d, w, nblk, s, &name);
+    return finish(e, name, (long)nblk);
+}
+
+qmv_status qmv_matvec_q8(float *y, const qmv_qtensor *W, const qmv_qact *x, int32_t r0, int32_t r1,
+                         void *stream) {
+    return matvec_pre(QMV_Q8_0, y, W, x, r0, r1, stream);
+}
+
+qmv_status qmv_matvec_q4(float *y, const qmv_qtensor *W, const qmv_qact *x, int32_t r0, int32_t r1,
+                         void *stream) {
+    return matvec_pre(QMV_Q4_0, y, W, x, r0, r1, stream);
+}
+
+qmv_status qmv_matvec_q8_fx(float *y, const qmv_qtensor *W, const float *x, qmv_qact *xq, int32_t r0,
+                            int32_t r1, void *stream) {
+    return matvec_fx(QMV_Q8_0, y, W, x, xq, r0, r1, stream);
+}
+
+qmv_status qmv_matvec_q4_fx(float *y, const qmv_qtensor *W, const float *x, qmv_qact *xq, int32_t r0,
+                            int32_t r1, void *stream) {
+    return matvec_fx(QMV_Q4_0, y, W, x, xq, r0, r1, stream);
+}
+
+qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
+                       void *stream) {
+    return gemm(QMV_Q8_0, Y, W, X, r0, r1, stream);
+}
+
+qmv_status qmv_gemm_q4(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
+                       void *stream) {
+    return gemm(QMV_Q4_0, Y, W, X, r0, r1, stream);
+}
+
+const char *qmv_status_str(qmv_status s) {
+    switch (s) {
+        case QMV_OK: return "QMV_OK";
+        case QMV_E_SHAPE: return "QMV_E_SHAPE: bad shape, size mismatch or row range";
+        case QMV_E_FORMAT: return "QMV_E_FORMAT: wrong quantization type tag";
+        case QMV_E_ARG: return "QMV_E_ARG: null or misaligned pointer";
+        case QMV_E_ARCH: return "QMV_E_ARCH: device is not gfx950";
+        case QMV_E_DEVICE: return "QMV_E_DEVICE: no usable HIP device or launch failure";
+    }
+    return "unknown qmv_status";
+}
+
+const char *qmv_last_kernel(void) { return t_last_kernel; }
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+"""Thin ctypes binding of libqmv (include/qmv.h).
+
+Argument marshalling only: torch tensors are passed as device pointers with
+the current HIP stream; every step of the computation runs in the library's
+gfx950 kernels.  There is no CPU or PyTorch fallback: if libqmv.so has not
+been built, or a call fails, an exception is raised.
+
+Function names follow the C ABI (qmv_quantize_q8, qmv_matvec_q4_fx, ...).
+Tensors hold the SoA formats of the header: a Q4_0 matrix is
+(q: uint8 or int8 [rows, K/2], d: float32 [rows, K/32]); a Q8_0 matrix or
+activation is (q: int8 [..., K], d: float32 [..., K/32]).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+QK = 32
+QMV_Q4_0 = 4
+QMV_Q8_0 = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmv.so")
+
+STATUS = {0: "QMV_OK", 1: "QMV_E_SHAPE", 2: "QMV_E_FORMAT", 3: "QMV_E_ARG", 4: "QMV_E_ARCH",
+          5: "QMV_E_DEVICE"}
+
+
+class QmvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)}")
+
+
+class QTensor(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("type", ctypes.c_uint8)]
+
+
+class QAct(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("n", ctypes.c_int32)]
+
+
+_lib = None
+
+# name -> argtypes (restype c_int = qmv_status)
+_P = ctypes.c_void_p
+_SIGS = {
+    "qmv_quantize_q8": [ctypes.POINTER(QAct), _P, ctypes.c_int64, _P],
+    "qmv_quantize_weights": [ctypes.POINTER(QTensor), _P, _P],
+    "qmv_matvec_q8": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_matvec_q4": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_matvec_q8_fx": [_P, ctypes.POINTER(QTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_matvec_q4_fx": [_P, ctypes.POINTER(QTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_gemm_q8": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_gemm_q4": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_device_check": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree libqmv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_quantized_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.qmv_status_str.argtypes = [ctypes.c_int]
+        L.qmv_status_str.restype = ctypes.c_char_p
+        L.qmv_last_kernel.argtypes = []
+        L.qmv_last_kernel.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise QmvError(code, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("libqmv takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libqmv takes contiguous tensors")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+    return t
+
+
+def qtensor(q: torch.Tensor, d: torch.Tensor, qtype: int) -> QTensor:
+    """Describe a device Q4_0/Q8_0 matrix (q, d) for the C ABI."""
+    _dev(q, (torch.int8, torch.uint8))
+    _dev(d, torch.float32)
+    rows = d.shape[0]
+    cols = d.shape[-1] * QK
+    return QTensor(q.data_ptr(), d.data_ptr(), rows, cols, qtype)
+
+
+def last_kernel() -> str:
+    return lib().qmv_last_kernel().decode()
+
+
+def status_str(code: int) -> str:
+    return lib().qmv_status_str(code).decode()
+
+
+def qmv_device_check() -> None:
+    _check(lib().qmv_device_check(), "qmv_device_check")
+
+
+def qmv_quantize_q8(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor | None = None):
+    """Q8_0-quantize a float32 device tensor whose last dim is a multiple of
+    32.  Returns (q int8 like x, d float32 [..., K/32])."""
+    _dev(x, torch.float32)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty(x.shape[:-1] + (x.shape[-1] // QK,), dtype=torch.float32, device=x.device)
+    act = QAct(q.data_ptr(), d.data_ptr(), 0)
+    _check(lib().qmv_quantize_q8(ctypes.byref(act), x.data_ptr(), x.numel(), _stream()), "qmv_quantize_q8")
+    return q, d
+
+
+def qmv_quantize_weights(w: torch.Tensor, qtype: int, q: torch.Tensor | None = None,
+                         d: torch.Tensor | None = None):
+    """Quantize a float32 [rows, K] device matrix to Q4_0 or Q8_0."""
+    _dev(w, torch.float32)
+    rows, cols = w.shape
+    if q is None:
+        q = torch.empty((rows, cols // 2 if qtype == QMV_Q4_0 else cols),
+                        dtype=torch.uint8 if qtype == QMV_Q4_0 else torch.int8, device=w.device)
+    if d is None:
+        d = torch.empty((rows, cols // QK), dtype=torch.float32, device=w.device)
+    W = QTensor(q.data_ptr(), d.data_ptr(), rows, cols, qtype)
+    _check(lib().qmv_quantize_weights(ctypes.byref(W), w.data_ptr(), _stream()), "qmv_quantize_weights")
+    return q, d
+
+
+def _out(y, n, like):
+    if y is None:
+        return torch.zeros(n, dtype=torch.float32, device=like.device)
+    _dev(y, torch.float32)
+    return y
+
+
+def _matvec(qtype, fname, wq, wd, xq, xd, r0, r1, y):
+    W = qtensor(wq, wd, qtype)
+    _dev(xq, torch.int8)
+    _dev(xd, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    y = _out(y, W.rows, wd)
+    act = QAct(xq.data_ptr(), xd.data_ptr(), xq.numel())
+    _check(getattr(lib(), fname)(y.data_ptr(), ctypes.byref(W), ctypes.byref(act), r0, r1, _stream()), fname)
+    return y
+
+
+def qmv_matvec_q8(wq, wd, xq, xd, r0=None, r1=None, y=None):
+    return _matvec(QMV_Q8_0, "qmv_matvec_q8", wq, wd, xq, xd, r0, r1, y)
+
+
+def qmv_matvec_q4(wq, wd, xq, xd, r0=None, r1=None, y=None):
+    return _matvec(QMV_Q4_0, "qmv_matvec_q4", wq, wd, xq, xd, r0, r1, y)
+
+
+def _matvec_fx(qtype, fname, wq, wd, x, r0, r1, y, xq_out):
+    W = qtensor(wq, wd, qtype)
+    _dev(x, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    y = _out(y, W.rows, wd)
+    act = None
+    if xq_out is not None:
+        q, d = xq_out
+        _dev(q, torch.int8)
+        _dev(d, torch.float32)
+        act = QAct(q.data_ptr(), d.data_ptr(), 0)
+    code = getattr(lib(), fname)(y.data_ptr(), ctypes.byref(W), x.data_ptr(),
+                                 ctypes.byref(act) if act is not None else None, r0, r1, _stream())
+    _check(code, fname)
+    return y
+
+
+def qmv_matvec_q8_fx(wq, wd, x, r0=None, r1=None, y=None, xq_out=None):
+    """y = W x with x float32 quantized inside the kernel.  xq_out, if given,
+    is a (q int8 [K], d float32 [K/32]) pair receiving the quantized x."""
+    return _matvec_fx(QMV_Q8_0, "qmv_matvec_q8_fx", wq, wd, x, r0, r1, y, xq_out)
+
+
+def qmv_matvec_q4_fx(wq, wd, x, r0=None, r1=None, y=None, xq_out=None):
+    return _matvec_fx(QMV_Q4_0, "qmv_matvec_q4_fx", wq, wd, x, r0, r1, y, xq_out)
+
+
+def _gemm(qtype, fname, wq, wd, xq, xd, r0, r1, Y):
+    W = qtensor(wq, wd, qtype)
+    X = qtensor(xq, xd, QMV_Q8_0)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    if Y is None:
+        Y = torch.zeros((X.rows, W.rows), dtype=torch.float32, device=wd.device)
+    _dev(Y, torch.float32)
+    _check(getattr(lib(), fname)(Y.data_ptr(), ctypes.byref(W), ctypes.byref(X), r0, r1, _stream()), fname)
+    return Y
+
+
+def qmv_gemm_q8(wq, wd, xq, xd, r0=None, r1=None, Y=None):
+    """Y[m, r] for all M rows of the Q8_0 activation (xq [M, K], xd [M, K/32])."""
+    return _gemm(QMV_Q8_0, "qmv_gemm_q8", wq, wd, xq, xd, r0, r1, Y)
+
+
+def qmv_gemm_q4(wq, wd, xq, xd, r0=None, r1=None, Y=None):
+    return _gemm(QMV_Q4_0, "qmv_gemm_q4", wq, wd, xq, xd, r0, r1, Y)

@@ -5,20 +5,22 @@ the workloads; it performs none of the method's arithmetic (no
 quantization, no dot products).  Both the HIP path and the CPU oracle take
 their inputs from here.
 
-Recipe (each tensor has its own generator, so any one tensor can be drawn
-without drawing the others):
-  * generator = numpy PCG64 seeded by SeedSequence(entropy=workload seed,
-    spawn_key=(kind, index, m)), kind 0 for weights, 1 for activations,
-    index = the tensor's position in the workload's list, m = activation
-    rows (0 for weights);
-  * values = standard_normal(float32) * sigma   (sigma 0.02 weights, 1.0
-    activations);
+Recipe (each tensor, and each 4 Mi-element chunk of it, has its own
+generator, so any one tensor can be drawn without drawing the others and
+the chunks can be filled on several threads with the same result):
+  * generator of chunk c = numpy PCG64 seeded by SeedSequence(entropy =
+    workload seed, spawn_key = (kind, index, m, c)), kind 0 for weights, 1
+    for activations, index = the tensor's position in the workload's list,
+    m = activation rows (0 for weights);
+  * values = standard_normal(float32) * sigma (sigma 0.02 for weights, 1.0
+    for activations), chunk c covering flat elements [c * 2^22, (c+1) * 2^22);
   * activation outliers (Llama-7B FFN stack): exactly round(0.01 * m * K)
-    distinct elements, drawn without replacement from the same generator
-    after the values, are multiplied by 20;
+    distinct elements, drawn without replacement by the generator of chunk
+    id 2^31 - 1, are multiplied by 20;
   * all-zero weight blocks (Qwen2.5-0.5B shapes): exactly
     round(0.01 * rows * K / 32) distinct 32-element blocks, drawn without
-    replacement after the values, are set to 0 before quantization.
+    replacement by the generator of chunk id 2^31 - 1, are set to 0 before
+    quantization.
 
 The shapes follow the model dimensions the pages quote for decode: a
 TinyLlama-1.1B layer, a Llama-7B FFN stack (1 x 4096 x 11008 products), a
@@ -27,6 +29,8 @@ models are stand-ins by shape only.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -122,21 +126,50 @@ WORKLOADS = {
 }
 
 
-def _rng(seed: int, kind: int, index: int, m: int) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(kind, index, m)))
+CHUNK = 1 << 22
+SELECT = (1 << 31) - 1   # chunk id of the generator that picks outliers / zero blocks
+
+
+def _rng(seed: int, kind: int, index: int, m: int, chunk: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(kind, index, m, chunk)))
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normal_fill(out: np.ndarray, seed: int, kind: int, index: int, m: int, sigma: float):
+    flat = out.reshape(-1)
+    nch = (flat.size + CHUNK - 1) // CHUNK
+
+    def fill(c):
+        seg = flat[c * CHUNK:(c + 1) * CHUNK]
+        _rng(seed, kind, index, m, c).standard_normal(out=seg, dtype=np.float32)
+        if sigma != 1.0:
+            seg *= np.float32(sigma)
+
+    if nch <= 1:
+        for c in range(nch):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(min(_threads(), nch)) as ex:
+            list(ex.map(fill, range(nch)))
 
 
 def weight(wl: Workload, name: str) -> np.ndarray:
     """float32 [rows, cols] weight draw for matrix `name` of workload `wl`."""
     idx = [mt.name for mt in wl.matrices].index(name)
     mt = wl.matrices[idx]
-    g = _rng(wl.seed, 0, idx, 0)
-    w = g.standard_normal((mt.rows, mt.cols), dtype=np.float32)
-    w *= np.float32(0.02)
+    w = np.empty((mt.rows, mt.cols), np.float32)
+    _normal_fill(w, wl.seed, 0, idx, 0, 0.02)
     if wl.zero_block_frac > 0.0:
         nblk = mt.rows * mt.cols // QK
         cnt = int(round(wl.zero_block_frac * nblk))
-        blk = g.choice(nblk, size=cnt, replace=False)
+        blk = _rng(wl.seed, 0, idx, 0, SELECT).choice(nblk, size=cnt, replace=False)
         w.reshape(nblk, QK)[blk] = 0.0
     return w
 
@@ -145,11 +178,11 @@ def activation(wl: Workload, act: str, m: int = 1) -> np.ndarray:
     """float32 [m, K] activation draw `act` of workload `wl` at m rows."""
     idx = [a for a, _ in wl.acts].index(act)
     k = wl.acts[idx][1]
-    g = _rng(wl.seed, 1, idx, m)
-    x = g.standard_normal((m, k), dtype=np.float32)
+    x = np.empty((m, k), np.float32)
+    _normal_fill(x, wl.seed, 1, idx, m, 1.0)
     if wl.outlier_frac > 0.0:
         cnt = int(round(wl.outlier_frac * m * k))
-        sel = g.choice(m * k, size=cnt, replace=False)
+        sel = _rng(wl.seed, 1, idx, m, SELECT).choice(m * k, size=cnt, replace=False)
         x.reshape(-1)[sel] *= np.float32(wl.outlier_mult)
     return x
 

@@ -1,0 +1,188 @@
+/*
+ * qmv.h -- C ABI of libqmv: block-quantized weight x activation products
+ * for LLM decode on one AMD Instinct MI355X (gfx950).
+ *
+ * Formats (Legacy-ISA ML Inference Runtime -- Design Spec, section 4,
+ * "Quantization Formats"):
+ *   - blocks of QK = 32 consecutive elements along K; every K is a multiple
+ *     of 32;
+ *   - Q8_0: one int8 per element, clamped to [-127, 127], plus one float32
+ *     scale d per block (value = q * d);
+ *   - Q4_0: 16 bytes per block, byte j holds element j in its low nibble and
+ *     element j + 16 in its high nibble, value = (nibble - 8) * d, plus one
+ *     float32 scale d per block;
+ *   - structure-of-arrays: all quant bytes of a tensor in one array q, all
+ *     scales in a second array d, both row-major over (row, block).
+ *     Row r of a rows x cols tensor starts at q + r * cols (Q8_0) or
+ *     q + r * cols / 2 (Q4_0) and at d + r * cols / 32.
+ *
+ * Arithmetic (section 4, "Integer dot per block"): per block the int8 dot
+ * sumi = sum of w * qx is formed exactly in int32; the output is the fp32
+ * sum over blocks of sumi * dw * dx.  The summation order over blocks is
+ * the library's; results are within |y - y_ref| <= 1e-5 * sum_b |sumi * dw
+ * * dx| + 1e-6 of the in-order sum, and quantized activations and every
+ * block sum are bit-exact.
+ *
+ * Memory: every data pointer is a DEVICE pointer owned by the caller (for
+ * example the storage of a torch tensor).  The library allocates nothing,
+ * keeps no state besides a per-device architecture check, and never frees
+ * caller memory.  The qmv_qtensor / qmv_qact structs themselves live in
+ * host memory and are read during the call only.
+ *
+ * Streams: every call is asynchronous on `stream` (a hipStream_t; NULL =
+ * the null stream).  A status of QMV_OK means the work was validated and
+ * enqueued; a fault inside a kernel surfaces at the caller's next
+ * synchronisation.
+ *
+ * Errors (section 6, "Error handling": library functions return a status,
+ * never abort): arguments are checked before anything is enqueued and a
+ * failed check enqueues nothing.  Order of checks: null pointers
+ * (QMV_E_ARG), type tags (QMV_E_FORMAT), shapes (QMV_E_SHAPE), alignment
+ * (QMV_E_ARG), then the device (QMV_E_DEVICE / QMV_E_ARCH).
+ *
+ * Preconditions not checked on the hot path: finite inputs; for
+ * activation quantization a block maximum of 0 or at least FLT_MIN; Q8_0
+ * weight quants in [-127, 127] (-128 is still computed exactly).
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (mirror the spec's section 6 status list, with the
+ * instruction-set check replaced by a device-architecture check). */
+typedef enum {
+    QMV_OK = 0,
+    QMV_E_SHAPE = 1,   /* K % 32 != 0, sizes disagree, bad row range, or a size beyond the documented limits */
+    QMV_E_FORMAT = 2,  /* wrong type tag for the call */
+    QMV_E_ARG = 3,     /* null or misaligned pointer */
+    QMV_E_ARCH = 4,    /* the current device is not gfx950 */
+    QMV_E_DEVICE = 5   /* no usable device, or the HIP runtime rejected a launch */
+} qmv_status;
+
+/* Type tags of qmv_qtensor.type (numeric values are this library's). */
+enum { QMV_Q4_0 = 4, QMV_Q8_0 = 8 };
+
+/* Block length. */
+#define QMV_QK 32
+
+/* Largest K accepted by the single-row and few-row products: the quantized
+ * activation rows are staged in on-chip LDS, 40 bytes per 32-element block
+ * per activation row, within 160 KiB. */
+#define QMV_LDS_BYTES (160 * 1024)
+
+/* A quantized weight matrix (spec section 4, ml_qtensor): rows x cols,
+ * q = rows * cols bytes (Q8_0) or rows * cols / 2 bytes (Q4_0),
+ * d = rows * cols / 32 floats.  q must be 16-byte aligned, d 4-byte
+ * aligned. */
+typedef struct {
+    int8_t *q;
+    float *d;
+    int32_t rows;
+    int32_t cols;
+    uint8_t type;      /* QMV_Q4_0 or QMV_Q8_0 */
+} qmv_qtensor;
+
+/* A Q8_0 activation vector (spec section 4, ml_qact): q = n bytes, d = n/32
+ * floats.  q must be 16-byte aligned, d 4-byte aligned. */
+typedef struct {
+    int8_t *q;
+    float *d;
+    int32_t n;
+} qmv_qact;
+
+/* ---------------------------------------------------------------------------
+ * qmv_quantize_q8 -- Q8_0 quantization of k floats (spec section 5,
+ * ml_k_quantize_q8; rule of section 4 "Q8 quantization" with the rounding
+ * of section 5): per block d = amax / 127, q = trunc(x * (127 / amax) +
+ * copysign(0.5, x)) with each float operation rounded separately,
+ * amax = 0 giving d = 0 and q = 0.
+ *   out->q : k bytes (16-byte aligned), out->d : k/32 floats.
+ *   x      : k floats, 16-byte aligned.  k % 32 == 0, 0 <= k <= INT32_MAX.
+ * Several activation rows of K elements each are quantized by one call
+ * with k = M * K (blocks never straddle rows because K % 32 == 0).
+ * Sets out->n = k.  k == 0 enqueues nothing and accepts null data
+ * pointers (out itself must not be null).
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_quantize_q8(qmv_qact *out, const float *x, int64_t k, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * qmv_quantize_weights -- quantize a row-major float32 matrix w
+ * (W->rows x W->cols, 16-byte aligned) into W's format.
+ *   QMV_Q8_0 : the Q8_0 rule above (the same rule the spec applies to Q8_0
+ *              weights and activations);
+ *   QMV_Q4_0 : the spec fixes only the Q4_0 storage and that quantization is
+ *              symmetric; this library's rule is the Q8_0 rule with 7 in
+ *              place of 127 (d = amax / 7, value = clamp(trunc(x * (7 / amax)
+ *              + copysign(0.5, x)), -8, 7), nibble = value + 8).
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_quantize_weights(const qmv_qtensor *W, const float *w, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * qmv_matvec_q8 / qmv_matvec_q4 -- y[r] = sum_b sumi(r, b) * dw(r, b) *
+ * dx(b) for r in [r0, r1) (spec section 5, ml_k_matvec_q8 / _q4: rows
+ * [r0, r1), the caller splits rows).
+ *   y : W->rows floats indexed by the absolute row r; entries outside
+ *       [r0, r1) are not written.
+ *   W : type QMV_Q8_0 (resp. QMV_Q4_0).  x : Q8_0 activation, x->n == W->cols.
+ *   0 <= r0 <= r1 <= W->rows; r0 == r1 enqueues nothing.
+ *   Limit: 40 * W->cols / 32 <= QMV_LDS_BYTES (K <= 131072).
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_matvec_q8(float *y, const qmv_qtensor *W, const qmv_qact *x,
+                         int32_t r0, int32_t r1, void *stream);
+qmv_status qmv_matvec_q4(float *y, const qmv_qtensor *W, const qmv_qact *x,
+                         int32_t r0, int32_t r1, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * qmv_matvec_q8_fx / qmv_matvec_q4_fx -- the same product from a float32
+ * activation x (W->cols floats, 16-byte aligned): the activation is
+ * quantized to Q8_0 inside the kernel (the rule of qmv_quantize_q8, the
+ * same bits) and never leaves the chip.  If xq is not NULL, xq->q (W->cols
+ * bytes) and xq->d (W->cols / 32 floats) also receive the quantized
+ * activation and xq->n is set to W->cols.
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_matvec_q8_fx(float *y, const qmv_qtensor *W, const float *x,
+                            qmv_qact *xq, int32_t r0, int32_t r1, void *stream);
+qmv_status qmv_matvec_q4_fx(float *y, const qmv_qtensor *W, const float *x,
+                            qmv_qact *xq, int32_t r0, int32_t r1, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * qmv_gemm_q8 / qmv_gemm_q4 -- the product for M activation rows at once:
+ * X is a Q8_0 qmv_qtensor with X->rows = M, X->cols = W->cols, each row
+ * quantized on its own; Y is M x W->rows row-major and
+ *   Y[m * W->rows + r] = sum_b sumi(m, r, b) * dw(r, b) * dx(m, b)
+ * for every m < M and r in [r0, r1); other entries are not written.
+ * The spec defines the single-row product; this applies it to each row of
+ * X while every weight byte is read from memory once.
+ *   1 <= M: M <= 8 runs on the dot-product path (limit 40 * M * K / 32 <=
+ *   QMV_LDS_BYTES); M >= 9 runs on the matrix-core path (no K limit).
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
+                       int32_t r0, int32_t r1, void *stream);
+qmv_status qmv_gemm_q4(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
+                       int32_t r0, int32_t r1, void *stream);
+
+/* Text of a status code (static storage). */
+const char *qmv_status_str(qmv_status s);
+
+/* Name of the kernel variant the calling thread's last successful call
+ * enqueued ("" before any); with the environment variable QMV_DIAG=1 every
+ * launch is also printed to stderr.  The string is thread-local and valid
+ * until the thread's next call. */
+const char *qmv_last_kernel(void);
+
+/* Checks that the current HIP device is usable and is a gfx950, caching the
+ * answer per device (every call does this on its own; this entry point
+ * lets a caller check up front).  Returns QMV_OK, QMV_E_DEVICE or
+ * QMV_E_ARCH. */
+qmv_status qmv_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

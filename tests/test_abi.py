@@ -1,0 +1,159 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+public header declares, and rejects bad arguments with the documented
+status codes before touching any device.  No compute call runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+LIB = os.path.join(ROOT, "block_quantized_decode_amd", "libqmv.so")
+
+OK, E_SHAPE, E_FORMAT, E_ARG, E_ARCH, E_DEVICE = range(6)
+Q4, Q8 = 4, 8
+
+
+class QT(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("type", ctypes.c_uint8)]
+
+
+class QA(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("n", ctypes.c_int32)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from block_quantized_decode_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    for f in declared_functions():
+        getattr(L, f).restype = ctypes.c_int
+    L.qmv_status_str.restype = ctypes.c_char_p
+    L.qmv_last_kernel.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_product_calls():
+    names = declared_functions()
+    for n in ("qmv_quantize_q8", "qmv_quantize_weights", "qmv_matvec_q8", "qmv_matvec_q4",
+              "qmv_matvec_q8_fx", "qmv_matvec_q4_fx", "qmv_gemm_q8", "qmv_gemm_q4",
+              "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in qmv.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.qmv_status_str(code).decode().startswith("QMV_")
+    assert lib.qmv_last_kernel().decode() == ""
+
+
+# Fake, never-dereferenced addresses: every call below fails validation on
+# the host, before any device is queried or any kernel launched.
+A = 0x10000          # 64 KiB-aligned
+B = 0x20000
+Y = 0x30000
+
+
+def _w(rows=8, cols=64, t=Q8, q=A, d=B):
+    return QT(q, d, rows, cols, t)
+
+
+def _x(n=64, q=A + 0x1000, d=B + 0x1000):
+    return QA(q, d, n)
+
+
+@pytest.mark.parametrize("fn,t", [("qmv_matvec_q8", Q8), ("qmv_matvec_q4", Q4)])
+def test_matvec_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    other = Q4 if t == Q8 else Q8
+    W, X = _w(t=t), _x()
+    assert f(None, ctypes.byref(W), ctypes.byref(X), 0, 8, None) == E_ARG            # null y
+    assert f(Y, None, ctypes.byref(X), 0, 8, None) == E_ARG                          # null W
+    assert f(Y, ctypes.byref(W), None, 0, 8, None) == E_ARG                          # null x
+    assert f(Y, ctypes.byref(_w(t=other)), ctypes.byref(X), 0, 8, None) == E_FORMAT  # wrong type
+    assert f(Y, ctypes.byref(_w(t=7)), ctypes.byref(X), 0, 8, None) == E_FORMAT      # unknown type
+    assert f(Y, ctypes.byref(_w(t=t, cols=48)), ctypes.byref(_x(48)), 0, 8, None) == E_SHAPE  # K % 32
+    assert f(Y, ctypes.byref(W), ctypes.byref(_x(96)), 0, 8, None) == E_SHAPE       # x->n != K
+    assert f(Y, ctypes.byref(W), ctypes.byref(X), -1, 8, None) == E_SHAPE           # r0 < 0
+    assert f(Y, ctypes.byref(W), ctypes.byref(X), 0, 9, None) == E_SHAPE            # r1 > rows
+    assert f(Y, ctypes.byref(W), ctypes.byref(X), 5, 4, None) == E_SHAPE            # r0 > r1
+    big = _w(t=t, cols=32 * 5000)
+    assert f(Y, ctypes.byref(big), ctypes.byref(_x(32 * 5000)), 0, 8, None) == E_SHAPE  # beyond LDS limit
+    assert f(Y, ctypes.byref(_w(t=t, q=A + 8)), ctypes.byref(X), 0, 8, None) == E_ARG   # q not 16-aligned
+    assert f(Y, ctypes.byref(_w(t=t, d=B + 2)), ctypes.byref(X), 0, 8, None) == E_ARG   # d not 4-aligned
+    assert f(Y, ctypes.byref(W), ctypes.byref(_x(q=A + 0x1004)), 0, 8, None) == E_ARG  # x q misaligned
+    assert f(Y + 2, ctypes.byref(W), ctypes.byref(X), 0, 8, None) == E_ARG            # y misaligned
+
+
+@pytest.mark.parametrize("fn,t", [("qmv_matvec_q8_fx", Q8), ("qmv_matvec_q4_fx", Q4)])
+def test_matvec_fx_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    W = _w(t=t)
+    assert f(Y, ctypes.byref(W), None, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(W), A + 0x1008, None, 0, 8, None) == E_ARG                # x not 16-aligned
+    bad = QA(0, B, 0)
+    assert f(Y, ctypes.byref(W), A + 0x1000, ctypes.byref(bad), 0, 8, None) == E_ARG  # xq with null q
+    assert f(Y, ctypes.byref(_w(t=Q4 if t == Q8 else Q8)), A + 0x1000, None, 0, 8, None) == E_FORMAT
+    assert f(Y, ctypes.byref(W), A + 0x1000, None, 3, 2, None) == E_SHAPE
+
+
+@pytest.mark.parametrize("fn,t", [("qmv_gemm_q8", Q8), ("qmv_gemm_q4", Q4)])
+def test_gemm_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    W = _w(t=t)
+    X = QT(A + 0x1000, B + 0x1000, 4, 64, Q8)
+    assert f(None, ctypes.byref(W), ctypes.byref(X), 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(W), None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(W), ctypes.byref(QT(A, B, 4, 64, Q4)), 0, 8, None) == E_FORMAT  # X must be Q8_0
+    assert f(Y, ctypes.byref(W), ctypes.byref(QT(A, B, 4, 96, Q8)), 0, 8, None) == E_SHAPE  # K mismatch
+    assert f(Y, ctypes.byref(W), ctypes.byref(QT(A, B, 0, 64, Q8)), 0, 8, None) == E_SHAPE  # M = 0
+    assert f(Y, ctypes.byref(W), ctypes.byref(X), 0, 9, None) == E_SHAPE
+    assert f(Y, ctypes.byref(W), ctypes.byref(QT(A + 4, B, 4, 64, Q8)), 0, 8, None) == E_ARG
+
+
+def test_quantize_validation(lib):
+    act = QA(A, B, 0)
+    assert lib.qmv_quantize_q8(None, ctypes.c_void_p(Y), ctypes.c_int64(64), None) == E_ARG
+    assert lib.qmv_quantize_q8(ctypes.byref(act), None, ctypes.c_int64(64), None) == E_ARG
+    empty = QA(0, 0, 5)
+    assert lib.qmv_quantize_q8(ctypes.byref(empty), None, ctypes.c_int64(0), None) == OK  # k = 0: nothing to do
+    assert empty.n == 0
+    assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(40), None) == E_SHAPE
+    assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(-32), None) == E_SHAPE
+    assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y + 4), ctypes.c_int64(64), None) == E_ARG
+    W = _w(t=Q4)
+    assert lib.qmv_quantize_weights(ctypes.byref(W), None, None) == E_ARG
+    assert lib.qmv_quantize_weights(ctypes.byref(_w(t=5)), ctypes.c_void_p(Y), None) == E_FORMAT
+    assert lib.qmv_quantize_weights(ctypes.byref(_w(t=Q8, cols=33)), ctypes.c_void_p(Y), None) == E_SHAPE
+
+
+def test_no_device_is_an_error_not_a_crash(lib):
+    """Valid arguments on a machine without a usable GPU: the device check
+    reports QMV_E_DEVICE (or QMV_E_ARCH on a non-gfx950 GPU) and nothing is
+    launched.  Skipped where a gfx950 is present, since the fake pointers
+    would then be used."""
+    st = lib.qmv_device_check()
+    if st == OK:
+        pytest.skip("a gfx950 device is present")
+    assert st in (E_DEVICE, E_ARCH)
+    W, X = _w(t=Q8), _x()
+    assert lib.qmv_matvec_q8(Y, ctypes.byref(W), ctypes.byref(X), 0, 8, None) == st
+    assert lib.qmv_matvec_q4_fx(Y, ctypes.byref(_w(t=Q4)), A + 0x1000, None, 0, 8, None) == st
+    act = QA(A, B, 0)
+    assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(64), None) == st
+    assert lib.qmv_last_kernel().decode() == ""
