@@ -24,7 +24,7 @@ __device__ __forceinline__ int quant_round(float x, float id, int lo, int hi) {
 #pragma clang fp contract(off)
     float v = x * id;
     float t = v + copysignf(0.5f, x);
-    int q = (int)truncf(t);
+    int q = (int)t;  // float -> int conversion truncates toward zero
     return min(max(q, lo), hi);
 }
 
@@ -104,6 +104,32 @@ __device__ __forceinline__ void quant_q8_lane(const float4 (&v)[8], v4i &lo, v4i
 #pragma unroll
     for (int i = 0; i < 8; ++i) s = __builtin_amdgcn_sdot4(w[i], 0x01010101, s, false);
     qsum = s;
+}
+
+// Q8_0 quantization of one block held by an aligned group of 4 lanes, 8
+// elements per lane (lane c of the group holds elements 8c..8c+7 in a and
+// b).  The same arithmetic as quant_q8_group8 (the block maximum is exact
+// and the two divisions and the per-element rounding are the same
+// operations), hence the same bits, with half the lanes repeating the
+// divisions.  Returns this lane's 8 quants packed little-endian in an int2;
+// d receives the block scale and qsum the sum of the block's 32 quants (both
+// identical in the 4 lanes).
+__device__ __forceinline__ int2 quant_q8_group4(float4 a, float4 b, float &d, int &qsum) {
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                       fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    amax = fmaxf(amax, __int_as_float(dpp_xor1(__float_as_int(amax))));
+    amax = fmaxf(amax, __int_as_float(dpp_xor2(__float_as_int(amax))));
+    d = amax / 127.0f;
+    const float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+    const int w0 = pack4(quant_round(a.x, id, -127, 127), quant_round(a.y, id, -127, 127),
+                         quant_round(a.z, id, -127, 127), quant_round(a.w, id, -127, 127));
+    const int w1 = pack4(quant_round(b.x, id, -127, 127), quant_round(b.y, id, -127, 127),
+                         quant_round(b.z, id, -127, 127), quant_round(b.w, id, -127, 127));
+    int s = __builtin_amdgcn_sdot4(w0, 0x01010101, __builtin_amdgcn_sdot4(w1, 0x01010101, 0, false), false);
+    s += dpp_xor1(s);
+    s += dpp_xor2(s);
+    qsum = s;
+    return make_int2(w0, w1);
 }
 
 // Q4_0 weight quantization of one block held by an aligned group of 8

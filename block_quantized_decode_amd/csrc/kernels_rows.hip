@@ -7,28 +7,33 @@
 //   sumi = exact int32 dot of the 32 weight and activation quants,
 // for r in [r0, r1).  The spec's CPU kernels take 4 rows at a time so that
 // one activation-block load serves 4 weight rows; here a wavefront takes 4
-// rows at a time and each of its 64 lanes owns one block column of them.
+// rows at a time (or 2 or 1 for matrices with few rows) and each of its 64
+// lanes owns block columns l, l + 64, l + 128, ... of them.
 //
-// Layout of the work:
-//   * the activation (M rows of K) is staged once per workgroup in LDS as
-//     two 16-byte halves per block plus {dx, 8 * sum of quants}; with a
-//     float32 activation (FX) the staging is the Q8_0 quantization itself,
-//     8 lanes per 32-element block (coalesced 1 KiB loads per wavefront,
-//     block max and quant sum by DPP within the 8 lanes), so the quantized
-//     activation never leaves the chip;
-//   * a wavefront walks "quads" of 4 weight rows; lane l takes blocks
-//     l, l + 64, l + 128, ... of the 4 rows, so every weight load of the
-//     wavefront is a contiguous 1 KiB (Q4_0) or 2 KiB (Q8_0) run per row
-//     (global_load_dwordx4, non-temporal: weights are streamed once);
-//   * the weight loads of the next step are issued before the current step
-//     is computed (register double buffering), and the very first step's
-//     loads are issued before the activation staging, so staging latency
-//     hides under the first HBM round trip;
+// How the work is laid out on the chip:
+//   * one wavefront per unit of R rows (R = 4, 2 or 1, picked so that every
+//     CU gets 8 - 16 wavefronts), and the grid covers all units: every
+//     weight byte a wavefront needs (its rows, whole length, up to 8 column
+//     groups = K 16384) is requested at once, so the memory system sees the
+//     whole matrix at the start and streams it at full rate; a CU holds its
+//     ~1/256 share of a 28 MB matrix in registers with room to spare;
+//   * weights are read with raw buffer loads: base and byte range live in a
+//     wave-uniform descriptor covering only the rows below r1, so rows past
+//     r1 and blocks past the row end read zeros without touching memory,
+//     and no load sits under a branch;
+//   * the activation is brought into LDS first, with direct-to-LDS buffer
+//     loads (1 KiB of contiguous float32 per wavefront instruction, no
+//     registers), so its requests go out ahead of the weight stream;
+//   * the workgroup then quantizes it in LDS (FX: Q8_0, one lane per
+//     32-element block, reading the block in a lane-rotated chunk order
+//     that avoids LDS bank conflicts) into two 16-byte halves
+//     per block plus dx and 8 * sum(q) per block; pre-quantized activations
+//     are copied the same way and only their quant sums are formed;
 //   * int8 block dots use v_dot4_i32_i8.  Q4_0 nibbles are used as unsigned
 //     bytes 0..15 (gfx950 has no mixed-sign dot4) and the -8 offset is
 //     folded in exactly: sumi = dot(nibble, qx) - 8 * sum(qx);
-//   * per lane, block sums are scaled and accumulated in fp32, then the
-//     4 * M partial sums of a quad are reduced across the wavefront with a
+//   * per lane, block sums are scaled and accumulated in fp32; the R * M
+//     partial sums of the unit are reduced across the wavefront with a
 //     transposing butterfly and stored by one lane each.
 #include "device_common.h"
 #include "launch.h"
@@ -40,30 +45,56 @@
 namespace qmv {
 namespace {
 
-template <int QT, int UJ>
+constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3, gfx9-family raw buffers
+constexpr int kNT = 2;                 // cache policy: non-temporal (weights are streamed once)
+constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor range used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufFlags);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the
+// wavefront lands at lds + 16 i (the instruction is issued by the whole
+// wavefront; lds must be wave-uniform).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voffset, 0, 0, 0);
+}
+
+// 4 bytes per lane from global memory straight into LDS (lane i at lds + 4 i).
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, voffset, 0, 0, 0);
+}
+
+template <int QT, int J, int R>
 struct WTile {
     static constexpr int QW = (QT == 8) ? 2 : 1;  // 16-byte words per block
-    v4i w[UJ][4][QW];
-    float dw[UJ][4];
+    v4i w[J][R][QW];
+    float dw[J][R];
 };
 
-template <int QT, int UJ>
-__device__ __forceinline__ void load_tile(WTile<QT, UJ> &t, const int8_t *__restrict__ wq,
-                                          const float *__restrict__ wd, int nb, int rb, int r1,
-                                          int j0, int lane) {
+// All weight loads of one unit chunk: rows rb .. rb+R-1 (those below r1),
+// block columns j0 .. j0+J-1 (lane l takes block l + 64 j).
+template <int QT, int J, int R>
+__device__ __forceinline__ void load_tile(WTile<QT, J, R> &t, const int8_t *__restrict__ wq,
+                                          const float *__restrict__ wd, int nb, int rb, int r1, int j0,
+                                          int lane) {
     constexpr int QB = (QT == 8) ? 32 : 16;  // quant bytes per block
-    const size_t rowbytes = (size_t)nb * QB;
+    const int rows_here = max(0, min(R, r1 - rb));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq + (size_t)rb * nb * QB, rows_here * nb * QB);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(wd + (size_t)rb * nb, rows_here * nb * 4);
 #pragma unroll
-    for (int u = 0; u < UJ; ++u) {
-        int b = lane + 64 * (j0 + u);
-        int bb = b < nb ? b : nb - 1;  // out-of-range lanes re-read a valid block; their scale is zeroed
+    for (int u = 0; u < J; ++u) {
+        const int b = lane + 64 * (j0 + u);
+        const int oq = b < nb ? b * QB : kOOB;
+        const int od = b < nb ? b * 4 : kOOB;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int row = min(rb + r, r1 - 1);  // rows past r1 re-read row r1 - 1; their result is not stored
-            const v4i *p = reinterpret_cast<const v4i *>(wq + (size_t)row * rowbytes + (size_t)bb * QB);
-            t.w[u][r][0] = __builtin_nontemporal_load(p);
-            if constexpr (QT == 8) t.w[u][r][WTile<QT, UJ>::QW - 1] = __builtin_nontemporal_load(p + 1);
-            t.dw[u][r] = __builtin_nontemporal_load(wd + (size_t)row * nb + bb);
+        for (int r = 0; r < R; ++r) {
+            t.w[u][r][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, oq, r * nb * QB, kNT));
+            if constexpr (QT == 8)
+                t.w[u][r][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, oq + 16, r * nb * QB, kNT));
+            t.dw[u][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, od, r * nb * 4, kNT));
         }
     }
 }
@@ -98,289 +129,242 @@ __device__ __forceinline__ int block_dot(const v4i *w, v4i xl, v4i xh, int sx8) 
 
 constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2); }
 
-// Activation staging, first half: issue the global loads of one batch of
-// staging tasks into registers.  FX: a task is one float4 (8 tasks per
-// 32-element block, aligned groups of 8 lanes, so a wavefront reads 1 KiB of
-// contiguous activation per load).  Otherwise a task is one 16-byte half of
-// a Q8_0 block (2 tasks per block).  Task indices past the end are
-// redirected to the last block so that every load stays in bounds and every
-// lane group stays complete; their results are not stored.
-template <bool FX, int SU>
-struct StageRegs {
-    float4 v[FX ? SU : 1];
-    v4i q[FX ? 1 : SU];
-    float d[FX ? 1 : SU];
-};
-
-template <int M, bool FX, int SU>
-__device__ __forceinline__ void stage_load(StageRegs<FX, SU> &st, int base, int ntask, int K,
-                                           const float *__restrict__ x, const int8_t *__restrict__ xq,
-                                           const float *__restrict__ xd) {
-    const int nb = K >> 5;
-#pragma unroll
-    for (int i = 0; i < SU; ++i) {
-        int e = base + i * (int)blockDim.x;
-        if (FX) {
-            if (e >= ntask) e = ntask - 8 + (e & 7);
-            const int blk = e >> 3, c = e & 7;
-            const int m = blk / nb, b = blk - m * nb;
-            st.v[i] = *reinterpret_cast<const float4 *>(x + (size_t)m * K + (size_t)b * QK + 4 * c);
-        } else {
-            if (e >= ntask) e = ntask - 2 + (e & 1);
-            const int blk = e >> 1, h = e & 1;
-            const int m = blk / nb, b = blk - m * nb;
-            st.q[i] = *reinterpret_cast<const v4i *>(xq + (size_t)m * K + (size_t)b * QK + 16 * h);
-            st.d[i] = xd[(size_t)m * nb + b];
-        }
-    }
+// LDS layout for M activation rows of nb blocks each:
+//   xlo [M*nb] 16 B  quants 0..15 of each block
+//   xhi [M*nb] 16 B  quants 16..31
+//   xdx [M*nb] 4 B   block scale dx
+//   xsx [M*nb] 4 B   8 * sum of the block's quants (for the Q4_0 offset)
+//   raw [M*K]  4 B   float32 activation as loaded (FX only), rounded up to
+//                    whole 1 KiB chunks
+// (the pre-quantized arrays are rounded up to whole 64-block chunks, the
+// granularity of their direct loads).
+__host__ __device__ constexpr size_t lds_bytes(int M, int K, bool fx) {
+    return (size_t)((M * (K / 32) + 63) / 64 * 64) * 40 + (fx ? ((size_t)M * K * 4 + 1023) / 1024 * 1024 : 0);
 }
 
-// Activation staging, second half: quantize (FX) or sum (pre-quantized) the
-// loaded tasks and write the LDS layout.  All lanes run the cross-lane steps
-// (DPP within groups of 8 or 2 lanes); only live tasks store.
-template <int M, bool FX, int SU>
-__device__ __forceinline__ void stage_store(const StageRegs<FX, SU> &st, int base, int ntask,
-                                            v4i *xlo, v4i *xhi, float2 *meta) {
-#pragma unroll
-    for (int i = 0; i < SU; ++i) {
-        const int e = base + i * (int)blockDim.x;
-        const bool live = e < ntask;
-        if (FX) {
-            const int c = e & 7;
-            const int blk = (live ? e : ntask - 8 + c) >> 3;
-            float d;
-            int s;
-            const int pk = quant_q8_group8(st.v[i], d, s);
-            if (live) {
-                reinterpret_cast<int *>((c < 4) ? (xlo + blk) : (xhi + blk))[c & 3] = pk;
-                if (c == 0) meta[blk] = make_float2(d, __int_as_float(8 * s));
-            }
-        } else {
-            const int h = e & 1;
-            const int blk = (live ? e : ntask - 2 + h) >> 1;
-            const v4i v = st.q[i];
-            int s = dot4(v.x, 0x01010101, dot4(v.y, 0x01010101, dot4(v.z, 0x01010101, dot4(v.w, 0x01010101, 0))));
-            s += dpp_xor1(s);
-            if (live) {
-                (h ? xhi : xlo)[blk] = v;
-                if (h == 0) meta[blk] = make_float2(st.d[i], __int_as_float(8 * s));
-            }
-        }
-    }
-}
-
-template <int QT, int M, bool FX, int UJ, int WPB, int SU>
+template <int QT, int M, bool FX, int J, int R, int WPB>
 __global__ void __launch_bounds__(64 * WPB)
 k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd,
        int32_t rows, int32_t K, const float *__restrict__ x, const int8_t *__restrict__ xq,
        const float *__restrict__ xd, int8_t *__restrict__ xq_out, float *__restrict__ xd_out,
        int32_t r0, int32_t r1) {
-    constexpr int NV = next_pow2(4 * M);
+    constexpr int NV = next_pow2(R * M);
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = K >> 5;
-    v4i *xlo = reinterpret_cast<v4i *>(smem);   // [M][nb] quants 0..15 of each block
-    v4i *xhi = xlo + M * nb;                    // [M][nb] quants 16..31
-    float2 *meta = reinterpret_cast<float2 *>(xhi + M * nb);  // [M][nb] {dx, bits of 8 * sum(q)}
+    const int nblk = M * nb;               // activation blocks
+    const int nblk64 = (nblk + 63) / 64 * 64;
+    v4i *xlo = reinterpret_cast<v4i *>(smem);
+    v4i *xhi = xlo + nblk64;
+    float *xdx = reinterpret_cast<float *>(xhi + nblk64);
+    int *xsx = reinterpret_cast<int *>(xdx + nblk64);
+    float *raw = reinterpret_cast<float *>(xsx + nblk64);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = blockIdx.x * WPB + (tid >> 6);
-    const int nwaves = gridDim.x * WPB;
-    const int nquads = (r1 - r0 + 3) >> 2;
-    const int nj = (nb + 63) >> 6;
-    const int ntask = M * nb * (FX ? 8 : 2);
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave within the workgroup
+    const int unit = blockIdx.x * WPB + wid;                    // this wavefront's R rows
+    const int nunits = (r1 - r0 + R - 1) / R;
+    const bool busy = unit < nunits;
+    const int rb = r0 + R * unit;
+    const int nchunk = (nb + 64 * J - 1) / (64 * J);  // column chunks per row
 
-    // This wave's steps: quads wave, wave + nwaves, ...; each quad takes
-    // nsq steps of UJ block columns.  The loop below is a software pipeline
-    // whose every iteration issues exactly one step of weight loads with no
-    // branch around them, so the compiler's wait counts stay exact (a load
-    // under a branch makes the wait at the join conservative, which would
-    // serialise the prefetch).
-    const int nsq = (nj + UJ - 1) / UJ;
-    const int myq = wave < nquads ? (nquads - 1 - wave) / nwaves + 1 : 0;
-    const int T = myq * nsq;
+    // 1. activation into LDS: direct loads, issued before any weight load
+    if constexpr (FX) {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 4);
+        const int nkb = (M * K * 4 + 1023) >> 10;  // 1 KiB chunks; the tail of the last reads zeros
+        for (int c = wid; c < nkb; c += WPB) load_lds16(rx, raw + 256 * c, 1024 * c + 16 * lane);
+    } else {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(xq, M * K);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(xd, M * nb * 4);
+        for (int c = wid; c < nblk64 / 64; c += WPB) {  // 64 blocks per instruction
+            const int b = 64 * c + lane;
+            const int o = b < nblk ? 32 * b : kOOB;
+            load_lds16(rq, xlo + 64 * c, o);
+            load_lds16(rq, xhi + 64 * c, o + 16);
+            load_lds4(rd, xdx + 64 * c, b < nblk ? 4 * b : kOOB);
+        }
+    }
 
-    // Activation loads first (they hit L2 after the first workgroup touches
-    // x), then the first weight step: loads return in issue order, so the
-    // quantization below waits only for the activation.
-    StageRegs<FX, SU> st;
-    stage_load<M, FX, SU>(st, tid, ntask, K, x, xq, xd);
-
-    WTile<QT, UJ> ta, tb;  // ping-pong weight tiles (no register copies between steps)
+    // 2. this unit's weights (first column chunk), all of it in flight at
+    //    once; an idle wavefront's descriptor has an empty range
+    WTile<QT, J, R> t;
 #if !QMV_STAGE_FIRST
-    load_tile<QT, UJ>(ta, wq, wd, nb, r0 + 4 * min(wave, nquads - 1), r1, 0, lane);
-    __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the quantization below
+    load_tile<QT, J, R>(t, wq, wd, nb, rb, busy ? r1 : rb, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
 #endif
 
-    stage_store<M, FX, SU>(st, tid, ntask, xlo, xhi, meta);
+    // 3. once the activation has landed, quantize / sum it in LDS
+    __syncthreads();
 #if QMV_STAGE_FIRST
+    load_tile<QT, J, R>(t, wq, wd, nb, rb, busy ? r1 : rb, 0, lane);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile<QT, UJ>(ta, wq, wd, nb, r0 + 4 * min(wave, nquads - 1), r1, 0, lane);
 #endif
-    for (int base = tid + SU * 64 * WPB; base < ntask; base += SU * 64 * WPB) {  // large K: more batches
-        stage_load<M, FX, SU>(st, base, ntask, K, x, xq, xd);
-        stage_store<M, FX, SU>(st, base, ntask, xlo, xhi, meta);
+    if constexpr (FX) {
+        // one lane per 32-element block: the two divisions once per block,
+        // no cross-lane steps.  Lane b reads its block's eight 16-byte
+        // chunks in the rotated order (k + b) mod 8, which keeps the 64
+        // lanes' LDS reads at most 2-way bank conflicted; every chunk's 4
+        // quants are written back to their own place in the block, so the
+        // order of the reads changes nothing in the result.
+        for (int blk = tid; blk < nblk; blk += 64 * WPB) {
+            const int rot = blk & 7;
+            const float4 *src = reinterpret_cast<const float4 *>(raw + 32 * blk);
+            float4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = src[(k + rot) & 7];
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
+            const float d = amax / 127.0f;
+            const float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+            int sum = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int c = (k + rot) & 7;  // chunk held in v[k]
+                const int pk = pack4(quant_round(v[k].x, id, -127, 127), quant_round(v[k].y, id, -127, 127),
+                                     quant_round(v[k].z, id, -127, 127), quant_round(v[k].w, id, -127, 127));
+                reinterpret_cast<int *>((c < 4) ? (xlo + blk) : (xhi + blk))[c & 3] = pk;
+                sum = dot4(pk, 0x01010101, sum);
+            }
+            xdx[blk] = d;
+            xsx[blk] = 8 * sum;
+        }
+    } else {
+        for (int e = tid; e < nblk * 2; e += 64 * WPB) {  // 2 lanes per block
+            const int blk = e >> 1, h = e & 1;
+            const v4i v = h ? xhi[blk] : xlo[blk];
+            int s = dot4(v.x, 0x01010101, dot4(v.y, 0x01010101, dot4(v.z, 0x01010101, dot4(v.w, 0x01010101, 0))));
+            s += dpp_xor1(s);
+            if (h == 0) xsx[blk] = 8 * s;
+        }
     }
     __syncthreads();
     if (FX && xq_out != nullptr && blockIdx.x == 0) {  // optional copy of the quantized activation
-        for (int blk = tid; blk < M * nb; blk += 64 * WPB) {
+        for (int blk = tid; blk < nblk; blk += 64 * WPB) {
             const int m = blk / nb, b = blk - m * nb;
             v4i *dst = reinterpret_cast<v4i *>(xq_out + (size_t)m * K + (size_t)b * QK);
             dst[0] = xlo[blk];
             dst[1] = xhi[blk];
-            xd_out[(size_t)m * nb + b] = meta[blk].x;
+            xd_out[(size_t)m * nb + b] = xdx[blk];
         }
     }
-    if (T == 0) return;  // no barrier follows
+    if (!busy) return;  // no barrier follows
 
+    // 4. block dots, scales, fp32 accumulation
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-
-    auto compute = [&](const WTile<QT, UJ> &w, int j0) __attribute__((always_inline)) {
+    for (int ch = 0; ch < nchunk; ++ch) {
+        if (ch > 0) load_tile<QT, J, R>(t, wq, wd, nb, rb, r1, ch * J, lane);  // K beyond 2048 J only
 #pragma unroll
-        for (int u = 0; u < UJ; ++u) {
-            const int b = lane + 64 * (j0 + u);
+        for (int u = 0; u < J; ++u) {
+            const int b = lane + 64 * (ch * J + u);
             const bool ok = b < nb;
             const int bb = ok ? b : nb - 1;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const v4i xl = xlo[m * nb + bb];
                 const v4i xh = xhi[m * nb + bb];
-                const float2 mt = meta[m * nb + bb];
-                const float dx = ok ? mt.x : 0.0f;
-                const int sx8 = __float_as_int(mt.y);
+                const float dx = ok ? xdx[m * nb + bb] : 0.0f;
+                const int sx8 = xsx[m * nb + bb];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = block_dot<QT>(w.w[u][r], xl, xh, sx8);
-                    acc[m * 4 + r] = fmaf((float)s, w.dw[u][r] * dx, acc[m * 4 + r]);
+                for (int r = 0; r < R; ++r) {
+                    const int s = block_dot<QT>(t.w[u][r], xl, xh, sx8);
+                    acc[m * R + r] = fmaf((float)s, t.dw[u][r] * dx, acc[m * R + r]);
                 }
             }
         }
-    };
-    // quad finished: reduce the 4*M partial sums over the wavefront, store, reset
-    auto finish_quad = [&](int q) __attribute__((always_inline)) {
-        const float tot = wave_reduce_transpose<NV>(acc);
-        const int idx = reduce_index<NV>(lane);
-        const int m = idx >> 2, r = idx & 3;
-        const int row = r0 + 4 * q + r;
-        if (reduce_owner<NV>(lane) && m < M && row < r1) y[(size_t)m * rows + row] = tot;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-    };
+    }
 
-    // Step t+1 is always in flight while step t is computed.  Tiles ta / tb
-    // alternate, so there are no register copies (a copy of a tile whose
-    // loads are still in flight would force a wait for them).
-    int quad = wave, jj = 0;     // step t
-    auto advance = [&](int &q, int &j) __attribute__((always_inline)) {
-        j += UJ;
-        if (j >= nj) {
-            j = 0;
-            q += nwaves;
-        }
-    };
-    int t = 0;
-    while (t + 2 < T) {
-        int q1 = quad, j1 = jj;
-        advance(q1, j1);
-        load_tile<QT, UJ>(tb, wq, wd, nb, r0 + 4 * q1, r1, j1, lane);
-        __builtin_amdgcn_sched_barrier(0);  // loads of the next step go out before this step's math
-        compute(ta, jj);
-        if (j1 == 0) finish_quad(quad);
-        int q2 = q1, j2 = j1;
-        advance(q2, j2);
-        load_tile<QT, UJ>(ta, wq, wd, nb, r0 + 4 * q2, r1, j2, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(tb, j1);
-        if (j2 == 0) finish_quad(q1);
-        quad = q2;
-        jj = j2;
-        t += 2;
-    }
-    if (t + 1 < T) {
-        int q1 = quad, j1 = jj;
-        advance(q1, j1);
-        load_tile<QT, UJ>(tb, wq, wd, nb, r0 + 4 * q1, r1, j1, lane);
-        __builtin_amdgcn_sched_barrier(0);  // loads of the next step go out before this step's math
-        compute(ta, jj);
-        if (j1 == 0) finish_quad(quad);
-        compute(tb, j1);
-        finish_quad(q1);
-    } else {
-        compute(ta, jj);
-        finish_quad(quad);
-    }
+    // 5. reduce the R*M partial sums over the wavefront and store
+    const float tot = wave_reduce_transpose<NV>(acc);
+    const int idx = reduce_index<NV>(lane);
+    const int m = idx / R, r = idx % R;
+    const int row = rb + r;
+    if (reduce_owner<NV>(lane) && m < M && row < r1) y[(size_t)m * rows + row] = tot;
 }
 
-template <int QT, int M, bool FX, int UJ, int WPB, int SU>
+template <int QT, int M, bool FX, int J, int R, int WPB>
 hipError_t launch_rows_t(const RowsArgs &a, hipStream_t s, const char **name) {
     static char kname[96];
-    auto kern = k_rows<QT, M, FX, UJ, WPB, SU>;
-    const int nb = a.K / QK;
-    const size_t lds = (size_t)M * nb * 40;
+    auto kern = k_rows<QT, M, FX, J, R, WPB>;
+    const size_t lds = lds_bytes(M, a.K, FX);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    const int nquads = (a.r1 - a.r0 + 3) / 4;
-    int grid = (nquads + WPB - 1) / WPB;
-    if (grid > a.max_groups) grid = a.max_groups;
-    if (grid < 1) grid = 1;
+    const int nunits = (a.r1 - a.r0 + R - 1) / R;
+    const int grid = (nunits + WPB - 1) / WPB;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq,
                        a.xd, a.xq_out, a.xd_out, a.r0, a.r1);
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "rows_q%d_m%d%s_u%d_w%d_s%d", QT, M, FX ? "_fx" : "", UJ, WPB, SU);
+    if (kname[0] == 0)
+        snprintf(kname, sizeof kname, "rows_q%d_m%d%s_j%d_r%d_w%d", QT, M, FX ? "_fx" : "", J, R, WPB);
     *name = kname;
     return hipGetLastError();
 }
 
-// Staging batch size: tasks per thread per batch (one batch covers the
-// whole activation of the common shapes).
-template <int QT, int M, bool FX, int UJ, int WPB>
-hipError_t launch_rows_s(const RowsArgs &a, hipStream_t s, const char **name) {
-    const int ntask = M * (a.K / QK) * (FX ? 8 : 2);
-    const int per = (ntask + 64 * WPB - 1) / (64 * WPB);
-    if (per <= 1) return launch_rows_t<QT, M, FX, UJ, WPB, 1>(a, s, name);
-    if (per <= 2) return launch_rows_t<QT, M, FX, UJ, WPB, 2>(a, s, name);
-    if (per <= 4) return launch_rows_t<QT, M, FX, UJ, WPB, 4>(a, s, name);
-    return launch_rows_t<QT, M, FX, UJ, WPB, 6>(a, s, name);
+// Column groups held per lane at once: the whole row when it fits
+// (K <= 2048 J), else chunks of J.  J is capped so that the weight
+// registers plus the R * M accumulators stay within the 256-VGPR file
+// without spilling: Q4_0 8 / 6 / 2 and Q8_0 4 / 2 column groups for
+// M <= 2 / M <= 4 / larger M.
+template <int QT, int M>
+constexpr int jmax() {
+    return QT == 4 ? (M <= 2 ? 8 : (M <= 4 ? 6 : 2)) : (M <= 4 ? 4 : 2);
+}
+
+// Rows per wavefront R and wavefronts per workgroup (16 / R): 4 rows per
+// wavefront when that still gives every CU at least 8 wavefronts,
+// otherwise 2 or 1, so that a matrix with few rows (4096 x 11008) still
+// spreads over 8 - 16 wavefronts per CU and each workgroup's activation
+// quantization is shared by that many wavefronts.  Several activation rows
+// always use R = 4.
+template <int QT, int M, bool FX, int J>
+hipError_t launch_rows_r(const RowsArgs &a, hipStream_t s, const char **name) {
+    constexpr int JJ = J < jmax<QT, M>() ? J : jmax<QT, M>();
+    if constexpr (M > 1) {
+        return launch_rows_t<QT, M, FX, JJ, 4, 4>(a, s, name);
+    } else {
+        const int nrows = a.r1 - a.r0;
+        const int per_cu = 8 * a.num_cu;
+        if (nrows / 4 >= per_cu) return launch_rows_t<QT, M, FX, JJ, 4, 4>(a, s, name);
+        if (nrows / 2 >= per_cu) return launch_rows_t<QT, M, FX, JJ, 2, 8>(a, s, name);
+        return launch_rows_t<QT, M, FX, JJ, 1, 16>(a, s, name);
+    }
 }
 
 template <int QT, int M, bool FX>
-hipError_t launch_rows_u(const RowsArgs &a, hipStream_t s, const char **name) {
+hipError_t launch_rows_j(const RowsArgs &a, hipStream_t s, const char **name) {
     const int nj = (a.K / QK + 63) / 64;
-#ifdef QMV_TUNE_WPB
-    constexpr int WPB = QMV_TUNE_WPB;
-#else
-    constexpr int WPB = 8;
-#endif
-#ifdef QMV_TUNE_UJ
-    if (QMV_TUNE_UJ == 2 && nj >= 2 && QT == 4) return launch_rows_s<QT, M, FX, 2, WPB>(a, s, name);
-    return launch_rows_s<QT, M, FX, 1, WPB>(a, s, name);
-#else
-    if (nj >= 2 && QT == 4) return launch_rows_s<QT, M, FX, 2, WPB>(a, s, name);
-    return launch_rows_s<QT, M, FX, 1, WPB>(a, s, name);
-#endif
+    if (nj <= 1) return launch_rows_r<QT, M, FX, 1>(a, s, name);
+    if (nj <= 2) return launch_rows_r<QT, M, FX, 2>(a, s, name);
+    if (nj <= 3) return launch_rows_r<QT, M, FX, 3>(a, s, name);
+    if (nj <= 4) return launch_rows_r<QT, M, FX, 4>(a, s, name);
+    if (nj <= 6) return launch_rows_r<QT, M, FX, 6>(a, s, name);
+    return launch_rows_r<QT, M, FX, 8>(a, s, name);
 }
 
 template <int QT>
 hipError_t launch_rows_q(const RowsArgs &a, hipStream_t s, const char **name) {
-    if (a.x != nullptr) return launch_rows_u<QT, 1, true>(a, s, name);
+    if (a.x != nullptr) return launch_rows_j<QT, 1, true>(a, s, name);
     switch (a.M) {
-        case 1: return launch_rows_u<QT, 1, false>(a, s, name);
-        case 2: return launch_rows_u<QT, 2, false>(a, s, name);
-        case 3: return launch_rows_u<QT, 3, false>(a, s, name);
-        case 4: return launch_rows_u<QT, 4, false>(a, s, name);
-        case 5: return launch_rows_u<QT, 5, false>(a, s, name);
-        case 6: return launch_rows_u<QT, 6, false>(a, s, name);
-        case 7: return launch_rows_u<QT, 7, false>(a, s, name);
-        case 8: return launch_rows_u<QT, 8, false>(a, s, name);
+        case 1: return launch_rows_j<QT, 1, false>(a, s, name);
+        case 2: return launch_rows_j<QT, 2, false>(a, s, name);
+        case 3: return launch_rows_j<QT, 3, false>(a, s, name);
+        case 4: return launch_rows_j<QT, 4, false>(a, s, name);
+        case 5: return launch_rows_j<QT, 5, false>(a, s, name);
+        case 6: return launch_rows_j<QT, 6, false>(a, s, name);
+        case 7: return launch_rows_j<QT, 7, false>(a, s, name);
+        case 8: return launch_rows_j<QT, 8, false>(a, s, name);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
+
+size_t rows_lds_bytes(int M, int K, bool fx) { return lds_bytes(M, K, fx); }
 
 hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name) {
     return a.qtype == 4 ? launch_rows_q<4>(a, s, name) : launch_rows_q<8>(a, s, name);

@@ -21,10 +21,13 @@ struct RowsArgs {
     int8_t *xq_out;            // optional copy of the fused quantization
     float *xd_out;
     int32_t r0, r1;
-    int max_groups;            // cap on the workgroup count
+    int num_cu;                // compute units of the device (sizes the grid)
 };
 
 hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name);
+// LDS bytes the row-streaming kernel needs for M activation rows of K
+// (fused: the float32 activation is staged too).
+size_t rows_lds_bytes(int M, int K, bool fused);
 
 // Q8_0 quantization of nblk blocks of 32 floats (activations or weights).
 hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,

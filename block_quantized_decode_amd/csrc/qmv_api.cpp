@@ -71,19 +71,6 @@ qmv_status finish(hipError_t e, const char *name, long grid_hint) {
     return QMV_OK;
 }
 
-#ifndef QMV_GROUPS_PER_CU
-#define QMV_GROUPS_PER_CU 1
-#endif
-
-// Upper bound on the workgroup count of the row-streaming kernels: one
-// workgroup per compute unit, whose wavefronts loop over row quads.  Every
-// workgroup stages the whole activation, so more workgroups only multiply
-// the activation traffic that every CU pulls through L2 at the same time.
-int groups_cap(int dev) {
-    int cu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
-    return cu * QMV_GROUPS_PER_CU;
-}
-
 qmv_status check_weight(const qmv_qtensor *W, int want_type) {
     if (W == nullptr || W->q == nullptr || W->d == nullptr) return QMV_E_ARG;
     if (W->type != QMV_Q4_0 && W->type != QMV_Q8_0) return QMV_E_FORMAT;
@@ -109,8 +96,8 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     qmv_status st = check_weight(W, qtype);
     if (st != QMV_OK) return st;
     if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
-    const int64_t nb = W->cols / QMV_QK;
-    if (40 * nb * (int64_t)M > QMV_LDS_BYTES) return QMV_E_SHAPE;
+    if (W->cols > 131072 || qmv::rows_lds_bytes(M, W->cols, x != nullptr) > (size_t)QMV_LDS_BYTES)
+        return QMV_E_SHAPE;
     if ((st = check_weight_align(W)) != QMV_OK) return st;
     if (!aligned(y, 4)) return QMV_E_ARG;
     if (x != nullptr && !aligned(x, 16)) return QMV_E_ARG;
@@ -135,7 +122,7 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     a.xd_out = xq_out ? xq_out->d : nullptr;
     a.r0 = r0;
     a.r1 = r1;
-    a.max_groups = groups_cap(dev);
+    a.num_cu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
     const char *name = "";
     hipError_t e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
     return finish(e, name, (r1 - r0 + 15) / 16);

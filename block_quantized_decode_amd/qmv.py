@@ -226,3 +226,52 @@ def qmv_gemm_q8(wq, wd, xq, xd, r0=None, r1=None, Y=None):
 
 def qmv_gemm_q4(wq, wd, xq, xd, r0=None, r1=None, Y=None):
     return _gemm(QMV_Q4_0, "qmv_gemm_q4", wq, wd, xq, xd, r0, r1, Y)
+
+
+class Prepared:
+    """A libqmv call with its arguments marshalled once: calling it costs one
+    ctypes call (on the stream current at preparation time unless another
+    is given), so host overhead does not starve the GPU between launches and
+    the call can be captured in a HIP graph.  The tensors must stay alive and
+    keep their storage while the object is used."""
+
+    def __init__(self, fname: str, args: list, keep: list, stream=None):
+        self._f = getattr(lib(), fname)
+        self._fname = fname
+        self._args = args
+        self._keep = keep
+        self._stream = stream
+
+    def __call__(self, stream=None):
+        s = stream if stream is not None else (self._stream if self._stream is not None else _stream())
+        code = self._f(*self._args, s)
+        if code != 0:
+            raise QmvError(code, self._fname)
+
+
+def prepare_matvec_fx(qtype, wq, wd, x, y, r0=None, r1=None, xq_out=None, stream=None) -> Prepared:
+    """Prepared qmv_matvec_q4_fx / qmv_matvec_q8_fx (same arguments as those)."""
+    W = qtensor(wq, wd, qtype)
+    _dev(x, torch.float32)
+    _dev(y, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    act = None
+    if xq_out is not None:
+        q, d = xq_out
+        act = QAct(_dev(q, torch.int8).data_ptr(), _dev(d, torch.float32).data_ptr(), 0)
+    fname = "qmv_matvec_q4_fx" if qtype == QMV_Q4_0 else "qmv_matvec_q8_fx"
+    args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), ctypes.byref(act) if act is not None else None, r0, r1]
+    return Prepared(fname, args, [W, act, wq, wd, x, y, xq_out], stream)
+
+
+def prepare_gemm(qtype, wq, wd, xq, xd, Y, r0=None, r1=None, stream=None) -> Prepared:
+    """Prepared qmv_gemm_q4 / qmv_gemm_q8."""
+    W = qtensor(wq, wd, qtype)
+    X = qtensor(xq, xd, QMV_Q8_0)
+    _dev(Y, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    fname = "qmv_gemm_q4" if qtype == QMV_Q4_0 else "qmv_gemm_q8"
+    args = [Y.data_ptr(), ctypes.byref(W), ctypes.byref(X), r0, r1]
+    return Prepared(fname, args, [W, X, wq, wd, xq, xd, Y], stream)

@@ -70,9 +70,12 @@ enum { QMV_Q4_0 = 4, QMV_Q8_0 = 8 };
 /* Block length. */
 #define QMV_QK 32
 
-/* Largest K accepted by the single-row and few-row products: the quantized
- * activation rows are staged in on-chip LDS, 40 bytes per 32-element block
- * per activation row, within 160 KiB. */
+/* On-chip LDS budget of the single-row and few-row products: the quantized
+ * activation rows are staged in LDS, 40 bytes per 32-element block per
+ * activation row (rounded up to 64 blocks), plus, for the fused calls, the
+ * float32 activation itself (4 bytes per element, rounded up to 1 KiB).
+ * That bounds K: at most 131072 for the pre-quantized single-row product,
+ * 31744 for the fused one, 16384 for 8 activation rows. */
 #define QMV_LDS_BYTES (160 * 1024)
 
 /* A quantized weight matrix (spec section 4, ml_qtensor): rows x cols,
@@ -130,7 +133,7 @@ qmv_status qmv_quantize_weights(const qmv_qtensor *W, const float *w, void *stre
  *       [r0, r1) are not written.
  *   W : type QMV_Q8_0 (resp. QMV_Q4_0).  x : Q8_0 activation, x->n == W->cols.
  *   0 <= r0 <= r1 <= W->rows; r0 == r1 enqueues nothing.
- *   Limit: 40 * W->cols / 32 <= QMV_LDS_BYTES (K <= 131072).
+ *   Limit: K <= 131072 (QMV_LDS_BYTES).
  * ------------------------------------------------------------------------- */
 qmv_status qmv_matvec_q8(float *y, const qmv_qtensor *W, const qmv_qact *x,
                          int32_t r0, int32_t r1, void *stream);
@@ -141,7 +144,8 @@ qmv_status qmv_matvec_q4(float *y, const qmv_qtensor *W, const qmv_qact *x,
  * qmv_matvec_q8_fx / qmv_matvec_q4_fx -- the same product from a float32
  * activation x (W->cols floats, 16-byte aligned): the activation is
  * quantized to Q8_0 inside the kernel (the rule of qmv_quantize_q8, the
- * same bits) and never leaves the chip.  If xq is not NULL, xq->q (W->cols
+ * same bits) and never leaves the chip (limit: K <= 31744, the LDS budget
+ * with the float32 activation staged).  If xq is not NULL, xq->q (W->cols
  * bytes) and xq->d (W->cols / 32 floats) also receive the quantized
  * activation and xq->n is set to W->cols.
  * ------------------------------------------------------------------------- */
@@ -158,8 +162,8 @@ qmv_status qmv_matvec_q4_fx(float *y, const qmv_qtensor *W, const float *x,
  * for every m < M and r in [r0, r1); other entries are not written.
  * The spec defines the single-row product; this applies it to each row of
  * X while every weight byte is read from memory once.
- *   1 <= M: M <= 8 runs on the dot-product path (limit 40 * M * K / 32 <=
- *   QMV_LDS_BYTES); M >= 9 runs on the matrix-core path (no K limit).
+ *   1 <= M: the dot-product path takes up to 8 activation rows per pass
+ *   over the weights (limit: the 8-row LDS budget, K <= 16384).
  * ------------------------------------------------------------------------- */
 qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
                        int32_t r0, int32_t r1, void *stream);

@@ -161,3 +161,40 @@ def test_gemm(qtype, m):
     Y = host(f(dev(wq), dev(ones_w), dev(xs), dev(ones_x)))
     want = pins.w_values(qtype, wq) @ xs.astype(np.int64).T
     assert np.array_equal(Y.astype(np.int64), want.T)
+
+
+def test_prepared_calls_and_graph_replay():
+    """Prepared calls captured in a HIP graph: every replay, with eager work
+    and synchronisations in between, gives the eager result bit for bit
+    (the kernels are deterministic: fixed summation order, no atomics)."""
+    announce("graph replay")
+    rng = np.random.default_rng(800)
+    dev_ = "cuda:0"
+    cases = []
+    for qtype, rows, k in ((4, 300, 4096), (4, 77, 11008), (8, 129, 896)):
+        wq, wd = _weights(rng, qtype, rows, k, raw=False)
+        x = synth.normal(rng, (k,))
+        cases.append((qtype, dev(wq), dev(wd), dev(x), torch.zeros(rows, dtype=torch.float32, device=dev_),
+                      orc.matvec(qtype, wq, wd, *orc.quantize_q8(x)), (wq, wd, x)))
+    stream = torch.cuda.Stream()
+    calls = [qmv.prepare_matvec_fx(qt, q, d, x, y, stream=stream.cuda_stream) for qt, q, d, x, y, _, _ in cases]
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    eager = [host(y).copy() for *_, y, _, _ in [(c[0], c[1], c[2], c[3], c[4], c[5], c[6]) for c in cases]]
+    for (qt, _, _, _, _, yref, (wq, wd, x)), ye in zip(cases, eager):
+        xq, xd = orc.quantize_q8(x)
+        check_close(qt, ye, yref, wq, wd, xq, xd, what="prepared eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for *_, y, _, _ in cases:
+            y.fill_(-1.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (*_, y, _, _), ye in zip(cases, eager):
+            assert np.array_equal(host(y), ye), f"replay {rep} differs from the eager result"
