@@ -29,6 +29,23 @@ hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name);
 // (fused: the float32 activation is staged too).
 size_t rows_lds_bytes(int M, int K, bool fused);
 
+// Arguments of the matrix-core product for up to 64 activation rows per launch.
+struct GemmArgs {
+    int qtype;                 // 4 or 8
+    float *Y;                  // M x rows, row-major (row m starts at Y + m * rows)
+    const int8_t *wq;
+    const float *wd;
+    int32_t rows, K;
+    const int8_t *xq;          // Q8_0 activation quants, M x K
+    const float *xd;           // Q8_0 activation scales, M x K/32
+    int32_t M;                 // 1 .. 64
+    int32_t r0, r1;
+};
+
+constexpr int kGemmMaxRows = 64;  // activation rows per matrix-core launch
+
+hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t s, const char **name);
+
 // Q8_0 quantization of nblk blocks of 32 floats (activations or weights).
 hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,
                            const char **name);

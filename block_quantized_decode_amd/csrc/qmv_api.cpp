@@ -153,12 +153,32 @@ qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
     if (X->rows < 1 || X->cols != W->cols) return QMV_E_SHAPE;
     if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
     if (!aligned(X->q, 16) || !aligned(X->d, 4)) return QMV_E_ARG;
-    // Dot-product path, up to 8 activation rows per pass over the weights.
-    for (int32_t m0 = 0; m0 < X->rows; m0 += 8) {
-        const int32_t mc = (X->rows - m0) < 8 ? (X->rows - m0) : 8;
-        st = rows_common(qtype, Y + (size_t)m0 * W->rows, W, mc, nullptr, X->q + (size_t)m0 * X->cols,
-                         X->d + (size_t)m0 * (X->cols / QMV_QK), nullptr, r0, r1, stream);
-        if (st != QMV_OK) return st;
+    if (X->rows <= 8)  // dot-product path: all rows in one pass over the weights
+        return rows_common(qtype, Y, W, X->rows, nullptr, X->q, X->d, nullptr, r0, r1, stream);
+    // matrix-core path: up to 64 activation rows per pass over the weights
+    if (W->cols > 131072) return QMV_E_SHAPE;
+    if ((st = check_weight_align(W)) != QMV_OK) return st;
+    if (!aligned(Y, 4)) return QMV_E_ARG;
+    int dev = -1;
+    if ((st = device_check(&dev)) != QMV_OK) return st;
+    if (r0 == r1) return QMV_OK;
+    const int32_t nb = W->cols / QMV_QK;
+    for (int32_t m0 = 0; m0 < X->rows; m0 += qmv::kGemmMaxRows) {
+        qmv::GemmArgs a;
+        a.qtype = qtype;
+        a.Y = Y + (size_t)m0 * W->rows;
+        a.wq = W->q;
+        a.wd = W->d;
+        a.rows = W->rows;
+        a.K = W->cols;
+        a.xq = X->q + (size_t)m0 * W->cols;
+        a.xd = X->d + (size_t)m0 * nb;
+        a.M = (X->rows - m0) < qmv::kGemmMaxRows ? (X->rows - m0) : qmv::kGemmMaxRows;
+        a.r0 = r0;
+        a.r1 = r1;
+        const char *name = "";
+        hipError_t e = qmv::launch_gemm_mfma(a, static_cast<hipStream_t>(stream), &name);
+        if ((st = finish(e, name, (r1 - r0 + 15) / 16)) != QMV_OK) return st;
     }
     return QMV_OK;
 }

@@ -75,7 +75,9 @@ enum { QMV_Q4_0 = 4, QMV_Q8_0 = 8 };
  * activation row (rounded up to 64 blocks), plus, for the fused calls, the
  * float32 activation itself (4 bytes per element, rounded up to 1 KiB).
  * That bounds K: at most 131072 for the pre-quantized single-row product,
- * 31744 for the fused one, 16384 for 8 activation rows. */
+ * 31744 for the fused one, M * K <= 131072 for M <= 8 activation rows.
+ * The matrix-core product (M > 8) stages nothing but its 32 KiB of partial
+ * sums. */
 #define QMV_LDS_BYTES (160 * 1024)
 
 /* A quantized weight matrix (spec section 4, ml_qtensor): rows x cols,
@@ -161,9 +163,15 @@ qmv_status qmv_matvec_q4_fx(float *y, const qmv_qtensor *W, const float *x,
  *   Y[m * W->rows + r] = sum_b sumi(m, r, b) * dw(r, b) * dx(m, b)
  * for every m < M and r in [r0, r1); other entries are not written.
  * The spec defines the single-row product; this applies it to each row of
- * X while every weight byte is read from memory once.
- *   1 <= M: the dot-product path takes up to 8 activation rows per pass
- *   over the weights (limit: the 8-row LDS budget, K <= 16384).
+ * X while every weight byte is read from memory once per pass.
+ *   1 <= M <= 8: the dot-product path, all M rows in one pass over the
+ *   weights.
+ *   M > 8: the int8 matrix-core path, one v_mfma instruction per 32-element
+ *   block and tile, up to 64 activation rows per pass over the weights
+ *   (ceil(M / 64) passes).
+ *   Limits: M * K <= 131072 for M <= 8 (QMV_LDS_BYTES), K <= 131072 for
+ *   M > 8.  Y must be 4-byte aligned, X->q 16-byte aligned.  The passes
+ *   of one call are ordered on the stream; each output is written once.
  * ------------------------------------------------------------------------- */
 qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
                        int32_t r0, int32_t r1, void *stream);
