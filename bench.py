@@ -64,13 +64,16 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 10}), flush=True)
 
 
+# The sources the timed kernel (the row-streaming matvec) is compiled from.
+TIMED_KERNEL_SOURCES = ("device_common.h", "kernels_rows.hip")
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_decode_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in TIMED_KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
