@@ -30,6 +30,9 @@ COMMON = [
     # IEEE fp32: keep denormals; division stays correctly rounded (hipcc default)
     "-fno-gpu-flush-denormals-to-zero",
     "-Wall", "-Wno-unused-function",
+    # matrix-instruction results in ordinary vector registers (no copies out of
+    # the accumulation registers before the fp32 epilogue)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
