@@ -14,7 +14,10 @@ timed region is K graph replays.  Printed: one JSON line with the metric
 the dominant kernel (every launch in the timed region is the fused
 matvec: its average launch duration is the timed region's HIP-event time
 per launch) and the CPU oracle timed on the same workload on the host
-cores.
+cores.  The second half of the metric, the M >= 16 product on the int8
+matrix cores (GOP/s and % of the int8 peak on the batched workload: both
+FFN matrices, Q4_0 and Q8_0, M = 16 and 64), is measured the same way and
+reported under "batched".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -43,6 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_ffn_stack_q4")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-batched", action="store_true", help="skip the M >= 16 matrix-core measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB (10 times), the reference for scaling the "
@@ -196,6 +200,11 @@ def main():
     sha = kernel_source_sha()
     traffic = load_traffic(kernel, sha)
 
+    # ---- the M >= 16 path (second half of the metric), timed the same way
+    batched = None
+    if not args.no_batched:
+        batched = batched_bench(dev)
+
     # ---- CPU oracle baseline on a bounded sample (and a parity spot-check)
     cpu = None
     if not args.no_cpu:
@@ -240,10 +249,84 @@ def main():
             "kernel_source_sha": sha,
         },
         "cpu_baseline": cpu,
+        "batched": batched,
     }
     print(json.dumps(line), flush=True)
     if cpu is not None and not cpu.get("parity_ok", True):
         sys.exit(1)
+
+
+def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
+    """The M >= 16 product (qmv_gemm_q4 / _q8, the int8 matrix-core kernel) on
+    the batched workload: both matrices, both weight formats, M = 16 and 64.
+    Weights are quantized on the GPU from the seeded float32 draw, then
+    copied so that the launches of one graph cycle through more than twice
+    the 256 MB last-level cache (every launch streams its weights from HBM);
+    activations are quantized with qmv_quantize_q8.  Each case is a graph of
+    2 x copies launches replayed `replays` times between HIP events on the
+    launch stream.  GOP/s counts 2 M N K operations per launch."""
+    import torch
+
+    from block_quantized_decode_amd import qmv, synth
+
+    wl = synth.WORKLOADS[name]
+    stream = torch.cuda.Stream()
+    cases = []
+    for mt in wl.matrices:
+        w = torch.from_numpy(synth.weight(wl, mt.name)).to(dev)
+        for qtype in wl.qtypes:
+            q0, d0 = qmv.qmv_quantize_weights(w, qtype)
+            wbytes = q0.numel() + 4 * d0.numel()
+            ncopy = max(2, (600 << 20) // wbytes + 1)
+            copies = [(q0, d0)] + [(q0.clone(), d0.clone()) for _ in range(ncopy - 1)]
+            for m in wl.ms:
+                x = torch.from_numpy(synth.activation(wl, mt.act, m)).to(dev)
+                xq, xd = qmv.qmv_quantize_q8(x)
+                y = torch.zeros((m, mt.rows), dtype=torch.float32, device=dev)
+                with torch.cuda.stream(stream):
+                    calls = [qmv.prepare_gemm(qtype, q, d, xq, xd, y, stream=stream.cuda_stream) for q, d in copies]
+                    for c in calls:
+                        c()
+                torch.cuda.synchronize()
+                kernel = qmv.last_kernel()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    for _ in range(2):
+                        for c in calls:
+                            c()
+                with torch.cuda.stream(stream):
+                    graph.replay()
+                torch.cuda.synchronize()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    t0.record(stream)
+                    for _ in range(replays):
+                        graph.replay()
+                    t1.record(stream)
+                torch.cuda.synchronize()
+                us = t0.elapsed_time(t1) * 1e3 / (replays * 2 * len(calls))
+                gops = 2.0 * m * mt.rows * mt.cols / (us * 1e-6) / 1e9
+                cases.append({"qtype": f"q{qtype}_0", "matrix": mt.name, "shape": f"{mt.rows}x{mt.cols}", "m": m,
+                              "us_per_launch": round(us, 2), "gop_s": round(gops, 1),
+                              "pct_int8_peak": round(100.0 * gops / (MFMA_I8_PEAK_TOPS * 1e3), 2),
+                              "weight_gb_s": round(wbytes / (us * 1e-6) / 1e9, 1), "kernel": kernel})
+                del graph, calls
+            del copies, q0, d0
+            torch.cuda.empty_cache()
+        del w
+    best = max(cases, key=lambda c: c["gop_s"])
+    return {
+        "metric": "M>=16 int8 GOP/s (% MFMA peak)",
+        "workload": name,
+        "best_gop_s": best["gop_s"],
+        "best_pct_int8_peak": best["pct_int8_peak"],
+        "best_case": f"{best['qtype']} {best['matrix']} {best['shape']} M={best['m']}",
+        "bound_note": "HBM-bound for M <= 64: 2M ops per weight element against 0.625 B (Q4_0) or 1.125 B (Q8_0) "
+                      "stays below the chip's 625 op/B ridge, so at M = 64 the ceiling is ~33% (Q4_0) / ~18% "
+                      "(Q8_0) of the int8 peak",
+        "cases": cases,
+    }
 
 
 def cpu_baseline(wl, qtype, mats, target_s):
