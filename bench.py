@@ -68,8 +68,8 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 10}), flush=True)
 
 
-# The sources the timed kernel (the row-streaming matvec) is compiled from.
-TIMED_KERNEL_SOURCES = ("device_common.h", "kernels_rows.hip")
+# The sources the timed kernel (the split-K fused matvec) is compiled from.
+TIMED_KERNEL_SOURCES = ("device_common.h", "kernels_fx.hip")
 
 
 def kernel_source_sha() -> str:

@@ -38,9 +38,6 @@
 #include "device_common.h"
 #include "launch.h"
 
-#ifndef QMV_STAGE_FIRST
-#define QMV_STAGE_FIRST 0
-#endif
 
 namespace qmv {
 namespace {
@@ -89,12 +86,16 @@ __device__ __forceinline__ void load_tile(WTile<QT, J, R> &t, const int8_t *__re
         const int b = lane + 64 * (j0 + u);
         const int oq = b < nb ? b * QB : kOOB;
         const int od = b < nb ? b * 4 : kOOB;
+        // the row offset goes into the per-lane offset, which the hardware
+        // range-checks (the scalar offset field is not): rows past r1 read
+        // zeros
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            t.w[u][r][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, oq, r * nb * QB, kNT));
+            const int rq_off = oq + r * nb * QB, rd_off = od + r * nb * 4;
+            t.w[u][r][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, rq_off, 0, kNT));
             if constexpr (QT == 8)
-                t.w[u][r][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, oq + 16, r * nb * QB, kNT));
-            t.dw[u][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, od, r * nb * 4, kNT));
+                t.w[u][r][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, rq_off + 16, 0, kNT));
+            t.dw[u][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, rd_off, 0, kNT));
         }
     }
 }
@@ -188,17 +189,11 @@ k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__rest
     // 2. this unit's weights (first column chunk), all of it in flight at
     //    once; an idle wavefront's descriptor has an empty range
     WTile<QT, J, R> t;
-#if !QMV_STAGE_FIRST
     load_tile<QT, J, R>(t, wq, wd, nb, rb, busy ? r1 : rb, 0, lane);
     __builtin_amdgcn_sched_barrier(0);
-#endif
 
     // 3. once the activation has landed, quantize / sum it in LDS
     __syncthreads();
-#if QMV_STAGE_FIRST
-    load_tile<QT, J, R>(t, wq, wd, nb, rb, busy ? r1 : rb, 0, lane);
-    __builtin_amdgcn_sched_barrier(0);
-#endif
     if constexpr (FX) {
         // one lane per 32-element block: the two divisions once per block,
         // no cross-lane steps.  Lane b reads its block's eight 16-byte

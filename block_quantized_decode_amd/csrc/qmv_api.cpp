@@ -124,7 +124,8 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     a.r1 = r1;
     a.num_cu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
     const char *name = "";
-    hipError_t e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
+    hipError_t e = qmv::launch_fx(a, static_cast<hipStream_t>(stream), &name);
+    if (e == hipErrorNotSupported) e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
     return finish(e, name, (r1 - r0 + 15) / 16);
 }
 
