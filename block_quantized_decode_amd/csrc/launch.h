@@ -48,7 +48,9 @@ struct GemmArgs {
 
 constexpr int kGemmMaxRows = 64;  // activation rows per matrix-core launch
 
-hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t s, const char **name);
+// Matrix-core product with one workgroup per compute unit and the K
+// dimension split over its wavefronts (num_cu sizes the row tiles).
+hipError_t launch_mm(const GemmArgs &a, int num_cu, hipStream_t s, const char **name);
 
 // Q8_0 quantization of nblk blocks of 32 floats (activations or weights).
 hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,

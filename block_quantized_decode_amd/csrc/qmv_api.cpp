@@ -178,7 +178,8 @@ qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
         a.r0 = r0;
         a.r1 = r1;
         const char *name = "";
-        hipError_t e = qmv::launch_gemm_mfma(a, static_cast<hipStream_t>(stream), &name);
+        const int ncu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+        hipError_t e = qmv::launch_mm(a, ncu, static_cast<hipStream_t>(stream), &name);
         if ((st = finish(e, name, (r1 - r0 + 15) / 16)) != QMV_OK) return st;
     }
     return QMV_OK;

@@ -179,3 +179,17 @@ def test_gemm_k_limit(qtype):
         xq, xd = _act(rng, m, k)
         with pytest.raises(qmv.QmvError, match="QMV_E_SHAPE"):
             _f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd))
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("rows,k,m", [(8187, 256, 20), (11000, 512, 64), (16387, 128, 33)])
+def test_gemm_mfma_row_tiles(qtype, rows, k, m):
+    """Weight-row counts that give a workgroup 2, 3 and 4 tiles of 16 rows
+    (more tiles than compute units), with a ragged last tile; the last case
+    also needs more workgroups than compute units."""
+    announce(f"gemm mfma q{qtype} m={m} rows={rows} k={k}")
+    rng = np.random.default_rng(rows + k + m + qtype)
+    wq, wd = _weights(rng, qtype, rows, k)
+    xq, xd = _act(rng, m, k)
+    Y = host(_f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd)))
+    _check_all(qtype, Y, wq, wd, xq, xd, 0, rows, f"q{qtype} {rows}x{k} m={m}")
