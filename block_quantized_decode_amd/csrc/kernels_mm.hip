@@ -280,6 +280,8 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
 template <int QT, int MT, int RT>
 hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
     // register stages in the ring (D - 1 in flight) by activation tiles
+    // (measured: deeper rings for one tile lose more to registers than they
+    // gain in flight; four tiles leave no room for a third stage)
     constexpr int WPB = 8, D = MT == 1 ? QMV_MM_D1 : MT == 2 ? QMV_MM_D2 : QMV_MM_D4;
     typedef Region<MT, RT> Rg;
     constexpr int lds_stage = WPB * Rg::BYTES, lds_part = WPB * RT * MT * 1024;
