@@ -308,13 +308,14 @@ def check_matvec_unit_scales():
         y = orc.matvec(qtype, wq, ones_w, xq, ones_x)
         want = (w_values(qtype, wq) * xq.astype(np.int64)[None, :]).sum(axis=1)
         assert np.all(np.abs(want) < 2 ** 24)
-        assert np.array_equal(y.astype(np.int64), want)
+        assert np.all(np.isfinite(y)) and np.array_equal(y.astype(np.int64), want)
         # one-hot dx isolates one block's sum at any K
         for b in (0, k // QK - 1, 5):
             oh = np.zeros(k // QK, np.float32)
             oh[b] = 1.0
             y = orc.matvec(qtype, wq, ones_w, xq, oh)
             wb = w_values(qtype, wq)[:, b * QK:(b + 1) * QK]
+            assert np.all(np.isfinite(y))
             assert np.array_equal(y.astype(np.int64), (wb * xq[b * QK:(b + 1) * QK].astype(np.int64)).sum(axis=1))
 
 
