@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--workload", default="llama7b_ffn_stack_q4")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the M >= 16 matrix-core measurement")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="only the M >= 16 matrix-core measurement (one JSON object; for profiling that path)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB (10 times), the reference for scaling the "
@@ -99,6 +101,13 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.batched_only:
+        import torch
+        from block_quantized_decode_amd import qmv
+        torch.cuda.set_device(0)
+        qmv.qmv_device_check()
+        print(json.dumps(batched_bench(torch.device("cuda:0"))), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -307,9 +316,13 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
                 torch.cuda.synchronize()
                 us = t0.elapsed_time(t1) * 1e3 / (replays * 2 * len(calls))
                 gops = 2.0 * m * mt.rows * mt.cols / (us * 1e-6) / 1e9
+                # ceiling from HBM alone: 2 m operations per weight against its
+                # bytes (0.625 B for Q4_0, 1.125 B for Q8_0), at the vendor 8 TB/s
+                hbm_cap = min(MFMA_I8_PEAK_TOPS * 1e3, 2.0 * m * (mt.rows * mt.cols) / wbytes * HBM_PEAK_GBS)
                 cases.append({"qtype": f"q{qtype}_0", "matrix": mt.name, "shape": f"{mt.rows}x{mt.cols}", "m": m,
                               "us_per_launch": round(us, 2), "gop_s": round(gops, 1),
                               "pct_int8_peak": round(100.0 * gops / (MFMA_I8_PEAK_TOPS * 1e3), 2),
+                              "hbm_cap_pct_int8_peak": round(100.0 * hbm_cap / (MFMA_I8_PEAK_TOPS * 1e3), 1),
                               "weight_gb_s": round(wbytes / (us * 1e-6) / 1e9, 1), "kernel": kernel})
                 del graph, calls
             del copies, q0, d0
@@ -323,8 +336,9 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
         "best_pct_int8_peak": best["pct_int8_peak"],
         "best_case": f"{best['qtype']} {best['matrix']} {best['shape']} M={best['m']}",
         "bound_note": "HBM-bound for M <= 64: 2M ops per weight element against 0.625 B (Q4_0) or 1.125 B (Q8_0) "
-                      "stays below the chip's 625 op/B ridge, so at M = 64 the ceiling is ~33% (Q4_0) / ~18% "
-                      "(Q8_0) of the int8 peak",
+                      "stays below the chip's 625 op/B ridge (hbm_cap_pct_int8_peak per case); the fp32 per-block "
+                      "epilogue (3 VALU per output per block against 64 int8 ops) caps any case at ~17% of the "
+                      "int8 peak",
         "cases": cases,
     }
 
