@@ -97,7 +97,7 @@ __device__ __forceinline__ float group_sum(float a) {
     return a;
 }
 
-template <int QT, int T, int NBL, int D, int D0, int WPB>
+template <int QT, int T, int NBL, int D, int D0, int WPB, bool KS>
 __global__ void __launch_bounds__(64 * WPB)
 k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t K,
      const float *__restrict__ x, int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1,
@@ -114,12 +114,18 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     const int nb = K >> 5;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int S = (nb + WPB - 1) / WPB;
-    const int kb0 = min(wid * S, nb);
+    // KS: the wavefronts split K (slice of S blocks each) and share every
+    // row; otherwise every wavefront holds all of K and takes every WPB-th
+    // pass of rows
+    const int S = KS ? (nb + WPB - 1) / WPB : nb;
+    const int kb0 = KS ? min(wid * S, nb) : 0;
     const int ns = min(S, nb - kb0);           // blocks in this wavefront's slice
     const int g0 = r0 + blockIdx.x * rw;       // this workgroup's rows g0 .. g1 - 1
     const int g1 = min(r1, g0 + rw);
-    const int npass = (g1 - g0 + PASS - 1) / PASS;
+    const int nrp = (g1 - g0 + PASS - 1) / PASS;  // passes of the workgroup
+    const int npass = KS ? nrp : (nrp + WPB - 1) / WPB;  // passes of this wavefront
+    const int pstride = KS ? 1 : WPB;          // pass j of this wavefront = workgroup pass j * pstride + pfirst
+    const int pfirst = KS ? 0 : wid;
 
     // 1. this wavefront's activation slice, coalesced: round k covers
     //    blocks kb0 + 16 k .. kb0 + 16 k + 15, lane l holding floats
@@ -150,10 +156,10 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     for (int k = 0; k < NBL; ++k) {
         const int c = lane % T + T * k;
         const bool ok = c < ns;
-        oq[k] = ok ? (prow * nb + kb0 + c) * QB : kOOB;
-        od[k] = ok ? (prow * nb + kb0 + c) * 4 : kOOB;
+        oq[k] = ok ? ((pfirst * PASS + prow) * nb + kb0 + c) * QB : kOOB;
+        od[k] = ok ? ((pfirst * PASS + prow) * nb + kb0 + c) * 4 : kOOB;
     }
-    const int pq = PASS * nb * QB, pd = PASS * nb * 4;  // bytes per pass
+    const int pq = pstride * PASS * nb * QB, pd = pstride * PASS * nb * 4;  // bytes per pass of this wavefront
     auto load = [&](Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NBL; ++k) {
@@ -247,11 +253,17 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                 a = fmaf((float)s, p.dw[k] * dx[k], a);
             }
             a = group_sum<T>(a);
-            const int r = j * PASS + prow;
-            if (lane % T == T - 1 && j < npass && r < rw) red[r] = a;
+            if constexpr (KS) {
+                const int r = j * PASS + prow;
+                if (lane % T == T - 1 && j < npass && r < rw) red[r] = a;
+            } else {  // whole rows: store directly
+                const int r = (j * pstride + pfirst) * PASS + prow;
+                if (lane % T == T - 1 && j < npass && r < rows_here) y[g0 + r] = a;
+            }
         }
     }
 
+    if constexpr (!KS) return;
     // 5. add the wavefronts' slice sums of each row in wavefront order
     __syncthreads();
     for (int r = threadIdx.x; r < rows_here; r += 64 * WPB) {
@@ -262,14 +274,14 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     }
 }
 
-template <int QT, int T, int NBL, int D, int WPB>
+template <int QT, int T, int NBL, int D, int WPB, bool KS = true>
 hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
     static char kname[64];
     constexpr int D0 = QMV_FX_D0 < D - 1 ? QMV_FX_D0 : D - 1;
-    auto kern = k_fx<QT, T, NBL, D, D0, WPB>;
+    auto kern = k_fx<QT, T, NBL, D, D0, WPB, KS>;
     const int nrows = a.r1 - a.r0;
     const int grid = (nrows + rw - 1) / rw;
-    const size_t lds = (size_t)WPB * rw * 4;
+    const size_t lds = KS ? (size_t)WPB * rw * 4 : 0;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -277,7 +289,7 @@ hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name)
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.K, a.x, a.xq_out, a.xd_out,
                        a.r0, a.r1, rw);
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "fx_q%d_t%d_n%d_d%d_w%d", QT, T, NBL, D, WPB);
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "fx_q%d_t%d_n%d_d%d_w%d%s", QT, T, NBL, D, WPB, KS ? "" : "_rows");
     *name = kname;
     return hipGetLastError();
 }
@@ -292,7 +304,14 @@ hipError_t launch_q(const RowsArgs &a, hipStream_t s, const char **name) {
     // rows per workgroup: a whole number of passes, at most one workgroup
     // per compute unit
     // (capped so that the slice sums fit in LDS)
-    auto rows_per = [&](int pass) { return min(1024, ((nrows + groups - 1) / groups + pass - 1) / pass * pass); };
+    // (capped so that the slice sums fit in LDS; whole-row workgroups need no
+    // slice sums)
+    auto rows_per = [&](int pass) {
+        const int want = ((nrows + groups - 1) / groups + pass - 1) / pass * pass;
+        return pass > 4 ? want : min(1024, want);
+    };
+    if (nb <= 16) return launch_t<QT, 16, 1, D, W, false>(a, rows_per(4 * W), s, name);
+    if (nb <= 32) return launch_t<QT, 32, 1, D, W, false>(a, rows_per(2 * W), s, name);
     if (S <= 16) return launch_t<QT, 16, 1, D, W>(a, rows_per(4), s, name);
     if (S <= 32) return launch_t<QT, 16, 2, D, W>(a, rows_per(4), s, name);
     if (S <= 48) return launch_t<QT, 16, 3, D, W>(a, rows_per(4), s, name);
@@ -301,11 +320,12 @@ hipError_t launch_q(const RowsArgs &a, hipStream_t s, const char **name) {
 
 }  // namespace
 
-// Fused M = 1 matvec for 64 <= K / 32 <= 64 * waves; any other shape is
-// not handled here (hipErrorNotSupported, nothing launched).
+// Fused M = 1 matvec for K / 32 <= 32 (whole rows per wavefront) and
+// 64 <= K / 32 <= 64 * waves (K split over the wavefronts); any other shape
+// is not handled here (hipErrorNotSupported, nothing launched).
 hipError_t launch_fx(const RowsArgs &a, hipStream_t s, const char **name) {
     const int nb = a.K / QK;
-    if (a.x == nullptr || a.M != 1 || nb < 64 || nb > 64 * QMV_FX_WPB) return hipErrorNotSupported;
+    if (a.x == nullptr || a.M != 1 || (nb > 32 && nb < 64) || nb > 64 * QMV_FX_WPB) return hipErrorNotSupported;
     return a.qtype == 4 ? launch_q<4>(a, s, name) : launch_q<8>(a, s, name);
 }
 

@@ -1,9 +1,11 @@
 """The fused M = 1 matvec (float32 activation quantized inside the kernel)
-on the GPU against the oracle, over the shapes that exercise the split-K
-kernel: ragged slices (K / 32 not a multiple of the wavefront count),
-partial last passes (rows not a multiple of a pass), the largest slice
-(K = 16384), the first K beyond it (handled by the row-streaming kernel),
-row sub-ranges, and row counts that hit the rows-per-workgroup cap.
+on the GPU against the oracle, over the shapes that exercise both modes of
+the fused kernel: small K (K / 32 <= 32, whole rows per wavefront: rows
+interleaved over the wavefronts, partial last rounds) and split K (ragged
+slices with K / 32 not a multiple of the wavefront count, partial last
+passes, the largest slice K = 16384), the K on either side of each mode
+(handled by the row-streaming kernel), row sub-ranges, and row counts that
+hit the rows-per-workgroup cap.
 
 Block sums are checked bit for bit through the fused entry point itself:
 an activation of integers in [-127, 127] with a +-127 in every block
@@ -39,11 +41,13 @@ def _unit_activation(rng, k, lim):
     return x
 
 
-# (rows, K): K / 32 = 64 (smallest split), 65 and 66 (ragged slices, a last
-# wavefront with 2 or 3 blocks), 128, 172, 344 (Llama-7B W_down), 512 (the
-# largest slice), 513 (beyond: row-streaming kernel); rows with partial
-# last passes and fewer rows than compute units
-SHAPES = [(5, 2048), (257, 2080), (3, 2112), (1031, 4096), (64, 5504), (37, 11008), (130, 16384), (9, 16416)]
+# (rows, K): K / 32 = 1, 16, 28 (Qwen2.5-0.5B hidden), 32 (whole rows per
+# wavefront; 33 beyond: row-streaming kernel), 64 (smallest split), 65 and
+# 66 (ragged slices, a last wavefront with 2 or 3 blocks), 128, 172, 344
+# (Llama-7B W_down), 512 (the largest slice), 513 (beyond: row-streaming
+# kernel); rows with partial last passes and fewer rows than compute units
+SHAPES = [(1, 32), (33, 512), (600, 512), (7, 896), (4871, 896), (77, 1024), (19, 1056),
+          (5, 2048), (257, 2080), (3, 2112), (1031, 4096), (64, 5504), (37, 11008), (130, 16384), (9, 16416)]
 
 
 @pytest.mark.parametrize("qtype", [4, 8])
@@ -98,6 +102,18 @@ def test_fx_row_ranges(qtype):
         assert np.all(y[:r0] == -7.5) and np.all(y[r1:] == -7.5), f"rows outside [{r0},{r1}) written"
         if r1 > r0:
             check_close(qtype, y, yref, wq, wd, xq, xd, r0, r1, what=f"[{r0},{r1})")
+    # whole-row mode (K / 32 = 28)
+    rows, k = 3001, 896
+    wq, wd = _weights(rng, qtype, rows, k)
+    x = synth.normal(rng, (k,))
+    xq, xd = orc.quantize_q8(x)
+    yref = orc.matvec(qtype, wq, wd, xq, xd)
+    for r0, r1 in ((0, rows), (2, 3), (5, 70), (999, 3001), (2990, 2999)):
+        ydev = torch.full((rows,), -7.5, dtype=torch.float32, device="cuda:0")
+        y = host(_fx(qtype)(dev(wq), dev(wd), dev(x), r0, r1, ydev))
+        assert np.all(y[:r0] == -7.5) and np.all(y[r1:] == -7.5), f"rows outside [{r0},{r1}) written"
+        if r1 > r0:
+            check_close(qtype, y, yref, wq, wd, xq, xd, r0, r1, what=f"[{r0},{r1})")
 
 
 def test_fx_rows_per_workgroup_cap():
@@ -115,10 +131,12 @@ def test_fx_rows_per_workgroup_cap():
 
 
 def test_fx_kernel_choice():
-    """K / 32 in [64, 512] runs the split-K kernel, other K the row kernel."""
+    """K / 32 <= 32 and K / 32 in [64, 512] run the fused kernel (whole-row
+    and split-K modes), other K the row kernel."""
     announce("fx kernel choice")
     rng = np.random.default_rng(1300)
-    for k, want in ((2016, "rows_"), (2048, "fx_"), (16384, "fx_"), (16416, "rows_")):
+    for k, want in ((32, "fx_"), (1024, "fx_"), (1056, "rows_"), (2016, "rows_"), (2048, "fx_"), (16384, "fx_"),
+                    (16416, "rows_")):
         wq, wd = _weights(rng, 4, 8, k)
         qmv.qmv_matvec_q4_fx(dev(wq), dev(wd), dev(synth.normal(rng, (k,))))
         torch.cuda.synchronize()
