@@ -14,10 +14,12 @@ timed region is K graph replays.  Printed: one JSON line with the metric
 the dominant kernel (every launch in the timed region is the fused
 matvec: its average launch duration is the timed region's HIP-event time
 per launch) and the CPU oracle timed on the same workload on the host
-cores.  The second half of the metric, the M >= 16 product on the int8
-matrix cores (GOP/s and % of the int8 peak on the batched workload: both
-FFN matrices, Q4_0 and Q8_0, M = 16 and 64), is measured the same way and
-reported under "batched".
+cores.  The same stack at M = 4 (small-batch decode, qmv_gemm_q4 on
+pre-quantized activation rows) is reported under "small_batch".  The
+second half of the metric, the M >= 16 product on the int8 matrix cores
+(GOP/s and % of the int8 peak on the batched workload: both FFN matrices,
+Q4_0 and Q8_0, M = 16 and 64), is measured the same way and reported under
+"batched".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -209,6 +211,12 @@ def main():
     sha = kernel_source_sha()
     traffic = load_traffic(kernel, sha)
 
+    # ---- the same stack at M = 4 (small-batch decode): 4 activation rows per
+    # matrix, quantized once with qmv_quantize_q8, one qmv_gemm per matrix
+    small = None
+    if wl.name.startswith("llama7b") and 4 in wl.ms:
+        small = small_batch_bench(wl, qtype, mats, stream, args.steps, args.warmup)
+
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
     if not args.no_batched:
@@ -258,11 +266,59 @@ def main():
             "kernel_source_sha": sha,
         },
         "cpu_baseline": cpu,
+        "small_batch": small,
         "batched": batched,
     }
     print(json.dumps(line), flush=True)
     if cpu is not None and not cpu.get("parity_ok", True):
         sys.exit(1)
+
+
+def small_batch_bench(wl, qtype, mats, stream, steps, warmup):
+    """The workload's stack at M = 4 activation rows: weight bytes per step
+    over the step time of a graph of one qmv_gemm per matrix (the weights of
+    the M = 1 step, already resident)."""
+    import torch
+
+    from block_quantized_decode_amd import qmv, synth
+
+    m = 4
+    calls, keep = [], []
+    xs = {}
+    for mt, q, d, _x, _y in mats:
+        if mt.act not in xs:
+            x = torch.from_numpy(synth.activation(wl, mt.act, m)).to(q.device)
+            xs[mt.act] = qmv.qmv_quantize_q8(x)
+        xq, xd = xs[mt.act]
+        Y = torch.zeros((m, mt.rows), dtype=torch.float32, device=q.device)
+        calls.append(qmv.prepare_gemm(qtype, q, d, xq, xd, Y, stream=stream.cuda_stream))
+        keep.append(Y)
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    kernel = qmv.last_kernel()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    wbytes = wl.weight_bytes(qtype)
+    ops = sum(2 * m * mt.rows * mt.cols for mt, *_ in mats)
+    return {"m": m, "ms_per_step": round(ms, 5), "weight_gb_s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "gop_s": round(ops / (ms * 1e-3) / 1e9, 1), "launches_per_step": len(calls), "kernel": kernel}
 
 
 def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
