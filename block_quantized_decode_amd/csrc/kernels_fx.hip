@@ -1,36 +1,41 @@
-// kernels_fx.hip -- the decode matvec with the activation quantized inside
-// the kernel (M = 1, float32 x), for K of 2048 .. 16384.
+// kernels_fx.hip -- the split-K streaming product for a few activation rows:
+// the decode matvec with the activation quantized inside the kernel (M = 1,
+// float32 x) and the same product on pre-quantized Q8_0 activation rows
+// (M = 1 .. 4), for K / 32 <= 32 and K of 2048 .. 16384.
 //
 // What is computed (Legacy-ISA ML Inference Runtime -- Design Spec,
 // section 4 "Q8 quantization" and "Integer dot per block", section 5
 // kernel interface and rounding rule):
-//   qx, dx = Q8_0(x)                       per 32-element block
-//   y[r]   = sum over blocks b of sumi(r, b) * dw(r, b) * dx(b),
-//   sumi   = exact int32 dot of the 32 weight quants and qx,
-// for r in [r0, r1).
+//   qx, dx    = Q8_0(x)                     per 32-element block (fused form)
+//   y[m, r]   = sum over blocks b of sumi(m, r, b) * dw(r, b) * dx(m, b),
+//   sumi      = exact int32 dot of the 32 weight quants and qx of row m,
+// for r in [r0, r1); y is M x rows, row-major.
 //
 // Layout on the chip.  One workgroup per compute unit owns a contiguous
 // range of rows; its wavefronts split K: wavefront w owns blocks
 // [w S, w S + S) of every row of the range (S = ceil(K / 32 / waves)).  So a
-// wavefront needs only its own slice of x: it loads that slice (one block
-// per lane), quantizes it in registers and shares it with its own lanes
+// wavefront needs only its own slice of the activation rows: it loads that
+// slice (4 lanes per block), quantizes it (fused form) or forms its quant
+// sums (pre-quantized form) in registers and shares it with its own lanes
 // through a private LDS region -- no workgroup barrier stands between the
-// activation and the first block dot, and x is read and quantized once per
+// activation and the first block dot, and the activation is read once per
 // workgroup.  The memory system accepts only a bounded number of
 // outstanding loads per compute unit and stalls a wavefront at a load it
 // cannot yet accept; so each wavefront first issues its activation loads,
-// then only the first D - 1 passes of weights, quantizes while those are in
-// flight, and then runs a software pipeline over passes: issue the loads of
-// pass j + D - 1, then compute pass j.  A wavefront stalled at a load leaves
-// the vector ALU to the others.
+// then only the first D - 1 passes of weights, prepares the activation
+// while those are in flight, and then runs a software pipeline over passes:
+// issue the loads of pass j + D - 1, then compute pass j.  A wavefront
+// stalled at a load leaves the vector ALU to the others.  Each weight block
+// in registers serves all M activation rows.
 //
 // A pass is 64 / T rows: lane l takes row l / T of the pass and the blocks
 // c = l % T + T k (k < NBL) of its wavefront's slice, so each group of T
 // lanes reads T consecutive blocks of one row (T * 16 or T * 32 contiguous
 // quant bytes).  The T lanes of a row are summed with row-shift DPP adds
 // (a fixed order), the wavefronts' slice sums of a row are added in LDS in
-// wavefront order, and one lane stores y[r]: repeated calls give identical
-// bits.
+// wavefront order, and one lane stores y[m, r]: repeated calls give
+// identical bits.  With K / 32 <= 32 every wavefront holds all of K instead
+// and takes every waves-th pass of rows, storing whole-row sums directly.
 //
 // Loads use raw buffer descriptors whose range covers only this
 // workgroup's rows, and every variable part of an address is in the
@@ -97,19 +102,26 @@ __device__ __forceinline__ float group_sum(float a) {
     return a;
 }
 
-template <int QT, int T, int NBL, int D, int D0, int WPB, bool KS>
+// LDS rows of slice sums per workgroup: the activation regions take
+// M * WPB * 64 * 40 bytes and the slice sums M * WPB * rw * 4 of the
+// 160 KiB of a compute unit.
+constexpr int rw_cap(int M) { return M <= 3 ? 1024 : 512; }
+
+template <int QT, int M, bool FX, int T, int NBL, int D, int D0, int WPB, bool KS>
 __global__ void __launch_bounds__(64 * WPB)
-k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t K,
-     const float *__restrict__ x, int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1,
-     int32_t rw) {
+k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
+     const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xd,
+     int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1, int32_t rw) {
     constexpr int PASS = 64 / T;               // rows per pass
     constexpr int QB = (QT == 8) ? 32 : 16;    // quant bytes per block
     static_assert(T * NBL <= 64 && (T * NBL) % 16 == 0, "a slice is at most 64 blocks, loaded 16 blocks at a time");
     static_assert(D0 >= 0 && D0 <= D - 1, "passes issued before the quantization");
-    __shared__ v4i s_lo[WPB][64], s_hi[WPB][64];
-    __shared__ float s_dx[WPB][64];
-    __shared__ int s_sx[WPB][64];
-    extern __shared__ float s_red[];           // [WPB][rw] slice sums
+    static_assert(!FX || M == 1, "the fused form takes one float32 activation row");
+    static_assert(M * WPB * 64 * 40 + (KS ? M * WPB * rw_cap(M) * 4 : 0) <= 163840, "LDS of one compute unit");
+    __shared__ v4i s_lo[M][WPB][64], s_hi[M][WPB][64];
+    __shared__ float s_dx[M][WPB][64];
+    __shared__ int s_sx[M][WPB][64];
+    extern __shared__ float s_red[];           // [M][WPB][rw] slice sums
 
     const int nb = K >> 5;
     const int lane = threadIdx.x & 63;
@@ -128,17 +140,39 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     const int pfirst = KS ? 0 : wid;
 
     // 1. this wavefront's activation slice, coalesced: round k covers
-    //    blocks kb0 + 16 k .. kb0 + 16 k + 15, lane l holding floats
-    //    8 (l % 4) .. 8 (l % 4) + 7 of block kb0 + 16 k + l / 4
+    //    blocks kb0 + 16 k .. kb0 + 16 k + 15, lane l holding elements
+    //    8 (l % 4) .. 8 (l % 4) + 7 of block kb0 + 16 k + l / 4 (float32
+    //    in the fused form, the quants and the block scale otherwise)
     constexpr int NR = T * NBL / 16;           // rounds of 16 blocks
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * 4);
-    float4 xa[NR], xb[NR];
+    constexpr int MX = FX ? 1 : M;
+    float4 xa[FX ? NR : 1], xb[FX ? NR : 1];
+    int xv0[MX][FX ? 1 : NR], xv1[MX][FX ? 1 : NR];
+    float xdv[MX][FX ? 1 : NR];
+    if constexpr (FX) {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * 4);
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        const int b = 16 * k + (lane >> 2);
-        const int o = b < ns ? (kb0 + b) * 128 + 32 * (lane & 3) : kOOB;
-        xa[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
-        xb[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16, 0, 0));
+        for (int k = 0; k < NR; ++k) {
+            const int b = 16 * k + (lane >> 2);
+            const int o = b < ns ? (kb0 + b) * 128 + 32 * (lane & 3) : kOOB;
+            xa[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
+            xb[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16, 0, 0));
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rxq = make_rsrc(xq, M * K);
+        const __amdgpu_buffer_rsrc_t rxd = make_rsrc(xd, M * nb * 4);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const int b = 16 * k + (lane >> 2);
+                const bool ok = b < ns;
+                const int blk = m * nb + kb0 + b;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rxq, ok ? blk * 32 + 8 * (lane & 3) : kOOB, 0, 0);
+                xv0[m][k] = (int)v[0];
+                xv1[m][k] = (int)v[1];
+                xdv[m][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxd, ok ? blk * 4 : kOOB, 0, 0));
+            }
+        }
     }
     __builtin_amdgcn_sched_barrier(0);  // the activation requests go out first
 #if QMV_FX_XBAR
@@ -176,40 +210,60 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     for (int d = 0; d < D0; ++d) load(ring[d], d);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. quantize the slice, 4 lanes per block (lanes past the slice hold
-    //    zeros), into the private LDS region -- no branch, so that the
+    // 3. quantize the slice (fused) or sum its quants (pre-quantized), 4
+    //    lanes per block (lanes past the slice hold zeros), into the
+    //    private LDS region -- no branch around the arithmetic, so that the
     //    activation loads stay ahead of the weight loads
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        const int b = 16 * k + (lane >> 2), c = lane & 3;
-        float d;
-        int qs;
-        const int2 pk = quant_q8_group4(xa[k], xb[k], d, qs);
-        *reinterpret_cast<int2 *>(reinterpret_cast<int *>(c < 2 ? &s_lo[wid][b] : &s_hi[wid][b]) + 2 * (c & 1)) = pk;
-        if (c == 0) {
-            s_dx[wid][b] = d;
-            s_sx[wid][b] = -8 * qs;
-        }
-        if (xq_out != nullptr && blockIdx.x == 0 && b < ns) {  // optional copy of the quantized activation
-            reinterpret_cast<int2 *>(xq_out + (size_t)(kb0 + b) * QK)[c] = pk;
-            if (c == 0) xd_out[kb0 + b] = d;
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int b = 16 * k + (lane >> 2), c = lane & 3;
+            float d;
+            int qs;
+            int2 pk;
+            if constexpr (FX) {
+                pk = quant_q8_group4(xa[k], xb[k], d, qs);
+            } else {
+                pk = make_int2(xv0[m][k], xv1[m][k]);
+                d = xdv[m][k];
+                qs = 0;
+                if constexpr (QT == 4) {
+                    qs = dot4(pk.x, 0x01010101, dot4(pk.y, 0x01010101, 0));
+                    qs += dpp_xor1(qs);
+                    qs += dpp_xor2(qs);
+                }
+            }
+            *reinterpret_cast<int2 *>(reinterpret_cast<int *>(c < 2 ? &s_lo[m][wid][b] : &s_hi[m][wid][b]) +
+                                      2 * (c & 1)) = pk;
+            if (c == 0) {
+                s_dx[m][wid][b] = d;
+                s_sx[m][wid][b] = -8 * qs;
+            }
+            if (FX && xq_out != nullptr && blockIdx.x == 0 && b < ns) {  // optional copy of the quantized activation
+                reinterpret_cast<int2 *>(xq_out + (size_t)(kb0 + b) * QK)[c] = pk;
+                if (c == 0) xd_out[kb0 + b] = d;
+            }
         }
     }
     // LDS operations of one wavefront complete in order: once this
     // wavefront's writes are done, all of its lanes read them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    v4i xl[NBL], xh[NBL];
-    float dx[NBL];
-    int sx[NBL];
+    v4i xl[M][NBL], xh[M][NBL];
+    float dx[M][NBL];
+    int sx[M][NBL];
 #pragma unroll
-    for (int k = 0; k < NBL; ++k) {
-        const int c = lane % T + T * k;
-        const bool ok = c < ns;
-        const int cc = ok ? c : 0;
-        xl[k] = s_lo[wid][cc];
-        xh[k] = s_hi[wid][cc];
-        dx[k] = ok ? s_dx[wid][cc] : 0.0f;
-        sx[k] = s_sx[wid][cc];
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) {
+            const int c = lane % T + T * k;
+            const bool ok = c < ns;
+            const int cc = ok ? c : 0;
+            xl[m][k] = s_lo[m][wid][cc];
+            xh[m][k] = s_hi[m][wid][cc];
+            dx[m][k] = ok ? s_dx[m][wid][cc] : 0.0f;
+            sx[m][k] = s_sx[m][wid][cc];
+        }
     }
 
     // the rest of the first D - 1 passes
@@ -217,7 +271,6 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     for (int d = D0; d < D - 1; ++d) load(ring[d], d);
 
     // 4. passes: loads of pass j + D - 1 in flight while pass j is computed
-    float *red = s_red + wid * rw;
     const int nit = (npass + D - 1) / D;
     for (int it = 0; it < nit; ++it) {
 #pragma unroll
@@ -225,40 +278,56 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
             const int j = it * D + d;
             load(ring[(d + D - 1) % D], j + D - 1);
             const Pass<QT, NBL> &p = ring[d];
-            float a = 0.0f;
+            float a[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) a[m] = 0.0f;
 #pragma unroll
             for (int k = 0; k < NBL; ++k) {
-                int s;
                 if constexpr (QT == 4) {
-                    const unsigned m = 0x0F0F0F0Fu;
+                    // byte j of the 16: low nibble = element j, high nibble = element j + 16
+                    const unsigned mk = 0x0F0F0F0Fu;
                     const v4i w = p.w[k][0];
-                    s = dot4((unsigned)w.x & m, xl[k].x, sx[k]);  // starts at -8 * sum(qx)
-                    s = dot4((unsigned)w.y & m, xl[k].y, s);
-                    s = dot4((unsigned)w.z & m, xl[k].z, s);
-                    s = dot4((unsigned)w.w & m, xl[k].w, s);
-                    s = dot4(((unsigned)w.x >> 4) & m, xh[k].x, s);
-                    s = dot4(((unsigned)w.y >> 4) & m, xh[k].y, s);
-                    s = dot4(((unsigned)w.z >> 4) & m, xh[k].z, s);
-                    s = dot4(((unsigned)w.w >> 4) & m, xh[k].w, s);
+                    const int l0 = (unsigned)w.x & mk, l1 = (unsigned)w.y & mk;
+                    const int l2 = (unsigned)w.z & mk, l3 = (unsigned)w.w & mk;
+                    const int h0 = ((unsigned)w.x >> 4) & mk, h1 = ((unsigned)w.y >> 4) & mk;
+                    const int h2 = ((unsigned)w.z >> 4) & mk, h3 = ((unsigned)w.w >> 4) & mk;
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        int s = dot4(l0, xl[m][k].x, sx[m][k]);  // starts at -8 * sum(qx)
+                        s = dot4(l1, xl[m][k].y, s);
+                        s = dot4(l2, xl[m][k].z, s);
+                        s = dot4(l3, xl[m][k].w, s);
+                        s = dot4(h0, xh[m][k].x, s);
+                        s = dot4(h1, xh[m][k].y, s);
+                        s = dot4(h2, xh[m][k].z, s);
+                        s = dot4(h3, xh[m][k].w, s);
+                        a[m] = fmaf((float)s, p.dw[k] * dx[m][k], a[m]);
+                    }
                 } else {
-                    s = dot4(p.w[k][0].x, xl[k].x, 0);
-                    s = dot4(p.w[k][0].y, xl[k].y, s);
-                    s = dot4(p.w[k][0].z, xl[k].z, s);
-                    s = dot4(p.w[k][0].w, xl[k].w, s);
-                    s = dot4(p.w[k][1].x, xh[k].x, s);
-                    s = dot4(p.w[k][1].y, xh[k].y, s);
-                    s = dot4(p.w[k][1].z, xh[k].z, s);
-                    s = dot4(p.w[k][1].w, xh[k].w, s);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        int s = dot4(p.w[k][0].x, xl[m][k].x, 0);
+                        s = dot4(p.w[k][0].y, xl[m][k].y, s);
+                        s = dot4(p.w[k][0].z, xl[m][k].z, s);
+                        s = dot4(p.w[k][0].w, xl[m][k].w, s);
+                        s = dot4(p.w[k][1].x, xh[m][k].x, s);
+                        s = dot4(p.w[k][1].y, xh[m][k].y, s);
+                        s = dot4(p.w[k][1].z, xh[m][k].z, s);
+                        s = dot4(p.w[k][1].w, xh[m][k].w, s);
+                        a[m] = fmaf((float)s, p.dw[k] * dx[m][k], a[m]);
+                    }
                 }
-                a = fmaf((float)s, p.dw[k] * dx[k], a);
             }
-            a = group_sum<T>(a);
-            if constexpr (KS) {
-                const int r = j * PASS + prow;
-                if (lane % T == T - 1 && j < npass && r < rw) red[r] = a;
-            } else {  // whole rows: store directly
-                const int r = (j * pstride + pfirst) * PASS + prow;
-                if (lane % T == T - 1 && j < npass && r < rows_here) y[g0 + r] = a;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float t = group_sum<T>(a[m]);
+                if constexpr (KS) {
+                    const int r = j * PASS + prow;
+                    if (lane % T == T - 1 && j < npass && r < rw) s_red[(m * WPB + wid) * rw + r] = t;
+                } else {  // whole rows: store directly
+                    const int r = (j * pstride + pfirst) * PASS + prow;
+                    if (lane % T == T - 1 && j < npass && r < rows_here) y[(size_t)m * rows + g0 + r] = t;
+                }
             }
         }
     }
@@ -267,65 +336,309 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     // 5. add the wavefronts' slice sums of each row in wavefront order
     __syncthreads();
     for (int r = threadIdx.x; r < rows_here; r += 64 * WPB) {
-        float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < WPB; ++w) s += s_red[w * rw + r];
-        y[g0 + r] = s;
+        for (int m = 0; m < M; ++m) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPB; ++w) s += s_red[(m * WPB + w) * rw + r];
+            y[(size_t)m * rows + g0 + r] = s;
+        }
     }
 }
 
-template <int QT, int T, int NBL, int D, int WPB, bool KS = true>
-hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
+// The same split-K streaming product for 3 or 4 pre-quantized activation
+// rows on the matrix cores: v_mfma_i32_4x4x4_16b_i8 computes 16 independent
+// 4 x 4 tiles of 4-element dots.  Lane l = 4 t + i supplies one 4-byte
+// chunk of weight row i of tile t (as the A operand) and the same chunk of
+// activation row i (as the B operand); register v of lane l receives
+// tile t's (weight row v, activation row i) dot.  Here tile t of a pass is
+// block c = t + 16 k of the wavefront's slice for the pass's 4 weight rows,
+// so eight chained instructions (the 8 chunks of a block) leave in lane
+// 4 t + i the block sums of the 4 weight rows against activation row i:
+// one lane per (weight row, block) loads its own weight block (16 lanes
+// read 16 consecutive blocks of a row, 4 rows per load instruction) and
+// its own activation row's block, straight into registers.  The Q4_0 offset
+// -8 * sum(qx) seeds the accumulator.  The fp32 scaling is spread over all
+// 64 lanes (4 block sums each), the 4 lanes of a tile share the weight
+// scales through quad permutes, and the 4 tiles of each 16-lane row are
+// added with row-shift DPP adds; the per-row partial sums of the 4 rows of
+// 16 lanes and of the wavefronts are added in LDS in a fixed order.
+constexpr int kMqRwCap = 256;  // rows per workgroup: slice sums [4][WPB][4][rw] in LDS
+
+template <int QT, int NBL, int D, int D0, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
+k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
+     int32_t M, const int8_t *__restrict__ xq, const float *__restrict__ xd, int32_t r0, int32_t r1, int32_t rw) {
+    constexpr int QB = (QT == 8) ? 32 : 16;    // quant bytes per block
+    static_assert(D0 >= 0 && D0 <= D - 1, "passes issued before the activation sums");
+    extern __shared__ float s_red[];           // [activation row][wavefront][quarter][rw] partial sums
+
+    const int nb = K >> 5;
+    const int lane = threadIdx.x & 63;
+    const int t = lane >> 2, i = lane & 3;     // tile (block of the pass) and row within the tile
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (nb + WPB - 1) / WPB;
+    const int kb0 = min(wid * S, nb);
+    const int ns = min(S, nb - kb0);           // blocks in this wavefront's slice
+    const int g0 = r0 + blockIdx.x * rw;       // this workgroup's rows g0 .. g1 - 1
+    const int g1 = min(r1, g0 + rw);
+    const int rows_here = g1 - g0;
+    const int npass = (rows_here + 3) >> 2;    // passes of 4 weight rows
+
+    // 1. activation row i, blocks kb0 + t + 16 k (rows at or past M, and
+    //    blocks past the slice, read zeros)
+    const __amdgpu_buffer_rsrc_t rxq = make_rsrc(xq, M * K);
+    const __amdgpu_buffer_rsrc_t rxd = make_rsrc(xd, M * nb * 4);
+    v4i xlo[NBL], xhi[NBL];
+    float dx[NBL];
+#pragma unroll
+    for (int k = 0; k < NBL; ++k) {
+        const int c = t + 16 * k;
+        const bool ok = c < ns && i < M;
+        const int blk = i * nb + kb0 + c;
+        xlo[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rxq, ok ? blk * 32 : kOOB, 0, 0));
+        xhi[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rxq, ok ? blk * 32 + 16 : kOOB, 0, 0));
+        dx[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxd, ok ? blk * 4 : kOOB, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the activation requests go out first
+#if QMV_FX_XBAR
+    __builtin_amdgcn_s_barrier();       // ... before any wavefront's weight requests
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+
+    // 2. the first D - 1 passes of weights: lane (t, i) reads row 4 j + i,
+    //    block kb0 + t + 16 k
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq + (size_t)g0 * nb * QB, rows_here * nb * QB);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(wd + (size_t)g0 * nb, rows_here * nb * 4);
+    int oq[NBL], od[NBL];
+#pragma unroll
+    for (int k = 0; k < NBL; ++k) {
+        const int c = t + 16 * k;
+        const bool ok = c < ns;
+        oq[k] = ok ? (i * nb + kb0 + c) * QB : kOOB;
+        od[k] = ok ? (i * nb + kb0 + c) * 4 : kOOB;
+    }
+    const int pq = 4 * nb * QB, pd = 4 * nb * 4;  // bytes per pass
+    auto load = [&](Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) {
+            const int a = oq[k] + j * pq, b = od[k] + j * pd;
+            p.w[k][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a, 0, kNT));
+            if constexpr (QT == 8)
+                p.w[k][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a + 16, 0, kNT));
+            p.dw[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, b, 0, kNT));
+        }
+    };
+    Pass<QT, NBL> ring[D];
+#pragma unroll
+    for (int d = 0; d < D0; ++d) load(ring[d], d);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. the Q4_0 offset of each activation block: -8 * sum of its quants
+    int sx[NBL];
+#pragma unroll
+    for (int k = 0; k < NBL; ++k) {
+        int s = 0;
+        if constexpr (QT == 4) {
+            s = dot4(xlo[k].x, 0x01010101, dot4(xlo[k].y, 0x01010101, dot4(xlo[k].z, 0x01010101,
+                dot4(xlo[k].w, 0x01010101, 0))));
+            s = dot4(xhi[k].x, 0x01010101, dot4(xhi[k].y, 0x01010101, dot4(xhi[k].z, 0x01010101,
+                dot4(xhi[k].w, 0x01010101, s))));
+        }
+        sx[k] = -8 * s;
+    }
+#pragma unroll
+    for (int d = D0; d < D - 1; ++d) load(ring[d], d);
+
+    // 4. passes: loads of pass j + D - 1 in flight while pass j is computed
+    float *red = s_red + ((i * WPB + wid) * 4 + (lane >> 4)) * rw;
+    const int nit = (npass + D - 1) / D;
+    for (int it = 0; it < nit; ++it) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int j = it * D + d;
+            load(ring[(d + D - 1) % D], j + D - 1);
+            const Pass<QT, NBL> &p = ring[d];
+            v4i acc[NBL];
+#pragma unroll
+            for (int k = 0; k < NBL; ++k) acc[k] = (v4i){sx[k], sx[k], sx[k], sx[k]};
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+#pragma unroll
+                for (int k = 0; k < NBL; ++k) {
+                    int a;
+                    if constexpr (QT == 4) {
+                        // byte j of the 16: low nibble = element j, high nibble = element j + 16
+                        const unsigned w = (unsigned)p.w[k][0][h & 3];
+                        a = (int)((h < 4 ? w : w >> 4) & 0x0F0F0F0Fu);
+                    } else {
+                        a = p.w[k][h >> 2][h & 3];
+                    }
+                    const int b = h < 4 ? xlo[k][h] : xhi[k][h - 4];
+                    acc[k] = __builtin_amdgcn_mfma_i32_4x4x4i8(a, b, acc[k], 0, 0, 0);
+                }
+            }
+            float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < NBL; ++k) {
+                const int dwi = __float_as_int(p.dw[k]);
+                // weight scale of row v of the tile: lane 4 t + v's (quad_perm [v, v, v, v])
+                const float w0 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x00, 0xF, 0xF, false));
+                const float w1 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x55, 0xF, 0xF, false));
+                const float w2 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0xAA, 0xF, 0xF, false));
+                const float w3 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0xFF, 0xF, 0xF, false));
+                f[0] = fmaf((float)acc[k][0], w0 * dx[k], f[0]);
+                f[1] = fmaf((float)acc[k][1], w1 * dx[k], f[1]);
+                f[2] = fmaf((float)acc[k][2], w2 * dx[k], f[2]);
+                f[3] = fmaf((float)acc[k][3], w3 * dx[k], f[3]);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // tiles 4 r .. 4 r + 3 of the 16-lane row r: lanes 12 .. 15 end with the sums
+                f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x114, 0xF, 0xF, false));
+                f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x118, 0xF, 0xF, false));
+            }
+            if ((lane & 15) >= 12 && j < npass)
+                *reinterpret_cast<float4 *>(red + 4 * j) = make_float4(f[0], f[1], f[2], f[3]);
+        }
+    }
+
+    // 5. add the partial sums of each (activation row, weight row): the 4
+    //    rows of 16 lanes of each wavefront, wavefronts in order
+    __syncthreads();
+    for (int r = threadIdx.x; r < rows_here; r += 64 * WPB) {
+        for (int m = 0; m < M; ++m) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPB; ++w) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) s += s_red[((m * WPB + w) * 4 + qq) * rw + r];
+            }
+            y[(size_t)m * rows + g0 + r] = s;
+        }
+    }
+}
+
+template <int QT, int NBL, int D, int WPB>
+hipError_t launch_mq_t(const RowsArgs &a, hipStream_t s, const char **name) {
     static char kname[64];
     constexpr int D0 = QMV_FX_D0 < D - 1 ? QMV_FX_D0 : D - 1;
-    auto kern = k_fx<QT, T, NBL, D, D0, WPB, KS>;
+    auto kern = k_mq<QT, NBL, D, D0, WPB>;
     const int nrows = a.r1 - a.r0;
+    const int groups = a.num_cu * QMV_FX_WG_PER_CU;
+    const int rw = min(kMqRwCap, ((nrows + groups - 1) / groups + 3) / 4 * 4);
     const int grid = (nrows + rw - 1) / rw;
-    const size_t lds = KS ? (size_t)WPB * rw * 4 : 0;
+    const size_t lds = (size_t)4 * WPB * 4 * rw * 4;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.K, a.x, a.xq_out, a.xd_out,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.M, a.xq, a.xd,
                        a.r0, a.r1, rw);
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "fx_q%d_t%d_n%d_d%d_w%d%s", QT, T, NBL, D, WPB, KS ? "" : "_rows");
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "mq_q%d_n%d_d%d_w%d", QT, NBL, D, WPB);
     *name = kname;
     return hipGetLastError();
 }
 
 template <int QT>
-hipError_t launch_q(const RowsArgs &a, hipStream_t s, const char **name) {
+hipError_t launch_mq(const RowsArgs &a, hipStream_t s, const char **name) {
     constexpr int W = QMV_FX_WPB, D = QMV_FX_D;
+    const int S = (a.K / QK + W - 1) / W;
+    if (S <= 16) return launch_mq_t<QT, 1, D, W>(a, s, name);
+    if (S <= 32) return launch_mq_t<QT, 2, D, W>(a, s, name);
+    if (S <= 48) return launch_mq_t<QT, 3, D, W>(a, s, name);
+    return launch_mq_t<QT, 4, D, W>(a, s, name);
+}
+
+template <int QT, int M, bool FX, int T, int NBL, int D, int WPB, bool KS = true>
+hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
+    static char kname[64];
+    constexpr int D0 = QMV_FX_D0 < D - 1 ? QMV_FX_D0 : D - 1;
+    auto kern = k_fx<QT, M, FX, T, NBL, D, D0, WPB, KS>;
+    const int nrows = a.r1 - a.r0;
+    const int grid = (nrows + rw - 1) / rw;
+    const size_t lds = KS ? (size_t)M * WPB * rw * 4 : 0;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq, a.xd,
+                       a.xq_out, a.xd_out, a.r0, a.r1, rw);
+    if (kname[0] == 0) {
+        if (FX)
+            snprintf(kname, sizeof kname, "fx_q%d_t%d_n%d_d%d_w%d%s", QT, T, NBL, D, WPB, KS ? "" : "_rows");
+        else
+            snprintf(kname, sizeof kname, "px_q%d_m%d_t%d_n%d_d%d_w%d%s", QT, M, T, NBL, D, WPB, KS ? "" : "_rows");
+    }
+    *name = kname;
+    return hipGetLastError();
+}
+
+// Ring depth: four passes in flight, three where the activation registers
+// of several rows leave no room for a fourth (Q8_0 with M * NBL > 6).
+template <int QT, int M, int NBL>
+constexpr int ring_depth() {
+    return (QT == 8 && M * NBL > 6) ? 3 : QMV_FX_D;
+}
+
+template <int QT, int M, bool FX>
+hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
+    constexpr int W = QMV_FX_WPB;
     const int nb = a.K / QK;
     const int S = (nb + W - 1) / W;
     const int nrows = a.r1 - a.r0;
     const int groups = a.num_cu * QMV_FX_WG_PER_CU;
     // rows per workgroup: a whole number of passes, at most one workgroup
-    // per compute unit
-    // (capped so that the slice sums fit in LDS)
-    // (capped so that the slice sums fit in LDS; whole-row workgroups need no
-    // slice sums)
-    auto rows_per = [&](int pass) {
+    // per compute unit (capped so that the slice sums fit in LDS; whole-row
+    // workgroups need no slice sums)
+    auto rows_per = [&](int pass, bool ks) {
         const int want = ((nrows + groups - 1) / groups + pass - 1) / pass * pass;
-        return pass > 4 ? want : min(1024, want);
+        return ks ? min(rw_cap(M), want) : want;
     };
-    if (nb <= 16) return launch_t<QT, 16, 1, D, W, false>(a, rows_per(4 * W), s, name);
-    if (nb <= 32) return launch_t<QT, 32, 1, D, W, false>(a, rows_per(2 * W), s, name);
-    if (S <= 16) return launch_t<QT, 16, 1, D, W>(a, rows_per(4), s, name);
-    if (S <= 32) return launch_t<QT, 16, 2, D, W>(a, rows_per(4), s, name);
-    if (S <= 48) return launch_t<QT, 16, 3, D, W>(a, rows_per(4), s, name);
-    return launch_t<QT, 16, 4, D, W>(a, rows_per(4), s, name);
+    if (nb <= 16) return launch_t<QT, M, FX, 16, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(4 * W, false), s, name);
+    if (nb <= 32) return launch_t<QT, M, FX, 32, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(2 * W, false), s, name);
+    // split K: the fused matvec, and pre-quantized Q8_0 weights with 2 .. 4
+    // activation rows (elsewhere the row-streaming kernel is as fast or faster)
+    if constexpr (FX || (QT == 8 && M >= 2)) {
+        if (S <= 16) return launch_t<QT, M, FX, 16, 1, ring_depth<QT, M, 1>(), W>(a, rows_per(4, true), s, name);
+        if (S <= 32) return launch_t<QT, M, FX, 16, 2, ring_depth<QT, M, 2>(), W>(a, rows_per(4, true), s, name);
+        if (S <= 48) return launch_t<QT, M, FX, 16, 3, ring_depth<QT, M, 3>(), W>(a, rows_per(4, true), s, name);
+        if constexpr (M <= 2) return launch_t<QT, M, FX, 16, 4, ring_depth<QT, M, 4>(), W>(a, rows_per(4, true), s, name);
+    }
+    return hipErrorNotSupported;
+}
+
+template <int QT>
+hipError_t launch_q(const RowsArgs &a, hipStream_t s, const char **name) {
+    if (a.x != nullptr) return launch_m<QT, 1, true>(a, s, name);
+    // pre-quantized: the matrix-core form for 4 rows of Q4_0 (measured
+    // faster than both dot-product kernels) and for 3 or 4 rows of 64-block
+    // slices (beyond the dot-product form's registers)
+    const int nb = a.K / QK, S = (nb + QMV_FX_WPB - 1) / QMV_FX_WPB;
+    if (nb > 32 && ((QT == 4 && a.M == 4) || (a.M >= 3 && S > 48))) return launch_mq<QT>(a, s, name);
+    switch (a.M) {
+        case 1: return launch_m<QT, 1, false>(a, s, name);
+        case 2: return launch_m<QT, 2, false>(a, s, name);
+        case 3: return launch_m<QT, 3, false>(a, s, name);
+        case 4: return launch_m<QT, 4, false>(a, s, name);
+        default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace
 
-// Fused M = 1 matvec for K / 32 <= 32 (whole rows per wavefront) and
-// 64 <= K / 32 <= 64 * waves (K split over the wavefronts); any other shape
-// is not handled here (hipErrorNotSupported, nothing launched).
+// Split-K product for K / 32 <= 32 (whole rows per wavefront, M = 1 .. 4)
+// and 64 <= K / 32 <= 64 * waves (K split over the wavefronts): the fused
+// M = 1 matvec; pre-quantized Q8_0 weights with 2 .. 4 activation rows; 4
+// rows of Q4_0 and 3 or 4 rows with slices beyond 48 blocks (matrix-core
+// form).  Any other shape is not handled here (hipErrorNotSupported,
+// nothing launched): the row-streaming kernel takes it.
 hipError_t launch_fx(const RowsArgs &a, hipStream_t s, const char **name) {
     const int nb = a.K / QK;
-    if (a.x == nullptr || a.M != 1 || (nb > 32 && nb < 64) || nb > 64 * QMV_FX_WPB) return hipErrorNotSupported;
+    if ((a.x != nullptr && a.M != 1) || a.M < 1 || a.M > 4 || (nb > 32 && nb < 64) || nb > 64 * QMV_FX_WPB)
+        return hipErrorNotSupported;
     return a.qtype == 4 ? launch_q<4>(a, s, name) : launch_q<8>(a, s, name);
 }
 

@@ -25,9 +25,9 @@ struct RowsArgs {
 };
 
 hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name);
-// Fused M = 1 matvec with the K dimension split over the wavefronts of a
-// workgroup; returns hipErrorNotSupported (nothing launched) for shapes it
-// does not cover.
+// Split-K product (the K dimension split over the wavefronts of a
+// workgroup): the fused M = 1 matvec and pre-quantized M = 1 .. 4; returns
+// hipErrorNotSupported (nothing launched) for shapes it does not cover.
 hipError_t launch_fx(const RowsArgs &a, hipStream_t s, const char **name);
 // LDS bytes the row-streaming kernel needs for M activation rows of K
 // (fused: the float32 activation is staged too).

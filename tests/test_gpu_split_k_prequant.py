@@ -1,0 +1,149 @@
+"""Products on pre-quantized Q8_0 activations (M = 1 .. 4 rows, through
+qmv_matvec_q4/q8 for M = 1 and qmv_gemm_q4/q8 for M = 2 .. 4) on the GPU
+against the oracle, over every kernel that serves them: the split-K kernel
+in its dot-product form (whole rows for K / 32 <= 32; K split for 2 .. 4
+rows of Q8_0) and its 4 x 4 matrix-core form (4 rows of Q4_0; 3 or 4 rows
+with slices of more than 48 blocks), and the row-streaming kernel (one row,
+2 or 3 rows of Q4_0, and K outside the split-K range).  Shapes cover small
+K, ragged slices, partial last passes, slices of up to 64 blocks, row
+sub-ranges with several activation rows, and rows-per-workgroup caps.
+
+Block sums are checked bit for bit through the public entry points with
+unit weight and activation scales: y[m, r] is then the exact sum of the
+block sums (while every partial sum stays below 2^24 in magnitude)."""
+import numpy as np
+import pytest
+import torch
+
+import pins
+from block_quantized_decode_amd import qmv, synth
+from gpu_util import announce, check_close, dev, host
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(rng, qtype, rows, k, raw=True):
+    if raw:
+        return synth.raw_q4(rng, rows, k) if qtype == 4 else synth.raw_q8(rng, rows, k)
+    w = synth.normal(rng, (rows, k), 0.02)
+    return orc.quantize_q4(w) if qtype == 4 else orc.quantize_q8(w)
+
+
+def _product(qtype, m, wq, wd, xq, xd, r0=None, r1=None, Y=None):
+    """Y [m, rows] through the matvec entry point (m = 1) or the batched one."""
+    if m == 1:
+        f = qmv.qmv_matvec_q4 if qtype == 4 else qmv.qmv_matvec_q8
+        y = f(dev(wq), dev(wd), dev(xq.reshape(-1)), dev(xd.reshape(-1)), r0, r1,
+              None if Y is None else Y.reshape(-1))
+        return y.reshape(1, -1)
+    f = qmv.qmv_gemm_q4 if qtype == 4 else qmv.qmv_gemm_q8
+    return f(dev(wq), dev(wd), dev(xq), dev(xd), r0, r1, Y)
+
+
+# (rows, K): K / 32 = 1, 16, 28, 32 (whole rows per wavefront), 64 (smallest
+# split), 65 and 66 (ragged slices), 128 (Llama-7B W_up), 172, 344 (W_down),
+# 384 (the largest dot-product slice for 3 and 4 rows), 417 (ragged, beyond
+# it), 512 (the largest slice); rows with partial last passes and fewer rows
+# than compute units
+SHAPES = [(1, 32), (33, 512), (7, 896), (301, 896), (77, 1024), (5, 2048), (257, 2080), (3, 2112),
+          (1031, 4096), (64, 5504), (37, 11008), (23, 12288), (19, 13344), (130, 16384)]
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("rows,k", SHAPES)
+def test_prequant_exact_block_sums(qtype, m, rows, k):
+    announce(f"split-K pre-quantized exact sums q{qtype} m={m} {rows}x{k}")
+    rng = np.random.default_rng(1500 + 7 * m + rows + k)
+    wq, _ = _weights(rng, qtype, rows, k)
+    xq = synth.raw_q8(rng, m, k)[0]
+    shrink = 2 if k <= 1024 else (8 if qtype == 4 else 64)
+    xq = (xq // shrink).astype(np.int8)        # keeps sum_b |sumi| below 2^24
+    for i in range(m):
+        assert np.all(np.abs(orc.block_sums(qtype, wq, xq[i])).astype(np.int64).sum(axis=1) < 2 ** 24)
+    want = xq.astype(np.int64) @ pins.w_values(qtype, wq).T
+    ones_w = np.ones((rows, k // 32), np.float32)
+    ones_x = np.ones((m, k // 32), np.float32)
+    Y = host(_product(qtype, m, wq, ones_w, xq, ones_x))
+    assert np.array_equal(Y.astype(np.int64), want)
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("rows,k", SHAPES)
+def test_prequant_tolerance(qtype, m, rows, k):
+    announce(f"split-K pre-quantized q{qtype} m={m} {rows}x{k}")
+    rng = np.random.default_rng(1600 + 7 * m + rows + k)
+    wq, wd = _weights(rng, qtype, rows, k, raw=False)
+    X = synth.normal(rng, (m, k))
+    X[:, rng.choice(k, size=max(1, k // 100), replace=False)] *= np.float32(20.0)
+    xq, xd = orc.quantize_q8(X)
+    Yref = orc.gemm(qtype, wq, wd, xq, xd)
+    Y = host(_product(qtype, m, wq, wd, xq, xd))
+    for i in range(m):
+        check_close(qtype, Y[i], Yref[i], wq, wd, xq[i], xd[i], what=f"q{qtype} m={m} {rows}x{k} row {i}")
+    Y2 = host(_product(qtype, m, wq, wd, xq, xd))
+    assert np.array_equal(Y, Y2), "same inputs, same bits"
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("m", [1, 4])
+def test_prequant_row_ranges(qtype, m):
+    announce(f"split-K pre-quantized row ranges q{qtype} m={m}")
+    rng = np.random.default_rng(1700 + m)
+    for rows, k, ranges in ((1333, 11008, ((0, 1333), (1, 2), (3, 11), (17, 1300), (1329, 1333), (640, 640))),
+                            (3001, 896, ((0, 3001), (2, 3), (5, 70), (999, 3001), (2990, 2999)))):
+        wq, wd = _weights(rng, qtype, rows, k, raw=False)
+        X = synth.normal(rng, (m, k))
+        xq, xd = orc.quantize_q8(X)
+        Yref = orc.gemm(qtype, wq, wd, xq, xd)
+        for r0, r1 in ranges:
+            Ydev = torch.full((m, rows), -7.5, dtype=torch.float32, device="cuda:0")
+            Y = host(_product(qtype, m, wq, wd, xq, xd, r0, r1, Ydev))
+            assert np.all(Y[:, :r0] == -7.5) and np.all(Y[:, r1:] == -7.5), f"rows outside [{r0},{r1}) written"
+            if r1 > r0:
+                for i in range(m):
+                    check_close(qtype, Y[i], Yref[i], wq, wd, xq[i], xd[i], r0, r1, what=f"[{r0},{r1}) row {i}")
+
+
+@pytest.mark.parametrize("qtype,m", [(8, 3), (4, 4)])
+def test_prequant_rows_per_workgroup_cap(qtype, m):
+    """More rows per compute unit than the slice-sum region holds (1024 rows
+    for 3 activation rows in the dot-product form, 256 in the matrix-core
+    form): the grid grows beyond one workgroup per compute unit; every row
+    of every activation row is written once."""
+    announce(f"split-K pre-quantized many rows q{qtype} m={m} 270000x2048")
+    rng = np.random.default_rng(1800 + m)
+    rows, k = 270000, 2048
+    wq, wd = _weights(rng, qtype, rows, k)
+    X = synth.normal(rng, (m, k))
+    xq, xd = orc.quantize_q8(X)
+    Yref = orc.gemm(qtype, wq, wd, xq, xd)
+    Y = host(_product(qtype, m, wq, wd, xq, xd))
+    assert qmv.last_kernel().startswith("px_" if qtype == 8 else "mq_"), qmv.last_kernel()
+    for i in range(m):
+        check_close(qtype, Y[i], Yref[i], wq, wd, xq[i], xd[i], what=f"270000 rows, row {i}")
+
+
+def test_prequant_kernel_choice():
+    """Pre-quantized calls: K / 32 <= 32 runs the split-K kernel's
+    whole-row mode (M = 1 .. 4); for K / 32 in [64, 512] the matrix-core
+    form takes 4 rows of Q4_0 and 3 or 4 rows with slices of more than 48
+    blocks (K / 32 > 384), the dot-product form 2 .. 4 rows of Q8_0, and the
+    row-streaming kernel one row and 2 or 3 rows of Q4_0 (measured as fast
+    or faster there); other K, and more rows, the row-streaming kernel."""
+    announce("split-K pre-quantized kernel choice")
+    rng = np.random.default_rng(1900)
+    cases = [(4, 1, 32, "px_"), (4, 1, 1024, "px_"), (4, 1, 1056, "rows_"), (4, 1, 2048, "rows_"),
+             (4, 1, 16384, "rows_"), (4, 2, 16384, "rows_"), (4, 3, 12288, "rows_"), (4, 3, 12320, "mq_"),
+             (4, 4, 2048, "mq_"), (4, 4, 11008, "mq_"), (4, 4, 16384, "mq_"), (4, 4, 16416, "rows_"),
+             (4, 4, 896, "px_"), (4, 5, 2048, "rows_"), (4, 8, 4096, "rows_"),
+             (8, 1, 2048, "rows_"), (8, 2, 2048, "px_"), (8, 3, 2048, "px_"), (8, 4, 11008, "px_"),
+             (8, 2, 16384, "px_"), (8, 2, 16416, "rows_"), (8, 4, 12320, "mq_"), (8, 1, 896, "px_")]
+    for qtype, m, k, want in cases:
+        wq, wd = _weights(rng, qtype, 8, k)
+        xq, xd = orc.quantize_q8(synth.normal(rng, (m, k)))
+        _product(qtype, m, wq, wd, xq, xd)
+        torch.cuda.synchronize()
+        assert qmv.last_kernel().startswith(want), (qtype, m, k, qmv.last_kernel())
