@@ -19,7 +19,10 @@ pre-quantized activation rows) is reported under "small_batch".  The
 second half of the metric, the M >= 16 product on the int8 matrix cores
 (GOP/s and % of the int8 peak on the batched workload: both FFN matrices,
 Q4_0 and Q8_0, M = 16 and 64), is measured the same way and reported under
-"batched".
+"batched".  "env" holds the per-launch floor of the smallest libqmv kernel
+replayed the same way and the shader clock rocm-smi reports; the CPU
+baseline also gives the oracle's single-thread rate, the host CPU model
+and the oracle's compiler flags.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -217,6 +220,9 @@ def main():
     if wl.name.startswith("llama7b") and 4 in wl.ms:
         small = small_batch_bench(wl, qtype, mats, stream, args.steps, args.warmup)
 
+    floor_us = launch_floor(stream)
+    sclk = gpu_clock_mhz()
+
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
     if not args.no_batched:
@@ -252,6 +258,7 @@ def main():
             "event_timed_launch_us": {k: round(float(np.mean(v)), 3) for k, v in per_matrix_us.items()},
             "setup_s": round(setup_s, 1),
         },
+        "env": {"launch_floor_us": floor_us, "gpu_sclk_mhz": sclk},
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
@@ -272,6 +279,66 @@ def main():
     print(json.dumps(line), flush=True)
     if cpu is not None and not cpu.get("parity_ok", True):
         sys.exit(1)
+
+
+def launch_floor(stream, n=16, reps=50):
+    """Per-launch time of the smallest libqmv kernel (Q8_0 quantization of
+    one 32-element block), n launches per HIP graph: the floor under any
+    one launch of the step, replayed the same way."""
+    import torch
+
+    from block_quantized_decode_amd import qmv
+
+    x = torch.ones(32, dtype=torch.float32, device="cuda:0")
+    q = torch.empty(32, dtype=torch.int8, device="cuda:0")
+    d = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    with torch.cuda.stream(stream):
+        qmv.qmv_quantize_q8(x, q, d)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(n):
+            qmv.qmv_quantize_q8(x, q, d)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return round(t0.elapsed_time(t1) * 1e3 / (reps * n), 3)
+
+
+def gpu_clock_mhz():
+    """Current shader clock of cuda:0 from its sysfs DPM table (the level
+    marked '*' in pp_dpm_sclk), or None where that file is not readable.
+    A plain file read: no subprocess is started from this GPU process."""
+    import glob
+    import re
+
+    import torch
+
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    except (AttributeError, AssertionError, RuntimeError):
+        return None
+    for dev_dir in glob.glob("/sys/class/drm/card*/device"):
+        try:
+            if not os.path.realpath(dev_dir).rsplit("/", 1)[-1].startswith(bus):
+                continue
+            with open(os.path.join(dev_dir, "pp_dpm_sclk")) as f:
+                for ln in f:
+                    if "*" in ln:
+                        m = re.search(r"(\d+)\s*Mhz", ln, re.I)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+    return None
 
 
 def small_batch_bench(wl, qtype, mats, stream, steps, warmup):
@@ -447,6 +514,12 @@ def cpu_baseline(wl, qtype, mats, target_s):
         if el >= target_s:
             break
     pool.shutdown()
+    # the same step on one thread (rows [0, rows) per call)
+    t1 = time.perf_counter()
+    for mt, wq, wd, xh, _, out in prepared:
+        xq, xd = orc.quantize_q8(xh)
+        orc.matvec(qtype, wq, wd, xq, xd, 0, mt.rows, y=out)
+    el1 = time.perf_counter() - t1
     parity_ok = True
     worst = 0.0
     for mt, wq, wd, xh, ygpu, out in prepared:
@@ -456,13 +529,23 @@ def cpu_baseline(wl, qtype, mats, target_s):
         worst = max(worst, float((err / tol).max()))
         parity_ok &= bool(np.all(err <= tol))
     wbytes = wl.weight_bytes(qtype)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(wbytes * passes / el / 1e9, 3),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
+        "single_thread_gb_s": round(wbytes / el1 / 1e9, 3),
+        "cpu_model": cpu_model,
+        "oracle_cflags": " ".join(["gcc", *orc.CFLAGS]),
         "sample": f"the full step ({len(prepared)} matrices, {wbytes} weight bytes, activation quantization "
-                  f"included) repeated {passes} times in {el:.1f} s, rows split over {cores} threads",
+                  f"included) repeated {passes} times in {el:.1f} s, rows split over {cores} threads; "
+                  f"once more on one thread in {el1:.1f} s",
         "parity_ok": parity_ok,
         "parity_max_err_over_tol": round(worst, 4),
     }
