@@ -19,7 +19,9 @@ pre-quantized activation rows) is reported under "small_batch".  The
 second half of the metric, the M >= 16 product on the int8 matrix cores
 (GOP/s and % of the int8 peak on the batched workload: both FFN matrices,
 Q4_0 and Q8_0, M = 16 and 64), is measured the same way and reported under
-"batched".  "env" holds the per-launch floor of the smallest libqmv kernel
+"batched".  The other configurations (256 x 512 Q8_0, a TinyLlama-1.1B
+layer with and without concatenated projections, the Qwen2.5-0.5B FFN and
+lm_head) are timed per call and per layer under "other_workloads".  "env" holds the per-launch floor of the smallest libqmv kernel
 replayed the same way and the shader clock rocm-smi reports; the CPU
 baseline also gives the oracle's single-thread rate, the host CPU model
 and the oracle's compiler flags.
@@ -52,6 +54,8 @@ def parse():
     ap.add_argument("--workload", default="llama7b_ffn_stack_q4")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the M >= 16 matrix-core measurement")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the per-call timings of the other configurations (keeps kernel traces to the step)")
     ap.add_argument("--batched-only", action="store_true",
                     help="only the M >= 16 matrix-core measurement (one JSON object; for profiling that path)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -223,6 +227,11 @@ def main():
     floor_us = launch_floor(stream)
     sclk = gpu_clock_mhz()
 
+    # ---- the other configurations: per call and per layer, cold
+    others = None
+    if not args.no_others:
+        others = other_workloads_bench(stream)
+
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
     if not args.no_batched:
@@ -274,6 +283,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "small_batch": small,
+        "other_workloads": others,
         "batched": batched,
     }
     print(json.dumps(line), flush=True)
@@ -339,6 +349,121 @@ def gpu_clock_mhz():
         except OSError:
             return None
     return None
+
+
+def _graph_us(calls, stream, reps=20):
+    """Microseconds per replay of a HIP graph of `calls` (after warm-up)."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / reps
+
+
+def other_workloads_bench(stream):
+    """The other configurations, per call and per layer, through the fused
+    entry point (M = 1, float32 activation), timed like the step: graphs of
+    prepared calls.  Weights are random normal draws quantized on the GPU
+    and rotated over copies whose total exceeds the 256 MB last-level cache
+    (TinyLlama layer x 20, Qwen2.5-0.5B FFN + lm_head x 4), so each call
+    streams from HBM; the 256 x 512 parity matrix (147 KB) is timed warm.
+    The TinyLlama layer is also timed with the projections concatenated as
+    the forward pass writes them (W_q|W_k|W_v 2560 x 2048, W_gate|W_up
+    11264 x 2048): 4 launches per layer instead of 7."""
+    import torch
+
+    from block_quantized_decode_amd import qmv, synth
+
+    dev = torch.device("cuda:0")
+    torch.manual_seed(5)
+    out = {}
+
+    def quantized(rows, cols, qtype):
+        w = torch.randn(rows, cols, device=dev) * 0.02
+        q, d = qmv.qmv_quantize_weights(w, qtype)
+        del w
+        return q, d
+
+    def calls_for(mats, qtype, copies):
+        """Per copy: [(name, prepared call, weight bytes)] in matrix order."""
+        xs = {}
+        res = []
+        for c in range(copies):
+            row = []
+            for name, rows, cols, act in mats:
+                q, d = quantized(rows, cols, qtype)
+                if act not in xs:
+                    xs[act] = torch.randn(cols, device=dev)
+                y = torch.zeros(rows, device=dev)
+                row.append((name, qmv.prepare_matvec_fx(qtype, q, d, xs[act], y, stream=stream.cuda_stream),
+                            q.numel() + d.numel() * 4))
+            res.append(row)
+        return res
+
+    # 256 x 512 Q8_0, warm
+    wl = synth.WORKLOADS["q8_256x512"]
+    cs = calls_for([(m.name, m.rows, m.cols, m.act) for m in wl.matrices], 8, 1)
+    us = _graph_us([cs[0][0][1]] * 16, stream) / 16
+    out[wl.name] = {"us_per_call": round(us, 3), "weight_gb_s": round(cs[0][0][2] / (us * 1e-6) / 1e9, 1),
+                    "note": "warm (147 KB stays in cache)", "kernel": qmv.last_kernel()}
+
+    # TinyLlama layer, Q4_0: per matrix, per layer, and concatenated
+    wl = synth.WORKLOADS["tinyllama_layer_q4"]
+    mats = [(m.name, m.rows, m.cols, m.act) for m in wl.matrices]
+    copies = 20
+    cs = calls_for(mats, 4, copies)
+    per = {}
+    for i, (name, *_r) in enumerate(mats):
+        per[name] = round(_graph_us([cs[c][i][1] for c in range(copies)], stream) / copies, 3)
+    layer_us = _graph_us([call for row in cs for _, call, _ in row], stream) / copies
+    lbytes = sum(b for _, _, b in cs[0])
+    del cs
+    torch.cuda.empty_cache()
+    cat = [("W_qkv", 2560, 2048, "x_attn"), ("W_o", 2048, 2048, "x_o"), ("W_gate_up", 11264, 2048, "x_ffn"),
+           ("W_down", 2048, 5632, "x_down")]
+    cs = calls_for(cat, 4, copies)
+    cat_us = _graph_us([call for row in cs for _, call, _ in row], stream) / copies
+    del cs
+    torch.cuda.empty_cache()
+    out[wl.name] = {"per_matrix_us": per, "layer_us": round(layer_us, 3), "layer_launches": len(mats),
+                    "layer_weight_gb_s": round(lbytes / (layer_us * 1e-6) / 1e9, 1),
+                    "layer_concat_us": round(cat_us, 3), "layer_concat_launches": len(cat),
+                    "layer_concat_weight_gb_s": round(lbytes / (cat_us * 1e-6) / 1e9, 1),
+                    "copies": copies}
+
+    # Qwen2.5-0.5B FFN + lm_head, Q8_0
+    wl = synth.WORKLOADS["qwen05b_ffn_lmhead_q8"]
+    mats = [(m.name, m.rows, m.cols, m.act) for m in wl.matrices]
+    copies = 4
+    cs = calls_for(mats, 8, copies)
+    per, gbs = {}, {}
+    for i, (name, *_r) in enumerate(mats):
+        us = _graph_us([cs[c][i][1] for c in range(copies)], stream) / copies
+        per[name] = round(us, 3)
+        gbs[name] = round(cs[0][i][2] / (us * 1e-6) / 1e9, 1)
+    ffn_us = _graph_us([cs[c][i][1] for c in range(copies) for i in range(3)], stream) / copies
+    del cs
+    torch.cuda.empty_cache()
+    out[wl.name] = {"per_matrix_us": per, "per_matrix_weight_gb_s": gbs, "ffn_us": round(ffn_us, 3),
+                    "lm_head_pct_hbm_peak": round(100.0 * gbs["lm_head"] / HBM_PEAK_GBS, 2), "copies": copies}
+    return out
 
 
 def small_batch_bench(wl, qtype, mats, stream, steps, warmup):

@@ -54,12 +54,16 @@ class _Lib:
             "orc_gemm_q8": [P, P, P, i32, i32, P, P, i32, i32, i32],
             "orc_gemm_q4": [P, P, P, i32, i32, P, P, i32, i32, i32],
             "orc_tol_abs": [ctypes.c_int, P, P, i32, P, P, i32, i32, P],
+            "orc_rmsnorm": [P, P, P, i64, ctypes.c_float],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = None
             setattr(self, name, f)
+        self.orc_sumsq = L.orc_sumsq
+        self.orc_sumsq.argtypes = [P, i64]
+        self.orc_sumsq.restype = ctypes.c_float
 
 
 _lib = None
@@ -219,3 +223,21 @@ def tol_abs(qtype, wq, wd, xq, xd, r0=None, r1=None):
 def tolerance(qtype, wq, wd, xq, xd, r0=None, r1=None):
     """Allowed |y - y_ref| per row: 1e-5 * A(r) + 1e-6."""
     return 1e-5 * tol_abs(qtype, wq, wd, xq, xd, r0, r1) + 1e-6
+
+
+def sumsq(x):
+    """The rmsnorm sum of squares in its stated order (pairwise within each
+    32-element block, then pairwise over the zero-padded block sums)."""
+    x = _f32(x).reshape(-1)
+    assert x.size % QK == 0 and x.size > 0
+    return np.float32(lib().orc_sumsq(_p(x), x.size))
+
+
+def rmsnorm(x, w, eps):
+    """o_j = w_j * (inv * x_j), inv = 1 / sqrt(sumsq(x) / n + eps), binary32."""
+    x = _f32(x).reshape(-1)
+    w = _f32(w).reshape(-1)
+    assert x.size == w.size and x.size % QK == 0 and x.size > 0
+    o = np.empty_like(x)
+    lib().orc_rmsnorm(_p(o), _p(x), _p(w), x.size, float(eps))
+    return o

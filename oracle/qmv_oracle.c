@@ -27,9 +27,14 @@
  *                       operations: "parity unpinned" beyond the bound.
  *   orc_gemm_*          pinned (M=1 slice and per-row equality with matvec)
  *   orc_tol_abs         pinned (closed forms)
+ *   orc_sumsq           pinned (a hand-derived pairwise sum that a left-to-
+ *                       right sum would not give, exact integer sums)
+ *   orc_rmsnorm         pinned (closed forms at constant input, sign and
+ *                       power-of-two invariants, fp64 brute force)
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define QK 32 /* block length, spec section 4 */
@@ -266,4 +271,55 @@ void orc_tol_abs(int type, const void *wq, const float *wd, int32_t cols,
         }
         out[r - r0] = a;
     }
+}
+
+/* ------------------------------------------------------------------------
+ * Root-mean-square normalization ahead of a quantization (spec section 5
+ * kernel list, ml_k_rmsnorm(o, x, w, n, eps); section 6 forward pass, where
+ * every quantize_q8 of a layer input follows one).  The spec lists the
+ * signature only; the formula read here is the llama2.c one the spec
+ * follows elsewhere (section 5, RoPE bullet):
+ *   ss = sum over j of x_j^2,  inv = 1 / sqrt(ss / n + eps),
+ *   o_j = w_j * (inv * x_j).
+ * The spec leaves the order of the sum open.  Read here: pairwise
+ * summation (recursive halving) of the 32 squares of each 32-element block
+ * of the Q8_0 format, then pairwise summation of the block sums with their
+ * count padded to a power of two by zeros (adding a zero is exact, so the
+ * padding changes no rounding).  Every float operation rounds to
+ * nearest-even in binary32; sqrtf and the divisions are correctly rounded.
+ * n must be a positive multiple of 32 (at most 2^24).
+ * ---------------------------------------------------------------------- */
+static float pairwise_sum(const float *v, int64_t n)  /* n a power of two */
+{
+    if (n == 1)
+        return v[0];
+    return pairwise_sum(v, n / 2) + pairwise_sum(v + n / 2, n / 2);
+}
+
+float orc_sumsq(const float *x, int64_t n)
+{
+    int64_t nb = n / QK, p = 1;
+    while (p < nb)
+        p *= 2;
+    float *bs = calloc((size_t)p, sizeof(float));  /* zeros past nb */
+    if (bs == NULL)
+        return NAN;
+    float sq[QK];
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int i = 0; i < QK; ++i)
+            sq[i] = x[b * QK + i] * x[b * QK + i];
+        bs[b] = pairwise_sum(sq, QK);
+    }
+    float ss = pairwise_sum(bs, p);
+    free(bs);
+    return ss;
+}
+
+void orc_rmsnorm(float *o, const float *x, const float *w, int64_t n, float eps)
+{
+    float ss = orc_sumsq(x, n);
+    float mean = ss / (float)n;
+    float inv = 1.0f / sqrtf(mean + eps);
+    for (int64_t j = 0; j < n; ++j)
+        o[j] = w[j] * (inv * x[j]);
 }

@@ -308,7 +308,9 @@ def check_matvec_unit_scales():
         y = orc.matvec(qtype, wq, ones_w, xq, ones_x)
         want = (w_values(qtype, wq) * xq.astype(np.int64)[None, :]).sum(axis=1)
         assert np.all(np.abs(want) < 2 ** 24)
-        assert np.all(np.isfinite(y)) and np.array_equal(y.astype(np.int64), want)
+        # integers below 2^24 in magnitude before the exact comparison (a wrong
+        # oracle may produce values no int64 holds)
+        assert np.all(np.abs(y) < 2.0 ** 24) and np.array_equal(y.astype(np.int64), want)
         # one-hot dx isolates one block's sum at any K
         for b in (0, k // QK - 1, 5):
             oh = np.zeros(k // QK, np.float32)
@@ -358,6 +360,63 @@ def check_gemm_rows():
             assert np.all(np.abs(Y[i].astype(np.float64) - y64) <= 1e-5 * a64 + 1e-6)
 
 
+def check_sumsq_pairwise_order():
+    """The rmsnorm sum of squares in its stated order, on inputs where the
+    order decides the rounding (values derived by hand):
+      * one block: x_0 = 1, x_1..x_31 = 2^-12 (squares 1 and 2^-24).  Pairwise:
+        1 + 2^-24 ties to 1; the fifteen other pairs give 2^-23 each; then
+        1 + 2^-23, + 2^-22, + 2^-21, + 2^-20 are exact: 1 + 15 * 2^-23.  A
+        left-to-right sum stays at 1 (every + 2^-24 ties back to 1).
+      * four blocks with sums 1, 2^-24, 2^-24, 2^-24: pairwise over the
+        blocks, (1 + 2^-24) + (2^-24 + 2^-24) = 1 + 2^-23; left to right, 1.
+      * three blocks (padded to four): sums 1, 2^-24, 2^-24 -> (1 + 2^-24) +
+        (2^-24 + 0) = 1 + 2^-24 -> 1."""
+    x = np.zeros(64, np.float32)
+    x[0] = 1.0
+    x[1:32] = np.float32(2.0 ** -12)
+    assert orc.sumsq(x) == np.float32(1.0 + 15 * 2.0 ** -23)
+    x = np.zeros(128, np.float32)
+    x[0] = 1.0
+    x[32] = x[64] = x[96] = np.float32(2.0 ** -12)
+    assert orc.sumsq(x) == np.float32(1.0 + 2.0 ** -23)
+    assert orc.sumsq(x[:96]) == np.float32(1.0)
+    # integer squares: every order is exact
+    rng = np.random.default_rng(21)
+    xi = rng.integers(-40, 41, size=32 * 28).astype(np.float32)
+    assert orc.sumsq(xi) == np.float32(int((xi.astype(np.int64) ** 2).sum()))
+
+
+def check_rmsnorm_closed_forms():
+    """Constant input: ss / n is the constant's square exactly, so with
+    eps = 0, inv * x rounds to exactly 1 and o = w bit for bit (x = 1, and
+    x = 3 where inv = RN(1/3) and RN(RN(1/3) * 3) = 1).  A zero input gives
+    zeros (eps > 0 keeps inv finite)."""
+    for n in (4096, 896, 64):
+        w = (np.arange(n, dtype=np.float32) - np.float32(n / 3)) * np.float32(0.01)
+        for c in (1.0, 3.0, -1.0):
+            o = orc.rmsnorm(np.full(n, c, np.float32), w, 0.0)
+            assert np.array_equal(o, w * np.float32(np.sign(c))), (n, c)
+        o = orc.rmsnorm(np.zeros(n, np.float32), w, 1e-5)
+        assert np.all(o == 0.0)
+
+
+def check_rmsnorm_invariants_and_brute():
+    rng = np.random.default_rng(22)
+    for n, sigma, eps in ((4096, 1.0, 1e-5), (2048, 0.01, 1e-4), (896, 3.0, 1e-6), (32 * 13, 0.5, 0.5)):
+        x = (rng.standard_normal(n) * sigma).astype(np.float32)
+        w = (1.0 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+        o = orc.rmsnorm(x, w, eps)
+        # float64 brute force: binary32 rounding of a few operations only
+        x64, w64 = x.astype(np.float64), w.astype(np.float64)
+        o64 = w64 * x64 / np.sqrt((x64 * x64).sum() / n + eps)
+        assert np.all(np.abs(o - o64) <= 4 * np.finfo(np.float32).eps * np.abs(o64) + 1e-30), n
+        assert np.array_equal(orc.rmsnorm(-x, w, eps), -o)
+        # powers of two scale every step exactly (eps = 0)
+        o0 = orc.rmsnorm(x, w, 0.0)
+        for k in (-3, 5):
+            assert np.array_equal(orc.rmsnorm(x * np.float32(2.0 ** k), w, 0.0), o0), (n, k)
+
+
 ALL_CHECKS = [
     check_q8_zero_block, check_q8_equal_block, check_q8_clamp_and_range,
     check_q8_unit_scale_textbook, check_q8_ties, check_q8_detectors,
@@ -366,6 +425,7 @@ ALL_CHECKS = [
     check_block_sum_closed_forms, check_block_sums_brute,
     check_matvec_brute64, check_matvec_unit_scales, check_matvec_invariants,
     check_gemm_rows,
+    check_sumsq_pairwise_order, check_rmsnorm_closed_forms, check_rmsnorm_invariants_and_brute,
 ]
 
 

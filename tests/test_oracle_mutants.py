@@ -41,6 +41,15 @@ MUTANTS = [
     ("sum_sign", "sumi += (int32_t)q4_elem(blk, i) * (int32_t)xv[i];", "sumi -= (int32_t)q4_elem(blk, i) * (int32_t)xv[i];", None),
     ("y_relative_index", "y[r] = row_q8(wq, wd, cols, xq, xd, r);", "y[r - r0] = row_q8(wq, wd, cols, xq, xd, r);", 1),
     ("gemm_x_stride", "xq + (int64_t)i * cols, xd + (int64_t)i * nb, r0, r1);", "xq + (int64_t)i * cols, xd, r0, r1);", None),
+    ("rms_block_left_to_right", "bs[b] = pairwise_sum(sq, QK);",
+     "float t = 0.0f;\n        for (int i = 0; i < QK; ++i)\n            t += sq[i];\n        bs[b] = t;", 1),
+    ("rms_blocks_left_to_right", "float ss = pairwise_sum(bs, p);",
+     "float ss = 0.0f;\n    for (int64_t b = 0; b < p; ++b)\n        ss += bs[b];", 1),
+    ("rms_no_eps", "float inv = 1.0f / sqrtf(mean + eps);", "float inv = 1.0f / sqrtf(mean);", 1),
+    ("rms_n_minus_1", "float mean = ss / (float)n;", "float mean = ss / (float)(n - 1);", 1),
+    ("rms_no_weight", "o[j] = w[j] * (inv * x[j]);", "o[j] = inv * x[j];", 1),
+    ("rms_abs_not_square", "sq[i] = x[b * QK + i] * x[b * QK + i];", "sq[i] = fabsf(x[b * QK + i]);", 1),
+    ("rms_weight_shift", "o[j] = w[j] * (inv * x[j]);", "o[j] = w[(j + 1) % n] * (inv * x[j]);", 1),
 ]
 
 
