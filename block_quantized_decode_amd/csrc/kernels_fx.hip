@@ -107,11 +107,41 @@ __device__ __forceinline__ float group_sum(float a) {
 // 160 KiB of a compute unit.
 constexpr int rw_cap(int M) { return M <= 3 ? 1024 : 512; }
 
-template <int QT, int M, bool FX, int T, int NBL, int D, int D0, int WPB, bool KS>
+// Activation forms of k_fx: Q8_0 rows as given, a float32 row quantized in
+// the kernel, or a float32 row normalized (rmsnorm) and then quantized.
+enum { kActQ8 = 0, kActF32 = 1, kActRms = 2 };
+
+// The rmsnorm scale 1 / sqrt(ss / n + eps), each operation rounded on its
+// own (contraction off; the division and the square root are the correctly
+// rounded ones).
+__device__ __forceinline__ float rms_inv(float ss, int n, float eps) {
+#pragma clang fp contract(off)
+    const float mean = ss / (float)n;
+    return 1.0f / sqrtf(mean + eps);
+}
+
+// w * (inv * x), two roundings.
+__device__ __forceinline__ float rms_apply(float x, float w, float inv) {
+#pragma clang fp contract(off)
+    const float t = inv * x;
+    return w * t;
+}
+
+// Pairwise (recursive-halving) sum of the squares of 8 consecutive values.
+__device__ __forceinline__ float sumsq8(float4 a, float4 b) {
+#pragma clang fp contract(off)
+    const float s0 = a.x * a.x, s1 = a.y * a.y, s2 = a.z * a.z, s3 = a.w * a.w;
+    const float s4 = b.x * b.x, s5 = b.y * b.y, s6 = b.z * b.z, s7 = b.w * b.w;
+    return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
+}
+
+template <int QT, int M, int AX, int T, int NBL, int D, int D0, int WPB, bool KS>
 __global__ void __launch_bounds__(64 * WPB)
 k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
      const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xd,
-     int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1, int32_t rw) {
+     const float *__restrict__ xn, float eps, int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0,
+     int32_t r1, int32_t rw) {
+    constexpr bool FX = AX != kActQ8;          // float32 activation, quantized here
     constexpr int PASS = 64 / T;               // rows per pass
     constexpr int QB = (QT == 8) ? 32 : 16;    // quant bytes per block
     static_assert(T * NBL <= 64 && (T * NBL) % 16 == 0, "a slice is at most 64 blocks, loaded 16 blocks at a time");
@@ -121,6 +151,7 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     __shared__ v4i s_lo[M][WPB][64], s_hi[M][WPB][64];
     __shared__ float s_dx[M][WPB][64];
     __shared__ int s_sx[M][WPB][64];
+    __shared__ float s_bs[AX == kActRms ? 64 * WPB : 1];  // rmsnorm: sums of squares per block
     extern __shared__ float s_red[];           // [M][WPB][rw] slice sums
 
     const int nb = K >> 5;
@@ -145,17 +176,23 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     //    in the fused form, the quants and the block scale otherwise)
     constexpr int NR = T * NBL / 16;           // rounds of 16 blocks
     constexpr int MX = FX ? 1 : M;
-    float4 xa[FX ? NR : 1], xb[FX ? NR : 1];
+    constexpr int NRN = AX == kActRms ? NR : 1;
+    float4 xa[FX ? NR : 1], xb[FX ? NR : 1], na[NRN], nb8[NRN];
     int xv0[MX][FX ? 1 : NR], xv1[MX][FX ? 1 : NR];
     float xdv[MX][FX ? 1 : NR];
     if constexpr (FX) {
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * 4);
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(xn, AX == kActRms ? K * 4 : 0);
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
             const int b = 16 * k + (lane >> 2);
             const int o = b < ns ? (kb0 + b) * 128 + 32 * (lane & 3) : kOOB;
             xa[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
             xb[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16, 0, 0));
+            if constexpr (AX == kActRms) {  // the norm weights of the same elements
+                na[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rn, o, 0, 0));
+                nb8[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rn, o + 16, 0, 0));
+            }
         }
     } else {
         const __amdgpu_buffer_rsrc_t rxq = make_rsrc(xq, M * K);
@@ -209,6 +246,51 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
 #pragma unroll
     for (int d = 0; d < D0; ++d) load(ring[d], d);
     __builtin_amdgcn_sched_barrier(0);
+
+    // 3a. rmsnorm: sum of squares of every block (pairwise over its 32
+    //     elements: 8 per lane, then the 4 lanes of the block), the blocks'
+    //     sums pairwise over their zero-padded count, then x <- w * (inv * x)
+    if constexpr (AX == kActRms) {
+        float *bs = KS ? s_bs : s_bs + 64 * wid;  // split K: the workgroup's K; whole rows: this wavefront's
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int b = 16 * k + (lane >> 2);
+            float q = sumsq8(xa[k], xb[k]);
+            q += __int_as_float(dpp_xor1(__float_as_int(q)));
+            q += __int_as_float(dpp_xor2(__float_as_int(q)));
+            if ((lane & 3) == 0 && b < ns) bs[kb0 + b] = q;
+        }
+        if constexpr (KS) {
+            __syncthreads();
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        int P = 1;
+        while (P < nb) P *= 2;                 // block count padded to a power of two (at most 512)
+        const int E = P > 64 ? P / 64 : 1;     // consecutive block sums per lane
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int b = lane * E + e;
+            v[e] = (e < E && b < nb) ? bs[b] : 0.0f;
+        }
+        // pairwise within the lane (E = 1, 2, 4 or 8 values; the rest are 0)
+        float ss = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        if (E == 1) ss = v[0];
+        else if (E == 2) ss = v[0] + v[1];
+        else if (E == 4) ss = (v[0] + v[1]) + (v[2] + v[3]);
+        // then across lanes: aligned groups of 2, 4, ... 64 lanes
+#pragma unroll
+        for (int o = 1; o < 64; o *= 2) ss += __shfl_xor(ss, o);
+        const float inv = rms_inv(ss, K, eps);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            xa[k] = make_float4(rms_apply(xa[k].x, na[k].x, inv), rms_apply(xa[k].y, na[k].y, inv),
+                                rms_apply(xa[k].z, na[k].z, inv), rms_apply(xa[k].w, na[k].w, inv));
+            xb[k] = make_float4(rms_apply(xb[k].x, nb8[k].x, inv), rms_apply(xb[k].y, nb8[k].y, inv),
+                                rms_apply(xb[k].z, nb8[k].z, inv), rms_apply(xb[k].w, nb8[k].w, inv));
+        }
+    }
 
     // 3. quantize the slice (fused) or sum its quants (pre-quantized), 4
     //    lanes per block (lanes past the slice hold zeros), into the
@@ -551,11 +633,12 @@ hipError_t launch_mq(const RowsArgs &a, hipStream_t s, const char **name) {
     return launch_mq_t<QT, 4, D, W>(a, s, name);
 }
 
-template <int QT, int M, bool FX, int T, int NBL, int D, int WPB, bool KS = true>
+template <int QT, int M, int AX, int T, int NBL, int D, int WPB, bool KS = true>
 hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
     static char kname[64];
     constexpr int D0 = QMV_FX_D0 < D - 1 ? QMV_FX_D0 : D - 1;
-    auto kern = k_fx<QT, M, FX, T, NBL, D, D0, WPB, KS>;
+    constexpr bool FX = AX != kActQ8;
+    auto kern = k_fx<QT, M, AX, T, NBL, D, D0, WPB, KS>;
     const int nrows = a.r1 - a.r0;
     const int grid = (nrows + rw - 1) / rw;
     const size_t lds = KS ? (size_t)M * WPB * rw * 4 : 0;
@@ -565,10 +648,11 @@ hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name)
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq, a.xd,
-                       a.xq_out, a.xd_out, a.r0, a.r1, rw);
+                       a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1, rw);
     if (kname[0] == 0) {
         if (FX)
-            snprintf(kname, sizeof kname, "fx_q%d_t%d_n%d_d%d_w%d%s", QT, T, NBL, D, WPB, KS ? "" : "_rows");
+            snprintf(kname, sizeof kname, "fx%s_q%d_t%d_n%d_d%d_w%d%s", AX == kActRms ? "n" : "", QT, T, NBL, D,
+                     WPB, KS ? "" : "_rows");
         else
             snprintf(kname, sizeof kname, "px_q%d_m%d_t%d_n%d_d%d_w%d%s", QT, M, T, NBL, D, WPB, KS ? "" : "_rows");
     }
@@ -583,8 +667,9 @@ constexpr int ring_depth() {
     return (QT == 8 && M * NBL > 6) ? 3 : QMV_FX_D;
 }
 
-template <int QT, int M, bool FX>
+template <int QT, int M, int AX>
 hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
+    constexpr bool FX = AX != kActQ8;
     constexpr int W = QMV_FX_WPB;
     const int nb = a.K / QK;
     const int S = (nb + W - 1) / W;
@@ -597,32 +682,33 @@ hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
         const int want = ((nrows + groups - 1) / groups + pass - 1) / pass * pass;
         return ks ? min(rw_cap(M), want) : want;
     };
-    if (nb <= 16) return launch_t<QT, M, FX, 16, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(4 * W, false), s, name);
-    if (nb <= 32) return launch_t<QT, M, FX, 32, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(2 * W, false), s, name);
+    if (nb <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(4 * W, false), s, name);
+    if (nb <= 32) return launch_t<QT, M, AX, 32, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(2 * W, false), s, name);
     // split K: the fused matvec, and pre-quantized Q8_0 weights with 2 .. 4
     // activation rows (elsewhere the row-streaming kernel is as fast or faster)
     if constexpr (FX || (QT == 8 && M >= 2)) {
-        if (S <= 16) return launch_t<QT, M, FX, 16, 1, ring_depth<QT, M, 1>(), W>(a, rows_per(4, true), s, name);
-        if (S <= 32) return launch_t<QT, M, FX, 16, 2, ring_depth<QT, M, 2>(), W>(a, rows_per(4, true), s, name);
-        if (S <= 48) return launch_t<QT, M, FX, 16, 3, ring_depth<QT, M, 3>(), W>(a, rows_per(4, true), s, name);
-        if constexpr (M <= 2) return launch_t<QT, M, FX, 16, 4, ring_depth<QT, M, 4>(), W>(a, rows_per(4, true), s, name);
+        if (S <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W>(a, rows_per(4, true), s, name);
+        if (S <= 32) return launch_t<QT, M, AX, 16, 2, ring_depth<QT, M, 2>(), W>(a, rows_per(4, true), s, name);
+        if (S <= 48) return launch_t<QT, M, AX, 16, 3, ring_depth<QT, M, 3>(), W>(a, rows_per(4, true), s, name);
+        if constexpr (M <= 2) return launch_t<QT, M, AX, 16, 4, ring_depth<QT, M, 4>(), W>(a, rows_per(4, true), s, name);
     }
     return hipErrorNotSupported;
 }
 
 template <int QT>
 hipError_t launch_q(const RowsArgs &a, hipStream_t s, const char **name) {
-    if (a.x != nullptr) return launch_m<QT, 1, true>(a, s, name);
+    if (a.x != nullptr)
+        return a.xn != nullptr ? launch_m<QT, 1, kActRms>(a, s, name) : launch_m<QT, 1, kActF32>(a, s, name);
     // pre-quantized: the matrix-core form for 4 rows of Q4_0 (measured
     // faster than both dot-product kernels) and for 3 or 4 rows of 64-block
     // slices (beyond the dot-product form's registers)
     const int nb = a.K / QK, S = (nb + QMV_FX_WPB - 1) / QMV_FX_WPB;
     if (nb > 32 && ((QT == 4 && a.M == 4) || (a.M >= 3 && S > 48))) return launch_mq<QT>(a, s, name);
     switch (a.M) {
-        case 1: return launch_m<QT, 1, false>(a, s, name);
-        case 2: return launch_m<QT, 2, false>(a, s, name);
-        case 3: return launch_m<QT, 3, false>(a, s, name);
-        case 4: return launch_m<QT, 4, false>(a, s, name);
+        case 1: return launch_m<QT, 1, kActQ8>(a, s, name);
+        case 2: return launch_m<QT, 2, kActQ8>(a, s, name);
+        case 3: return launch_m<QT, 3, kActQ8>(a, s, name);
+        case 4: return launch_m<QT, 4, kActQ8>(a, s, name);
         default: return hipErrorNotSupported;
     }
 }

@@ -18,6 +18,8 @@ struct RowsArgs {
     const float *x;            // float32 activation (fused quantization), or null
     const int8_t *xq;          // Q8_0 activation quants (when x is null)
     const float *xd;           // Q8_0 activation scales (when x is null)
+    const float *xn;           // rmsnorm weights applied to x before its quantization, or null
+    float eps;                 // rmsnorm epsilon (when xn is given)
     int8_t *xq_out;            // optional copy of the fused quantization
     float *xd_out;
     int32_t r0, r1;

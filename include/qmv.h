@@ -157,6 +157,36 @@ qmv_status qmv_matvec_q4_fx(float *y, const qmv_qtensor *W, const float *x,
                             qmv_qact *xq, int32_t r0, int32_t r1, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * qmv_matvec_q8_fx_rmsnorm / qmv_matvec_q4_fx_rmsnorm -- the fused product
+ * with the root-mean-square normalization that precedes every quantization
+ * of a layer input in the spec's forward pass (section 6: h = rmsnorm(x);
+ * qa = quantize_q8(h); ... = matvec(W, qa)), all in one launch:
+ *   h_j = w_norm_j * (inv * x_j),  inv = 1 / sqrt(ss / K + eps),
+ *   ss  = sum of x_j^2 (section 5 lists ml_k_rmsnorm(o, x, w, n, eps); the
+ *         formula is the llama2.c one the spec follows elsewhere),
+ * then h is quantized to Q8_0 (the qmv_quantize_q8 rule) and multiplied as
+ * in qmv_matvec_q8_fx.  ss is summed pairwise: the 32 squares of each
+ * 32-element block by recursive halving, then the block sums by recursive
+ * halving over their count padded to a power of two with zeros.  Every
+ * float operation is rounded on its own (no contraction; correctly rounded
+ * division and square root), so the quantized h is bit-identical to that
+ * definition evaluated on any IEEE binary32 machine.
+ *   x, w_norm : W->cols floats each, 16-byte aligned, device memory.
+ *   eps       : finite and >= 0 (QMV_E_ARG otherwise); with eps = 0 an
+ *               all-zero x gives a non-finite inv (the caller's choice).
+ *   xq        : NULL, or receives the quantized h (as in qmv_matvec_*_fx).
+ *   K / 32 must be at most 32 or in [64, 512] (QMV_E_SHAPE otherwise: the
+ *   normalization is built into the split-K kernel only).
+ *   Rows, y indexing and errors otherwise as qmv_matvec_q8_fx.
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_matvec_q8_fx_rmsnorm(float *y, const qmv_qtensor *W, const float *x,
+                                    const float *w_norm, float eps, qmv_qact *xq,
+                                    int32_t r0, int32_t r1, void *stream);
+qmv_status qmv_matvec_q4_fx_rmsnorm(float *y, const qmv_qtensor *W, const float *x,
+                                    const float *w_norm, float eps, qmv_qact *xq,
+                                    int32_t r0, int32_t r1, void *stream);
+
+/* ---------------------------------------------------------------------------
  * qmv_gemm_q8 / qmv_gemm_q4 -- the product for M activation rows at once:
  * X is a Q8_0 qmv_qtensor with X->rows = M, X->cols = W->cols, each row
  * quantized on its own; Y is M x W->rows row-major and

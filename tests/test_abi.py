@@ -47,6 +47,7 @@ def test_header_declares_the_product_calls():
     names = declared_functions()
     for n in ("qmv_quantize_q8", "qmv_quantize_weights", "qmv_matvec_q8", "qmv_matvec_q4",
               "qmv_matvec_q8_fx", "qmv_matvec_q4_fx", "qmv_gemm_q8", "qmv_gemm_q4",
+              "qmv_matvec_q8_fx_rmsnorm", "qmv_matvec_q4_fx_rmsnorm",
               "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
         assert n in names
 
@@ -112,6 +113,26 @@ def test_matvec_fx_validation(lib, fn, t):
     assert f(Y, ctypes.byref(W), A + 0x1000, None, 3, 2, None) == E_SHAPE
 
 
+@pytest.mark.parametrize("fn,t", [("qmv_matvec_q8_fx_rmsnorm", Q8), ("qmv_matvec_q4_fx_rmsnorm", Q4)])
+def test_matvec_fx_rmsnorm_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, P, P, ctypes.c_float, P, ctypes.c_int32, ctypes.c_int32, P]
+    W = _w(t=t)
+    X, N = A + 0x1000, A + 0x2000
+    assert f(Y, ctypes.byref(W), None, N, 1e-5, None, 0, 8, None) == E_ARG                 # null x
+    assert f(Y, ctypes.byref(W), X, None, 1e-5, None, 0, 8, None) == E_ARG                 # null w_norm
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert f(Y, ctypes.byref(W), X, N, eps, None, 0, 8, None) == E_ARG, eps
+    assert f(Y, ctypes.byref(W), X, N + 4, 1e-5, None, 0, 8, None) == E_ARG               # w_norm misaligned
+    assert f(Y, ctypes.byref(W), X + 8, N, 1e-5, None, 0, 8, None) == E_ARG               # x misaligned
+    assert f(Y, ctypes.byref(W), X, N, 1e-5, ctypes.byref(QA(0, B, 0)), 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(_w(t=Q4 if t == Q8 else Q8)), X, N, 1e-5, None, 0, 8, None) == E_FORMAT
+    for cols in (32 * 33, 32 * 63, 32 * 513):                                              # outside the kernel's K
+        assert f(Y, ctypes.byref(_w(t=t, cols=cols)), X, N, 1e-5, None, 0, 8, None) == E_SHAPE, cols
+    assert f(Y, ctypes.byref(W), X, N, 1e-5, None, 3, 2, None) == E_SHAPE
+
+
 @pytest.mark.parametrize("fn,t", [("qmv_gemm_q8", Q8), ("qmv_gemm_q4", Q4)])
 def test_gemm_validation(lib, fn, t):
     f = getattr(lib, fn)
@@ -154,6 +175,10 @@ def test_no_device_is_an_error_not_a_crash(lib):
     W, X = _w(t=Q8), _x()
     assert lib.qmv_matvec_q8(Y, ctypes.byref(W), ctypes.byref(X), 0, 8, None) == st
     assert lib.qmv_matvec_q4_fx(Y, ctypes.byref(_w(t=Q4)), A + 0x1000, None, 0, 8, None) == st
+    f = lib.qmv_matvec_q8_fx_rmsnorm
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, P, P, ctypes.c_float, P, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(Y, ctypes.byref(W), A + 0x1000, A + 0x2000, 1e-5, None, 0, 8, None) == st
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(64), None) == st
     assert lib.qmv_last_kernel().decode() == ""
