@@ -55,6 +55,7 @@ class _Lib:
             "orc_gemm_q4": [P, P, P, i32, i32, P, P, i32, i32, i32],
             "orc_tol_abs": [ctypes.c_int, P, P, i32, P, P, i32, i32, P],
             "orc_rmsnorm": [P, P, P, i64, ctypes.c_float],
+            "orc_silu_mul": [P, P, P, i64],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -240,4 +241,14 @@ def rmsnorm(x, w, eps):
     assert x.size == w.size and x.size % QK == 0 and x.size > 0
     o = np.empty_like(x)
     lib().orc_rmsnorm(_p(o), _p(x), _p(w), x.size, float(eps))
+    return o
+
+
+def silu_mul(g, u):
+    """o_j = (g_j * (1 / (1 + expf(-g_j)))) * u_j in binary32."""
+    g = _f32(g).reshape(-1)
+    u = _f32(u).reshape(-1)
+    assert g.size == u.size
+    o = np.empty_like(g)
+    lib().orc_silu_mul(_p(o), _p(g), _p(u), g.size)
     return o

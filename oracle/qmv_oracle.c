@@ -31,6 +31,8 @@
  *                       right sum would not give, exact integer sums)
  *   orc_rmsnorm         pinned (closed forms at constant input, sign and
  *                       power-of-two invariants, fp64 brute force)
+ *   orc_silu_mul        pinned (closed forms at 0 and at saturation, the
+ *                       identity silu(g) - silu(-g) = g, fp64 brute force)
  */
 #include <math.h>
 #include <stdint.h>
@@ -322,4 +324,23 @@ void orc_rmsnorm(float *o, const float *x, const float *w, int64_t n, float eps)
     float inv = 1.0f / sqrtf(mean + eps);
     for (int64_t j = 0; j < n; ++j)
         o[j] = w[j] * (inv * x[j]);
+}
+
+/* ------------------------------------------------------------------------
+ * The FFN gate (spec section 5 kernel list, ml_k_silu_mul(g, u, n):
+ * g = silu(g) * u; section 6 forward pass: silu_mul(g, u), then
+ * quantize_q8(g) ahead of W2).  silu(v) = v * sigmoid(v), evaluated as the
+ * llama2.c reference the spec follows: v * (1 / (1 + expf(-v))), then * u,
+ * each float operation rounded on its own.  expf is the C library's (the
+ * spec's scalar path; its SIMD paths use an exp with relative error at
+ * most 1e-6, so results of this step are defined to that accuracy).
+ * ---------------------------------------------------------------------- */
+void orc_silu_mul(float *o, const float *g, const float *u, int64_t n)
+{
+    for (int64_t j = 0; j < n; ++j) {
+        float v = g[j];
+        float s = 1.0f / (1.0f + expf(-v));
+        v = v * s;
+        o[j] = v * u[j];
+    }
 }

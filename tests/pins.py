@@ -417,6 +417,31 @@ def check_rmsnorm_invariants_and_brute():
             assert np.array_equal(orc.rmsnorm(x * np.float32(2.0 ** k), w, 0.0), o0), (n, k)
 
 
+def check_silu_mul():
+    """silu(0) = 0; far from 0 the sigmoid saturates exactly in binary32
+    (1 + expf(-v) rounds to 1 for v >= 17, so o = v * u; expf(-v) overflows
+    to +inf for v <= -89, so o = +-0); silu(g) - silu(-g) = g; and fp64
+    brute force within a few binary32 roundings (the C library's expf is
+    within 1 ulp)."""
+    u = np.array([1.0, -2.5, 3.0, 0.125], np.float32)
+    assert np.all(orc.silu_mul(np.zeros(4, np.float32), u) == 0.0)
+    for v in (17.0, 40.0, 100.0):
+        g = np.full(4, v, np.float32)
+        assert np.array_equal(orc.silu_mul(g, u), g * u), v
+    for v in (-89.0, -100.0, -1e30):
+        assert np.all(orc.silu_mul(np.full(4, v, np.float32), u) == 0.0), v
+    rng = np.random.default_rng(23)
+    g = (rng.standard_normal(4096) * 4.0).astype(np.float32)
+    u = rng.standard_normal(4096).astype(np.float32)
+    ones = np.ones_like(g)
+    d = orc.silu_mul(g, ones).astype(np.float64) - orc.silu_mul(-g, ones).astype(np.float64)
+    assert np.all(np.abs(d - g) <= 4 * np.finfo(np.float32).eps * np.abs(g))
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    o64 = g64 / (1.0 + np.exp(-g64)) * u64
+    o = orc.silu_mul(g, u).astype(np.float64)
+    assert np.all(np.abs(o - o64) <= 6 * np.finfo(np.float32).eps * np.abs(o64) + 1e-37)
+
+
 ALL_CHECKS = [
     check_q8_zero_block, check_q8_equal_block, check_q8_clamp_and_range,
     check_q8_unit_scale_textbook, check_q8_ties, check_q8_detectors,
@@ -426,6 +451,7 @@ ALL_CHECKS = [
     check_matvec_brute64, check_matvec_unit_scales, check_matvec_invariants,
     check_gemm_rows,
     check_sumsq_pairwise_order, check_rmsnorm_closed_forms, check_rmsnorm_invariants_and_brute,
+    check_silu_mul,
 ]
 
 

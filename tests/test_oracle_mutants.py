@@ -49,6 +49,9 @@ MUTANTS = [
     ("rms_n_minus_1", "float mean = ss / (float)n;", "float mean = ss / (float)(n - 1);", 1),
     ("rms_no_weight", "o[j] = w[j] * (inv * x[j]);", "o[j] = inv * x[j];", 1),
     ("rms_abs_not_square", "sq[i] = x[b * QK + i] * x[b * QK + i];", "sq[i] = fabsf(x[b * QK + i]);", 1),
+    ("silu_sign", "float s = 1.0f / (1.0f + expf(-v));", "float s = 1.0f / (1.0f + expf(v));", 1),
+    ("silu_no_gate", "o[j] = v * u[j];", "o[j] = v;", 1),
+    ("silu_sigmoid_only", "v = v * s;\n        o[j] = v * u[j];", "v = s;\n        o[j] = v * u[j];", 1),
     ("rms_weight_shift", "o[j] = w[j] * (inv * x[j]);", "o[j] = w[(j + 1) % n] * (inv * x[j]);", 1),
 ]
 
