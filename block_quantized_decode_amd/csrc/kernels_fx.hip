@@ -1,7 +1,8 @@
 // kernels_fx.hip -- the split-K streaming product for a few activation rows:
 // the decode matvec with the activation quantized inside the kernel (M = 1,
-// float32 x) and the same product on pre-quantized Q8_0 activation rows
-// (M = 1 .. 4), for K / 32 <= 32 and K of 2048 .. 16384.
+// float32 x; optionally normalized first, rmsnorm, or formed from the FFN
+// gate silu(g) * u) and the same product on pre-quantized Q8_0 activation
+// rows (M = 1 .. 4), for K / 32 <= 32 and K of 2048 .. 16384.
 //
 // What is computed (Legacy-ISA ML Inference Runtime -- Design Spec,
 // section 4 "Q8 quantization" and "Integer dot per block", section 5
@@ -108,8 +109,9 @@ __device__ __forceinline__ float group_sum(float a) {
 constexpr int rw_cap(int M) { return M <= 3 ? 1024 : 512; }
 
 // Activation forms of k_fx: Q8_0 rows as given, a float32 row quantized in
-// the kernel, or a float32 row normalized (rmsnorm) and then quantized.
-enum { kActQ8 = 0, kActF32 = 1, kActRms = 2 };
+// the kernel, a float32 row normalized (rmsnorm) and then quantized, or the
+// FFN gate silu(g) * u of two float32 rows, then quantized.
+enum { kActQ8 = 0, kActF32 = 1, kActRms = 2, kActSilu = 3 };
 
 // The rmsnorm scale 1 / sqrt(ss / n + eps), each operation rounded on its
 // own (contraction off; the division and the square root are the correctly
@@ -125,6 +127,16 @@ __device__ __forceinline__ float rms_apply(float x, float w, float inv) {
 #pragma clang fp contract(off)
     const float t = inv * x;
     return w * t;
+}
+
+// silu(g) * u as g * (1 / (1 + exp(-g))) * u, each operation rounded on its
+// own (the division is the correctly rounded one; expf is the device
+// library's, within a few ulp -- the spec allows 1e-6 relative).
+__device__ __forceinline__ float silu_mul1(float g, float u) {
+#pragma clang fp contract(off)
+    const float s = 1.0f / (1.0f + expf(-g));
+    const float v = g * s;
+    return v * u;
 }
 
 // Pairwise (recursive-halving) sum of the squares of 8 consecutive values.
@@ -176,20 +188,20 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     //    in the fused form, the quants and the block scale otherwise)
     constexpr int NR = T * NBL / 16;           // rounds of 16 blocks
     constexpr int MX = FX ? 1 : M;
-    constexpr int NRN = AX == kActRms ? NR : 1;
+    constexpr int NRN = (AX == kActRms || AX == kActSilu) ? NR : 1;
     float4 xa[FX ? NR : 1], xb[FX ? NR : 1], na[NRN], nb8[NRN];
     int xv0[MX][FX ? 1 : NR], xv1[MX][FX ? 1 : NR];
     float xdv[MX][FX ? 1 : NR];
     if constexpr (FX) {
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * 4);
-        const __amdgpu_buffer_rsrc_t rn = make_rsrc(xn, AX == kActRms ? K * 4 : 0);
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(xn, (AX == kActRms || AX == kActSilu) ? K * 4 : 0);
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
             const int b = 16 * k + (lane >> 2);
             const int o = b < ns ? (kb0 + b) * 128 + 32 * (lane & 3) : kOOB;
             xa[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
             xb[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16, 0, 0));
-            if constexpr (AX == kActRms) {  // the norm weights of the same elements
+            if constexpr (AX == kActRms || AX == kActSilu) {  // norm weights, or u, of the same elements
                 na[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rn, o, 0, 0));
                 nb8[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rn, o + 16, 0, 0));
             }
@@ -289,6 +301,17 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                                 rms_apply(xa[k].z, na[k].z, inv), rms_apply(xa[k].w, na[k].w, inv));
             xb[k] = make_float4(rms_apply(xb[k].x, nb8[k].x, inv), rms_apply(xb[k].y, nb8[k].y, inv),
                                 rms_apply(xb[k].z, nb8[k].z, inv), rms_apply(xb[k].w, nb8[k].w, inv));
+        }
+    }
+
+    // 3b. FFN gate: x <- silu(g) * u elementwise
+    if constexpr (AX == kActSilu) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            xa[k] = make_float4(silu_mul1(xa[k].x, na[k].x), silu_mul1(xa[k].y, na[k].y),
+                                silu_mul1(xa[k].z, na[k].z), silu_mul1(xa[k].w, na[k].w));
+            xb[k] = make_float4(silu_mul1(xb[k].x, nb8[k].x), silu_mul1(xb[k].y, nb8[k].y),
+                                silu_mul1(xb[k].z, nb8[k].z), silu_mul1(xb[k].w, nb8[k].w));
         }
     }
 
@@ -648,11 +671,11 @@ hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name)
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq, a.xd,
-                       a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1, rw);
+                       AX == kActSilu ? a.xu : a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1, rw);
     if (kname[0] == 0) {
         if (FX)
-            snprintf(kname, sizeof kname, "fx%s_q%d_t%d_n%d_d%d_w%d%s", AX == kActRms ? "n" : "", QT, T, NBL, D,
-                     WPB, KS ? "" : "_rows");
+            snprintf(kname, sizeof kname, "fx%s_q%d_t%d_n%d_d%d_w%d%s",
+                     AX == kActRms ? "n" : (AX == kActSilu ? "s" : ""), QT, T, NBL, D, WPB, KS ? "" : "_rows");
         else
             snprintf(kname, sizeof kname, "px_q%d_m%d_t%d_n%d_d%d_w%d%s", QT, M, T, NBL, D, WPB, KS ? "" : "_rows");
     }
@@ -697,8 +720,10 @@ hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
 
 template <int QT>
 hipError_t launch_q(const RowsArgs &a, hipStream_t s, const char **name) {
-    if (a.x != nullptr)
+    if (a.x != nullptr) {
+        if (a.xu != nullptr) return launch_m<QT, 1, kActSilu>(a, s, name);
         return a.xn != nullptr ? launch_m<QT, 1, kActRms>(a, s, name) : launch_m<QT, 1, kActF32>(a, s, name);
+    }
     // pre-quantized: the matrix-core form for 4 rows of Q4_0 (measured
     // faster than both dot-product kernels) and for 3 or 4 rows of 64-block
     // slices (beyond the dot-product form's registers)

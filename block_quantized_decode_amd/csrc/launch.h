@@ -20,6 +20,7 @@ struct RowsArgs {
     const float *xd;           // Q8_0 activation scales (when x is null)
     const float *xn;           // rmsnorm weights applied to x before its quantization, or null
     float eps;                 // rmsnorm epsilon (when xn is given)
+    const float *xu;           // FFN gate: the activation is silu(x) * xu, or null
     int8_t *xq_out;            // optional copy of the fused quantization
     float *xd_out;
     int32_t r0, r1;

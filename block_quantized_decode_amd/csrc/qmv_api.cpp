@@ -93,7 +93,7 @@ qmv_status check_weight_align(const qmv_qtensor *W) {
 
 qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, const float *x,
                        const int8_t *xq, const float *xd, qmv_qact *xq_out, int32_t r0, int32_t r1,
-                       void *stream, const float *xn = nullptr, float eps = 0.0f) {
+                       void *stream, const float *xn = nullptr, float eps = 0.0f, const float *xu = nullptr) {
     if (y == nullptr) return QMV_E_ARG;
     qmv_status st = check_weight(W, qtype);
     if (st != QMV_OK) return st;
@@ -122,6 +122,7 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     a.xd = xd;
     a.xn = xn;
     a.eps = eps;
+    a.xu = xu;
     a.xq_out = xq_out ? xq_out->q : nullptr;
     a.xd_out = xq_out ? xq_out->d : nullptr;
     a.r0 = r0;
@@ -129,7 +130,8 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     a.num_cu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
     const char *name = "";
     hipError_t e = qmv::launch_fx(a, static_cast<hipStream_t>(stream), &name);
-    if (e == hipErrorNotSupported && xn == nullptr) e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
+    if (e == hipErrorNotSupported && xn == nullptr && xu == nullptr)
+        e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
     return finish(e, name, (r1 - r0 + 15) / 16);
 }
 
@@ -160,6 +162,18 @@ qmv_status matvec_fx_rmsnorm(int qtype, float *y, const qmv_qtensor *W, const fl
     if ((nb > 32 && nb < 64) || nb > 512) return QMV_E_SHAPE;  // the split-K kernel's range
     if (!aligned(w_norm, 16)) return QMV_E_ARG;
     return rows_common(qtype, y, W, 1, x, nullptr, nullptr, xq, r0, r1, stream, w_norm, eps);
+}
+
+qmv_status matvec_fx_silu_mul(int qtype, float *y, const qmv_qtensor *W, const float *g, const float *u,
+                              qmv_qact *xq, int32_t r0, int32_t r1, void *stream) {
+    if (g == nullptr || u == nullptr) return QMV_E_ARG;
+    if (xq != nullptr && (xq->q == nullptr || xq->d == nullptr)) return QMV_E_ARG;
+    qmv_status st = check_weight(W, qtype);
+    if (st != QMV_OK) return st;
+    const int32_t nb = W->cols / QMV_QK;
+    if ((nb > 32 && nb < 64) || nb > 512) return QMV_E_SHAPE;  // the split-K kernel's range
+    if (!aligned(u, 16)) return QMV_E_ARG;
+    return rows_common(qtype, y, W, 1, g, nullptr, nullptr, xq, r0, r1, stream, nullptr, 0.0f, u);
 }
 
 qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
@@ -269,6 +283,16 @@ qmv_status qmv_matvec_q8_fx_rmsnorm(float *y, const qmv_qtensor *W, const float 
 qmv_status qmv_matvec_q4_fx_rmsnorm(float *y, const qmv_qtensor *W, const float *x, const float *w_norm,
                                     float eps, qmv_qact *xq, int32_t r0, int32_t r1, void *stream) {
     return matvec_fx_rmsnorm(QMV_Q4_0, y, W, x, w_norm, eps, xq, r0, r1, stream);
+}
+
+qmv_status qmv_matvec_q8_fx_silu_mul(float *y, const qmv_qtensor *W, const float *g, const float *u,
+                                     qmv_qact *xq, int32_t r0, int32_t r1, void *stream) {
+    return matvec_fx_silu_mul(QMV_Q8_0, y, W, g, u, xq, r0, r1, stream);
+}
+
+qmv_status qmv_matvec_q4_fx_silu_mul(float *y, const qmv_qtensor *W, const float *g, const float *u,
+                                     qmv_qact *xq, int32_t r0, int32_t r1, void *stream) {
+    return matvec_fx_silu_mul(QMV_Q4_0, y, W, g, u, xq, r0, r1, stream);
 }
 
 qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,

@@ -58,6 +58,10 @@ _SIGS = {
                                  ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_matvec_q4_fx_rmsnorm": [_P, ctypes.POINTER(QTensor), _P, _P, ctypes.c_float, ctypes.POINTER(QAct),
                                  ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_matvec_q8_fx_silu_mul": [_P, ctypes.POINTER(QTensor), _P, _P, ctypes.POINTER(QAct), ctypes.c_int32,
+                                  ctypes.c_int32, _P],
+    "qmv_matvec_q4_fx_silu_mul": [_P, ctypes.POINTER(QTensor), _P, _P, ctypes.POINTER(QAct), ctypes.c_int32,
+                                  ctypes.c_int32, _P],
     "qmv_gemm_q8": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_gemm_q4": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_device_check": [],
@@ -239,6 +243,34 @@ def qmv_matvec_q4_fx_rmsnorm(wq, wd, x, w_norm, eps, r0=None, r1=None, y=None, x
     return _matvec_fx_rmsnorm(QMV_Q4_0, "qmv_matvec_q4_fx_rmsnorm", wq, wd, x, w_norm, eps, r0, r1, y, xq_out)
 
 
+def _matvec_fx_silu_mul(qtype, fname, wq, wd, g, u, r0, r1, y, xq_out):
+    W = qtensor(wq, wd, qtype)
+    _dev(g, torch.float32)
+    _dev(u, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    y = _out(y, W.rows, wd)
+    act = None
+    if xq_out is not None:
+        q, d = xq_out
+        _dev(q, torch.int8)
+        _dev(d, torch.float32)
+        act = QAct(q.data_ptr(), d.data_ptr(), 0)
+    code = getattr(lib(), fname)(y.data_ptr(), ctypes.byref(W), g.data_ptr(), u.data_ptr(),
+                                 ctypes.byref(act) if act is not None else None, r0, r1, _stream())
+    _check(code, fname)
+    return y
+
+
+def qmv_matvec_q8_fx_silu_mul(wq, wd, g, u, r0=None, r1=None, y=None, xq_out=None):
+    """y = W q8(silu(g) * u) in one launch (see include/qmv.h)."""
+    return _matvec_fx_silu_mul(QMV_Q8_0, "qmv_matvec_q8_fx_silu_mul", wq, wd, g, u, r0, r1, y, xq_out)
+
+
+def qmv_matvec_q4_fx_silu_mul(wq, wd, g, u, r0=None, r1=None, y=None, xq_out=None):
+    return _matvec_fx_silu_mul(QMV_Q4_0, "qmv_matvec_q4_fx_silu_mul", wq, wd, g, u, r0, r1, y, xq_out)
+
+
 def _gemm(qtype, fname, wq, wd, xq, xd, r0, r1, Y):
     W = qtensor(wq, wd, qtype)
     X = qtensor(xq, xd, QMV_Q8_0)
@@ -314,6 +346,24 @@ def prepare_matvec_fx_rmsnorm(qtype, wq, wd, x, w_norm, eps, y, r0=None, r1=None
     args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), w_norm.data_ptr(), ctypes.c_float(eps),
             ctypes.byref(act) if act is not None else None, r0, r1]
     return Prepared(fname, args, [W, act, wq, wd, x, w_norm, y, xq_out], stream)
+
+
+def prepare_matvec_fx_silu_mul(qtype, wq, wd, g, u, y, r0=None, r1=None, xq_out=None, stream=None) -> Prepared:
+    """Prepared qmv_matvec_q4_fx_silu_mul / qmv_matvec_q8_fx_silu_mul."""
+    W = qtensor(wq, wd, qtype)
+    _dev(g, torch.float32)
+    _dev(u, torch.float32)
+    _dev(y, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    act = None
+    if xq_out is not None:
+        q, d = xq_out
+        act = QAct(_dev(q, torch.int8).data_ptr(), _dev(d, torch.float32).data_ptr(), 0)
+    fname = "qmv_matvec_q4_fx_silu_mul" if qtype == QMV_Q4_0 else "qmv_matvec_q8_fx_silu_mul"
+    args = [y.data_ptr(), ctypes.byref(W), g.data_ptr(), u.data_ptr(),
+            ctypes.byref(act) if act is not None else None, r0, r1]
+    return Prepared(fname, args, [W, act, wq, wd, g, u, y, xq_out], stream)
 
 
 def prepare_gemm(qtype, wq, wd, xq, xd, Y, r0=None, r1=None, stream=None) -> Prepared:

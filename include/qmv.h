@@ -187,6 +187,31 @@ qmv_status qmv_matvec_q4_fx_rmsnorm(float *y, const qmv_qtensor *W, const float 
                                     int32_t r0, int32_t r1, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * qmv_matvec_q8_fx_silu_mul / qmv_matvec_q4_fx_silu_mul -- the fused product
+ * whose activation is the FFN gate of the spec's forward pass (section 6:
+ * silu_mul(g, u); x += matvec(W2, quantize_q8(g)); section 5 lists
+ * ml_k_silu_mul(g, u, n): g = silu(g) * u), all in one launch:
+ *   a_j = (g_j * (1 / (1 + exp(-g_j)))) * u_j,
+ * each operation rounded on its own, then a is quantized to Q8_0 (the
+ * qmv_quantize_q8 rule) and multiplied as in qmv_matvec_q8_fx.  exp is the
+ * device math library's single-precision exp (a few ulp); the spec allows
+ * its SIMD exp a relative error of 1e-6, so codes may differ by one from a
+ * host evaluation where a * 127 / amax falls that close to a rounding
+ * boundary.
+ *   g, u : W->cols floats each, 16-byte aligned, device memory (they may be
+ *          the two halves of one concatenated W1|W3 output).
+ *   xq   : NULL, or receives the quantized a.
+ *   K / 32 must be at most 32 or in [64, 512] (QMV_E_SHAPE otherwise).
+ *   Rows, y indexing and errors otherwise as qmv_matvec_q8_fx.
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_matvec_q8_fx_silu_mul(float *y, const qmv_qtensor *W, const float *g,
+                                     const float *u, qmv_qact *xq, int32_t r0, int32_t r1,
+                                     void *stream);
+qmv_status qmv_matvec_q4_fx_silu_mul(float *y, const qmv_qtensor *W, const float *g,
+                                     const float *u, qmv_qact *xq, int32_t r0, int32_t r1,
+                                     void *stream);
+
+/* ---------------------------------------------------------------------------
  * qmv_gemm_q8 / qmv_gemm_q4 -- the product for M activation rows at once:
  * X is a Q8_0 qmv_qtensor with X->rows = M, X->cols = W->cols, each row
  * quantized on its own; Y is M x W->rows row-major and

@@ -48,6 +48,7 @@ def test_header_declares_the_product_calls():
     for n in ("qmv_quantize_q8", "qmv_quantize_weights", "qmv_matvec_q8", "qmv_matvec_q4",
               "qmv_matvec_q8_fx", "qmv_matvec_q4_fx", "qmv_gemm_q8", "qmv_gemm_q4",
               "qmv_matvec_q8_fx_rmsnorm", "qmv_matvec_q4_fx_rmsnorm",
+              "qmv_matvec_q8_fx_silu_mul", "qmv_matvec_q4_fx_silu_mul",
               "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
         assert n in names
 
@@ -133,6 +134,24 @@ def test_matvec_fx_rmsnorm_validation(lib, fn, t):
     assert f(Y, ctypes.byref(W), X, N, 1e-5, None, 3, 2, None) == E_SHAPE
 
 
+@pytest.mark.parametrize("fn,t", [("qmv_matvec_q8_fx_silu_mul", Q8), ("qmv_matvec_q4_fx_silu_mul", Q4)])
+def test_matvec_fx_silu_mul_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    W = _w(t=t)
+    G, U = A + 0x1000, A + 0x2000
+    assert f(Y, ctypes.byref(W), None, U, None, 0, 8, None) == E_ARG                      # null g
+    assert f(Y, ctypes.byref(W), G, None, None, 0, 8, None) == E_ARG                      # null u
+    assert f(Y, ctypes.byref(W), G + 4, U, None, 0, 8, None) == E_ARG                     # g misaligned
+    assert f(Y, ctypes.byref(W), G, U + 8, None, 0, 8, None) == E_ARG                     # u misaligned
+    assert f(Y, ctypes.byref(W), G, U, ctypes.byref(QA(A, 0, 0)), 0, 8, None) == E_ARG    # xq with null d
+    assert f(Y, ctypes.byref(_w(t=Q4 if t == Q8 else Q8)), G, U, None, 0, 8, None) == E_FORMAT
+    for cols in (32 * 33, 32 * 63, 32 * 513):
+        assert f(Y, ctypes.byref(_w(t=t, cols=cols)), G, U, None, 0, 8, None) == E_SHAPE, cols
+    assert f(Y, ctypes.byref(W), G, U, None, 0, 9, None) == E_SHAPE
+
+
 @pytest.mark.parametrize("fn,t", [("qmv_gemm_q8", Q8), ("qmv_gemm_q4", Q4)])
 def test_gemm_validation(lib, fn, t):
     f = getattr(lib, fn)
@@ -179,6 +198,9 @@ def test_no_device_is_an_error_not_a_crash(lib):
     P = ctypes.c_void_p
     f.argtypes = [P, P, P, P, ctypes.c_float, P, ctypes.c_int32, ctypes.c_int32, P]
     assert f(Y, ctypes.byref(W), A + 0x1000, A + 0x2000, 1e-5, None, 0, 8, None) == st
+    f = lib.qmv_matvec_q8_fx_silu_mul
+    f.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(Y, ctypes.byref(W), A + 0x1000, A + 0x2000, None, 0, 8, None) == st
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(64), None) == st
     assert lib.qmv_last_kernel().decode() == ""
