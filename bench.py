@@ -21,7 +21,9 @@ second half of the metric, the M >= 16 product on the int8 matrix cores
 Q4_0 and Q8_0, M = 16 and 64), is measured the same way and reported under
 "batched".  The other configurations (256 x 512 Q8_0, a TinyLlama-1.1B
 layer with and without concatenated projections, the Qwen2.5-0.5B FFN and
-lm_head) are timed per call and per layer under "other_workloads".  "env" holds the per-launch floor of the smallest libqmv kernel
+lm_head) are timed per call and per layer under "other_workloads", and the
+decode-step neighbours fused into the product's launch (rmsnorm ahead of
+the quantization, the FFN gate silu(g) * u) under "fusion".  "env" holds the per-launch floor of the smallest libqmv kernel
 replayed the same way and the shader clock rocm-smi reports; the CPU
 baseline also gives the oracle's single-thread rate, the host CPU model
 and the oracle's compiler flags.
@@ -229,8 +231,10 @@ def main():
 
     # ---- the other configurations: per call and per layer, cold
     others = None
+    fusion = None
     if not args.no_others:
         others = other_workloads_bench(stream)
+        fusion = fusion_bench(stream)
 
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
@@ -284,6 +288,7 @@ def main():
         "cpu_baseline": cpu,
         "small_batch": small,
         "other_workloads": others,
+        "fusion": fusion,
         "batched": batched,
     }
     print(json.dumps(line), flush=True)
@@ -463,6 +468,88 @@ def other_workloads_bench(stream):
     torch.cuda.empty_cache()
     out[wl.name] = {"per_matrix_us": per, "per_matrix_weight_gb_s": gbs, "ffn_us": round(ffn_us, 3),
                     "lm_head_pct_hbm_peak": round(100.0 * gbs["lm_head"] / HBM_PEAK_GBS, 2), "copies": copies}
+    return out
+
+
+def fusion_bench(stream):
+    """The decode-step neighbours fused into the product's launch: rmsnorm
+    ahead of the quantization, and the FFN gate silu(g) * u.  Timed like
+    the step (graphs of prepared calls, weights rotated over copies beyond
+    the 256 MB cache):
+      * a TinyLlama-1.1B layer's matrix path in 4 launches -- rmsnorm + Q|K|V
+        (2560 x 2048), W_o, rmsnorm + gate|up (11264 x 2048), silu_mul + down
+        (g, u = the two halves of the gate|up output) -- against the same 4
+        launches with no rmsnorm or gate (the layer_concat figure of
+        other_workloads);
+      * one Llama-7B FFN launch of each form against the plain fused one:
+        W_up 11008 x 4096 with rmsnorm, W_down 4096 x 11008 with the gate."""
+    import torch
+
+    from block_quantized_decode_amd import qmv
+
+    dev = torch.device("cuda:0")
+    torch.manual_seed(6)
+
+    def quantized(rows, cols, qtype=4):
+        w = torch.randn(rows, cols, device=dev) * 0.02
+        q, d = qmv.qmv_quantize_weights(w, qtype)
+        del w
+        return q, d
+
+    out = {}
+    sid = stream.cuda_stream
+    # TinyLlama layer
+    copies = 20
+    x_attn = torch.randn(2048, device=dev)
+    x_o = torch.randn(2048, device=dev)
+    x_ffn = torch.randn(2048, device=dev)
+    n_attn = 1.0 + 0.1 * torch.randn(2048, device=dev)
+    n_ffn = 1.0 + 0.1 * torch.randn(2048, device=dev)
+    fused, plain = [], []
+    keep = []
+    for _ in range(copies):
+        qkv, wo, gu, dn = quantized(2560, 2048), quantized(2048, 2048), quantized(11264, 2048), quantized(2048, 5632)
+        y_qkv = torch.zeros(2560, device=dev)
+        y_o = torch.zeros(2048, device=dev)
+        y_gu = torch.randn(11264, device=dev)
+        y_dn = torch.zeros(2048, device=dev)
+        fused += [qmv.prepare_matvec_fx_rmsnorm(4, *qkv, x_attn, n_attn, 1e-5, y_qkv, stream=sid),
+                  qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
+                  qmv.prepare_matvec_fx_rmsnorm(4, *gu, x_ffn, n_ffn, 1e-5, y_gu, stream=sid),
+                  qmv.prepare_matvec_fx_silu_mul(4, *dn, y_gu[:5632], y_gu[5632:], y_dn, stream=sid)]
+        plain += [qmv.prepare_matvec_fx(4, *qkv, x_attn, y_qkv, stream=sid),
+                  qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
+                  qmv.prepare_matvec_fx(4, *gu, x_ffn, y_gu, stream=sid),
+                  qmv.prepare_matvec_fx(4, *dn, y_gu[:5632], y_dn, stream=sid)]
+        keep.append((qkv, wo, gu, dn, y_qkv, y_o, y_gu, y_dn))
+    fused_us = _graph_us(fused, stream) / copies
+    plain_us = _graph_us(plain, stream) / copies
+    out["tinyllama_layer_q4"] = {"fused_us": round(fused_us, 3), "plain_us": round(plain_us, 3), "launches": 4,
+                                 "fused_steps": "rmsnorm+QKV, W_o, rmsnorm+gate|up, silu_mul+down", "copies": copies}
+    del keep, fused, plain
+    torch.cuda.empty_cache()
+    # Llama-7B FFN launches
+    copies = 8
+    res = {}
+    for name, rows, cols, form in (("W_up+rmsnorm", 11008, 4096, "rms"), ("W_down+silu_mul", 4096, 11008, "silu")):
+        x = torch.randn(cols, device=dev)
+        x2 = torch.randn(cols, device=dev)
+        f_calls, p_calls, keep = [], [], []
+        for _ in range(copies):
+            q, d = quantized(rows, cols)
+            y = torch.zeros(rows, device=dev)
+            if form == "rms":
+                f_calls.append(qmv.prepare_matvec_fx_rmsnorm(4, q, d, x, x2, 1e-5, y, stream=sid))
+            else:
+                f_calls.append(qmv.prepare_matvec_fx_silu_mul(4, q, d, x, x2, y, stream=sid))
+            p_calls.append(qmv.prepare_matvec_fx(4, q, d, x, y, stream=sid))
+            keep.append((q, d, y))
+        res[name] = {"fused_us": round(_graph_us(f_calls, stream) / copies, 3),
+                     "plain_us": round(_graph_us(p_calls, stream) / copies, 3)}
+        del keep, f_calls, p_calls
+        torch.cuda.empty_cache()
+    out["llama7b_ffn_q4"] = res
+    out["launch_floor_us"] = launch_floor(stream)
     return out
 
 

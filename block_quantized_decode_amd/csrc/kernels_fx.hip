@@ -72,6 +72,16 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #ifndef QMV_FX_WG_PER_CU
 #define QMV_FX_WG_PER_CU 1
 #endif
+// Weight passes issued before the activation transform of the rmsnorm form
+// (its workgroup barrier and norm weights lengthen the prologue: 3 passes,
+// capped at D - 1, measured 7.6 against 8.1 us for one on Llama-7B W_up)
+// and of the FFN-gate form (1 pass measured best on W_down).
+#ifndef QMV_FX_D0_RMS
+#define QMV_FX_D0_RMS 3
+#endif
+#ifndef QMV_FX_D0_SILU
+#define QMV_FX_D0_SILU 1
+#endif
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
@@ -129,12 +139,27 @@ __device__ __forceinline__ float rms_apply(float x, float w, float inv) {
     return w * t;
 }
 
-// silu(g) * u as g * (1 / (1 + exp(-g))) * u, each operation rounded on its
-// own (the division is the correctly rounded one; expf is the device
-// library's, within a few ulp -- the spec allows 1e-6 relative).
+// exp(-g) to a few ulp (the spec bounds silu's exp at 1e-6 relative) in six
+// instructions: 2^t with t = -g log2(e).  The product is rounded (t_hi) and
+// its rounding error recovered exactly by an FMA, the low part of log2(e)
+// added to that residual r, and 2^t = 2^t_hi (v_exp_f32, 1 ulp) * (1 + r ln 2)
+// with |r| < 2^-17, so the neglected (r ln 2)^2 / 2 stays below 1e-11.
+// t >= 128 overflows to +inf as exp does.
+__device__ __forceinline__ float exp_neg(float g) {
+    const float x = -g;
+    const float t = x * 1.44269502f;                     // log2(e), rounded
+    float r = __builtin_fmaf(x, 1.44269502f, -t);        // x log2e_hi - t, exact
+    r = __builtin_fmaf(x, 1.92596303e-8f, r);            // + x (log2(e) - log2e_hi)
+    const float e = __builtin_amdgcn_exp2f(t);
+    return t < 128.0f ? __builtin_fmaf(e, r * 0.693147182f, e) : e;
+}
+
+// silu(g) * u as g * (1 / (1 + exp(-g))) * u: the exp above and the
+// hardware reciprocal (1 ulp), well within the spec's 1e-6; each other
+// operation rounded on its own.
 __device__ __forceinline__ float silu_mul1(float g, float u) {
 #pragma clang fp contract(off)
-    const float s = 1.0f / (1.0f + expf(-g));
+    const float s = __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
     const float v = g * s;
     return v * u;
 }
@@ -291,9 +316,16 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
         if (E == 1) ss = v[0];
         else if (E == 2) ss = v[0] + v[1];
         else if (E == 4) ss = (v[0] + v[1]) + (v[2] + v[3]);
-        // then across lanes: aligned groups of 2, 4, ... 64 lanes
-#pragma unroll
-        for (int o = 1; o < 64; o *= 2) ss += __shfl_xor(ss, o);
+        // then across lanes, aligned groups of 2, 4, ... 64 lanes: quad
+        // permutes for 2 and 4, then mirrors within 8 and 16 lanes (each
+        // lane of a group already holds the group's sum, so the mirrored
+        // lane holds the partner group's), then 32 and 64
+        ss += __int_as_float(dpp_xor1(__float_as_int(ss)));
+        ss += __int_as_float(dpp_xor2(__float_as_int(ss)));
+        ss += __int_as_float(dpp_mirror8(__float_as_int(ss)));
+        ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x140, 0xF, 0xF, false));
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
         const float inv = rms_inv(ss, K, eps);
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
@@ -659,7 +691,8 @@ hipError_t launch_mq(const RowsArgs &a, hipStream_t s, const char **name) {
 template <int QT, int M, int AX, int T, int NBL, int D, int WPB, bool KS = true>
 hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
     static char kname[64];
-    constexpr int D0 = QMV_FX_D0 < D - 1 ? QMV_FX_D0 : D - 1;
+    constexpr int D0W = AX == kActRms ? QMV_FX_D0_RMS : (AX == kActSilu ? QMV_FX_D0_SILU : QMV_FX_D0);
+    constexpr int D0 = D0W < D - 1 ? D0W : D - 1;
     constexpr bool FX = AX != kActQ8;
     auto kern = k_fx<QT, M, AX, T, NBL, D, D0, WPB, KS>;
     const int nrows = a.r1 - a.r0;
