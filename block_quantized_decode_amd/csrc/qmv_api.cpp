@@ -109,7 +109,7 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     if ((st = device_check(&dev)) != QMV_OK) return st;
     if (xq_out != nullptr) xq_out->n = W->cols;
     if (r0 == r1) return QMV_OK;
-    qmv::RowsArgs a;
+    qmv::RowsArgs a = {};
     a.qtype = qtype;
     a.y = y;
     a.wq = W->q;
