@@ -119,3 +119,71 @@ def test_rmsnorm_fx_unsupported_k():
         with pytest.raises(qmv.QmvError):
             qmv.qmv_matvec_q4_fx_rmsnorm(dev(wq), dev(wd), dev(synth.normal(rng, (k,))),
                                          dev(np.ones(k, np.float32)), 1e-5)
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("rows,k", [(2560, 2048), (11264, 2048), (11008, 4096)])
+def test_rmsnorm_fx_full_size_launches(qtype, rows, k):
+    """The launches the bench's fusion section times, at full size: rmsnorm
+    ahead of the concatenated TinyLlama-1.1B projections (W_q|W_k|W_v 2560 x
+    2048, W_gate|W_up 11264 x 2048) and of the Llama-7B W_up."""
+    announce(f"rmsnorm fx full size q{qtype} {rows}x{k}")
+    rng = np.random.default_rng(3000 + rows + k)
+    wq, wd = _weights(rng, qtype, rows, k)
+    x = synth.normal(rng, (k,))
+    wn = (1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32)
+    xq, xd = orc.quantize_q8(orc.rmsnorm(x, wn, 1e-5))
+    yref = orc.matvec(qtype, wq, wd, xq, xd)
+    y, qo, do = _run(qtype, wq, wd, x, wn, 1e-5)
+    assert np.array_equal(qo, xq) and np.array_equal(do.view(np.uint32), xd.view(np.uint32))
+    check_close(qtype, y, yref, wq, wd, xq, xd, what=f"full size {rows}x{k}")
+
+
+def test_fused_forms_graph_replay():
+    """Prepared calls of the rmsnorm and FFN-gate forms and of the 4-row
+    matrix-core product captured in one HIP graph, chained as in a decode
+    layer (the gate form reads the halves of the gate|up output the rmsnorm
+    form wrote): every replay, with eager work and synchronisations in
+    between, gives the eager result bit for bit."""
+    announce("fused forms graph replay")
+    rng = np.random.default_rng(3200)
+    k, hidden = 2048, 5632
+    stream = torch.cuda.Stream()
+    s = stream.cuda_stream
+    wgu_q, wgu_d = _weights(rng, 4, 2 * hidden, k)
+    wdn_q, wdn_d = _weights(rng, 4, k, hidden)
+    x = dev(synth.normal(rng, (k,)))
+    wn = dev((1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32))
+    y_gu = torch.zeros(2 * hidden, dtype=torch.float32, device="cuda:0")
+    y_dn = torch.zeros(k, dtype=torch.float32, device="cuda:0")
+    X4 = synth.normal(rng, (4, k))
+    x4q, x4d = orc.quantize_q8(X4)
+    Y4 = torch.zeros((4, 2 * hidden), dtype=torch.float32, device="cuda:0")
+    gq, gd = dev(wgu_q), dev(wgu_d)
+    calls = [qmv.prepare_matvec_fx_rmsnorm(4, gq, gd, x, wn, 1e-5, y_gu, stream=s),
+             qmv.prepare_matvec_fx_silu_mul(4, dev(wdn_q), dev(wdn_d), y_gu[:hidden], y_gu[hidden:], y_dn, stream=s),
+             qmv.prepare_gemm(4, gq, gd, dev(x4q), dev(x4d), Y4, stream=s)]
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    eager = [host(t).copy() for t in (y_gu, y_dn, Y4)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for t in (y_gu, y_dn, Y4):
+            t.fill_(-1.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip((y_gu, y_dn, Y4), eager):
+            assert np.array_equal(host(t), e), f"replay {rep} differs from the eager result"
+    # the eager chain itself against the oracle
+    h = orc.rmsnorm(host(x), host(wn), 1e-5)
+    hq, hd = orc.quantize_q8(h)
+    check_close(4, eager[0], orc.matvec(4, wgu_q, wgu_d, hq, hd), wgu_q, wgu_d, hq, hd, what="rmsnorm + gate|up")
+    Y4ref = orc.gemm(4, wgu_q, wgu_d, x4q, x4d)
+    for i in range(4):
+        check_close(4, eager[2][i], Y4ref[i], wgu_q, wgu_d, x4q[i], x4d[i], what=f"4-row product row {i}")

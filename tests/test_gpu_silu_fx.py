@@ -95,3 +95,23 @@ def test_silu_fx_concatenated_halves_and_rows(qtype):
         _check_activation(a_ref, qh, dh)
         assert np.all(y[:r0] == -7.5) and np.all(y[r1:] == -7.5)
         check_close(qtype, y, orc.matvec(qtype, wq, wd, qh, dh), wq, wd, qh, dh, r0, r1, what=f"[{r0},{r1})")
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("rows,k", [(2048, 5632), (4096, 11008)])
+def test_silu_fx_full_size_launches(qtype, rows, k):
+    """The launches the bench's fusion section times, at full size: the gate
+    ahead of the TinyLlama-1.1B and Llama-7B down projections, g and u read
+    from the two halves of one gate|up output buffer."""
+    announce(f"silu fx full size q{qtype} {rows}x{k}")
+    rng = np.random.default_rng(3100 + rows + k)
+    wq, wd = _weights(rng, qtype, rows, k)
+    gu = synth.normal(rng, (2 * k,))
+    gu_dev = dev(gu)
+    a_ref = orc.silu_mul(gu[:k], gu[k:])
+    qo = torch.zeros(k, dtype=torch.int8, device="cuda:0")
+    do = torch.zeros(k // 32, dtype=torch.float32, device="cuda:0")
+    y = host(_fxs(qtype)(dev(wq), dev(wd), gu_dev[:k], gu_dev[k:], xq_out=(qo, do)))
+    qh, dh = host(qo), host(do)
+    _check_activation(a_ref, qh, dh)
+    check_close(qtype, y, orc.matvec(qtype, wq, wd, qh, dh), wq, wd, qh, dh, what=f"full size {rows}x{k}")
