@@ -99,7 +99,12 @@ struct Region {
     static constexpr int BYTES = DX + 4 * 64 * 4;
 };
 
-template <int QT, int MT, int RT, int WPB, int D>
+// PK: the weights come in the pack-once layout of kernels_pack.hip (units of
+// 16 rows x 4 blocks, quants in the A operand's lane order, scales [row][block]);
+// the quants go from the load straight into the operand, never through LDS.
+// The sums are the same operations in the same order as for the row-major
+// layout, so the two give the same bits.
+template <int QT, int MT, int RT, int WPB, int D, bool PK>
 __global__ void __launch_bounds__(64 * WPB)
 k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
      const int8_t *__restrict__ xq, const float *__restrict__ xd, int32_t M, int32_t r0, int32_t r1) {
@@ -124,8 +129,15 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     const int nst = wid < ns ? (ns - wid + WPB - 1) / WPB : 0;
     auto stage = [&](int j) { return wid + WPB * j; };
 
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + (size_t)g0 * nb * QB, nrow * nb * QB);
-    const __amdgpu_buffer_rsrc_t rwd = make_rsrc(wd + (size_t)g0 * nb, nrow * nb * 4);
+    // packed: unit (tile T, quad s) at T nq + s, UQ bytes of quants and 256 of
+    // scales; g0 is a multiple of 16 there
+    const int nq = (nb + KU - 1) / KU;
+    constexpr int UQ = 64 * KU * QB / 4;
+    const int ntile = (nrow + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t rw = PK ? make_rsrc(wq + (size_t)(g0 >> 4) * nq * UQ, ntile * nq * UQ)
+                                         : make_rsrc(wq + (size_t)g0 * nb * QB, nrow * nb * QB);
+    const __amdgpu_buffer_rsrc_t rwd = PK ? make_rsrc(wd + (size_t)(g0 >> 4) * nq * 64, ntile * nq * 256)
+                                          : make_rsrc(wd + (size_t)g0 * nb, nrow * nb * 4);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq, M * K);
     const __amdgpu_buffer_rsrc_t rxd = make_rsrc(xd, M * nb * 4);
 
@@ -134,25 +146,32 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     //   weights Q8_0: row 8 i + l / 8, 16-byte piece l % 8 of the stage's 128 bytes
     //   activation: row 8 i + l / 8, piece l % 8
     //   scales: row l, the stage's 4 blocks (16 bytes)
+    //   packed weights: tile i (Q4_0) or i / 2 (Q8_0, half i % 2), this lane's 16 bytes
+    //   packed scales: row lane % 16 of tile lane / 16, the unit's 4 blocks
     int ow[St::NW];
 #pragma unroll
-    for (int i = 0; i < St::NW; ++i)
-        ow[i] = (QT == 8) ? ((8 * i + (lane >> 3)) * nb * 32 + 16 * (lane & 7))
-                          : ((16 * i + (lane >> 2)) * nb * 16 + 16 * (lane & 3));
+    for (int i = 0; i < St::NW; ++i) {
+        if constexpr (PK)
+            ow[i] = (QT == 8) ? ((i >> 1) * nq * UQ + 1024 * (i & 1) + 16 * lane) : (i * nq * UQ + 16 * lane);
+        else
+            ow[i] = (QT == 8) ? ((8 * i + (lane >> 3)) * nb * 32 + 16 * (lane & 7))
+                              : ((16 * i + (lane >> 2)) * nb * 16 + 16 * (lane & 3));
+    }
     int ox[2 * MT];
 #pragma unroll
     for (int i = 0; i < 2 * MT; ++i) ox[i] = (8 * i + (lane >> 3)) * K + 16 * (lane & 7);
-    const int odw = lane < 16 * RT ? lane * nb * 4 : kOOB;
+    const int odw = lane >= 16 * RT ? kOOB : PK ? (lane >> 4) * nq * 256 + 16 * (lane & 15) : lane * nb * 4;
+    const int sw = PK ? UQ : KU * QB, sd = PK ? 256 : KU * 4;  // weight and scale bytes per stage
     const int odx = lane < 16 * MT ? lane * nb * 4 : kOOB;
 
     auto load = [&](St &st, int j) __attribute__((always_inline)) {
         const bool live = j < nst;  // past this wavefront's stages: empty loads
         const int s = stage(j);
 #pragma unroll
-        for (int i = 0; i < St::NW; ++i) st.w[i] = ld16<kNT>(rw, live ? ow[i] + s * KU * QB : kOOB);
+        for (int i = 0; i < St::NW; ++i) st.w[i] = ld16<kNT>(rw, live ? ow[i] + s * sw : kOOB);
 #pragma unroll
         for (int i = 0; i < 2 * MT; ++i) st.x[i] = ld16<0>(rx, live ? ox[i] + s * KU * 32 : kOOB);
-        st.dw = __builtin_bit_cast(v4f, ld16<0>(rwd, live ? odw + s * KU * 4 : kOOB));
+        st.dw = __builtin_bit_cast(v4f, ld16<0>(rwd, live ? odw + s * sd : kOOB));
         st.dx = __builtin_bit_cast(v4f, ld16<0>(rxd, live ? odx + s * KU * 4 : kOOB));
     };
     auto stash = [&](St &st, int j) __attribute__((always_inline)) {
@@ -164,7 +183,9 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
                 st.dx[e] = 0.0f;
             }
         }
-        if constexpr (QT == 8) {
+        if constexpr (PK) {
+            // the quants stay in registers
+        } else if constexpr (QT == 8) {
 #pragma unroll
             for (int i = 0; i < St::NW; ++i)
                 *reinterpret_cast<v4i *>(reg + Rg::W + img(8 * i + (lane >> 3), lane & 7)) = st.w[i];
@@ -203,7 +224,7 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[a][t][v] = 0.0f;
 
-    auto compute = [&]() __attribute__((always_inline)) {
+    auto compute = [&](const St &st) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int q = 2 * u + (g >> 1), h = 8 * (g & 1);  // piece and half of elements 8 g .. 8 g + 7
@@ -223,7 +244,16 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
             }
 #pragma unroll
             for (int a = 0; a < RT; ++a) {
-                const v2i aw = *reinterpret_cast<const v2i *>(reg + Rg::W + img(16 * a + i16, q) + h);
+                v2i aw;
+                if constexpr (PK && QT == 4) {  // nibbles of elements 8 g + j and 8 g + 4 + j in byte j
+                    const unsigned w = (unsigned)st.w[a][u];
+                    aw = (v2i){(int)(w & 0x0F0F0F0Fu), (int)((w >> 4) & 0x0F0F0F0Fu)};
+                } else if constexpr (PK) {
+                    const v4i &w = st.w[2 * a + (u >> 1)];
+                    aw = (v2i){w[2 * (u & 1)], w[2 * (u & 1) + 1]};
+                } else {
+                    aw = *reinterpret_cast<const v2i *>(reg + Rg::W + img(16 * a + i16, q) + h);
+                }
                 const v4f dw4 = *reinterpret_cast<const v4f *>(reg + Rg::DW + 4 * (64 * u + 16 * a + 4 * g));
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
@@ -251,7 +281,7 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
             // in order)
             stash(ring[d], j);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            compute();
+            compute(ring[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -277,7 +307,7 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     }
 }
 
-template <int QT, int MT, int RT>
+template <int QT, int MT, int RT, bool PK>
 hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
     // register stages in the ring (D - 1 in flight) by activation tiles
     // (measured: deeper rings for one tile lose more to registers than they
@@ -288,38 +318,38 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
     constexpr int lds = lds_stage > lds_part ? lds_stage : lds_part;
     static_assert(lds <= 160 * 1024, "LDS budget");
     static char kname[64];
-    auto kern = k_mm<QT, MT, RT, WPB, D>;
+    auto kern = k_mm<QT, MT, RT, WPB, D, PK>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
     const int grid = (a.r1 - a.r0 + 16 * RT - 1) / (16 * RT);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.Y, a.wq, a.wd, a.rows, a.K, a.xq, a.xd, a.M,
-                       a.r0, a.r1);
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "mm_q%d_mt%d_rt%d_w%d_d%d", QT, MT, RT, WPB, D);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.Y, PK ? static_cast<const int8_t *>(a.pq) : a.wq,
+                       PK ? a.pd : a.wd, a.rows, a.K, a.xq, a.xd, a.M, a.r0, a.r1);
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "mm%s_q%d_mt%d_rt%d_w%d_d%d", PK ? "p" : "", QT, MT, RT, WPB, D);
     *name = kname;
     return hipGetLastError();
 }
 
-template <int QT, int MT>
+template <int QT, int MT, bool PK>
 hipError_t launch_mt(const GemmArgs &a, int num_cu, hipStream_t s, const char **name) {
     // weight-row tiles per workgroup: enough that one workgroup per compute
     // unit covers the range, at most 4
     const int tiles = (a.r1 - a.r0 + 15) / 16;
     const int rt = (tiles + num_cu - 1) / num_cu;
-    if (rt <= 1) return launch_cfg<QT, MT, 1>(a, s, name);
-    if (rt <= 2) return launch_cfg<QT, MT, 2>(a, s, name);
-    if (rt <= 3) return launch_cfg<QT, MT, 3>(a, s, name);
-    return launch_cfg<QT, MT, 4>(a, s, name);
+    if (rt <= 1) return launch_cfg<QT, MT, 1, PK>(a, s, name);
+    if (rt <= 2) return launch_cfg<QT, MT, 2, PK>(a, s, name);
+    if (rt <= 3) return launch_cfg<QT, MT, 3, PK>(a, s, name);
+    return launch_cfg<QT, MT, 4, PK>(a, s, name);
 }
 
-template <int QT>
+template <int QT, bool PK>
 hipError_t launch_q(const GemmArgs &a, int num_cu, hipStream_t s, const char **name) {
     switch ((a.M + 15) / 16) {
-        case 1: return launch_mt<QT, 1>(a, num_cu, s, name);
-        case 2: return launch_mt<QT, 2>(a, num_cu, s, name);
-        default: return launch_mt<QT, 4>(a, num_cu, s, name);
+        case 1: return launch_mt<QT, 1, PK>(a, num_cu, s, name);
+        case 2: return launch_mt<QT, 2, PK>(a, num_cu, s, name);
+        default: return launch_mt<QT, 4, PK>(a, num_cu, s, name);
     }
 }
 
@@ -327,7 +357,11 @@ hipError_t launch_q(const GemmArgs &a, int num_cu, hipStream_t s, const char **n
 
 hipError_t launch_mm(const GemmArgs &a, int num_cu, hipStream_t s, const char **name) {
     if (a.M < 1 || a.M > kGemmMaxRows) return hipErrorNotSupported;
-    return a.qtype == 4 ? launch_q<4>(a, num_cu, s, name) : launch_q<8>(a, num_cu, s, name);
+    if (a.pq != nullptr) {
+        if (a.r0 % 16 != 0) return hipErrorInvalidValue;  // packed tiles start every 16 rows
+        return a.qtype == 4 ? launch_q<4, true>(a, num_cu, s, name) : launch_q<8, true>(a, num_cu, s, name);
+    }
+    return a.qtype == 4 ? launch_q<4, false>(a, num_cu, s, name) : launch_q<8, false>(a, num_cu, s, name);
 }
 
 }  // namespace qmv

@@ -46,7 +46,9 @@ struct GemmArgs {
     const int8_t *xq;          // Q8_0 activation quants, M x K
     const float *xd;           // Q8_0 activation scales, M x K/32
     int32_t M;                 // 1 .. 64
-    int32_t r0, r1;
+    int32_t r0, r1;            // packed weights: r0 a multiple of 16
+    const void *pq;            // packed quants (pack-once layout), or null: wq / wd row-major
+    const float *pd;           // packed scales
 };
 
 constexpr int kGemmMaxRows = 64;  // activation rows per matrix-core launch
@@ -54,6 +56,14 @@ constexpr int kGemmMaxRows = 64;  // activation rows per matrix-core launch
 // Matrix-core product with one workgroup per compute unit and the K
 // dimension split over its wavefronts (num_cu sizes the row tiles).
 hipError_t launch_mm(const GemmArgs &a, int num_cu, hipStream_t s, const char **name);
+
+// Pack-once layout of Q4_0 / Q8_0 weights for the matrix-core product (units
+// of 16 rows x 4 blocks in the A operand's lane order): sizes in bytes of the
+// packed quants and scales, and the packing launch (a pure permutation).
+size_t pack_q_bytes(int qtype, int32_t rows, int32_t K);
+size_t pack_d_bytes(int32_t rows, int32_t K);
+hipError_t launch_pack(int qtype, void *pq, float *pd, const int8_t *wq, const float *wd, int32_t rows, int32_t K,
+                       hipStream_t s, const char **name);
 
 // Q8_0 quantization of nblk blocks of 32 floats (activations or weights).
 hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,

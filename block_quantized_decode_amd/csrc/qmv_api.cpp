@@ -176,6 +176,9 @@ qmv_status matvec_fx_silu_mul(int qtype, float *y, const qmv_qtensor *W, const f
     return rows_common(qtype, y, W, 1, g, nullptr, nullptr, xq, r0, r1, stream, nullptr, 0.0f, u);
 }
 
+qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, const void *pq, const float *pd,
+                       int32_t rows, int32_t K, const qmv_qtensor *X, int32_t r0, int32_t r1, int dev, void *stream);
+
 qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
                 void *stream) {
     if (X == nullptr || X->q == nullptr || X->d == nullptr || Y == nullptr) return QMV_E_ARG;
@@ -194,16 +197,43 @@ qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
     int dev = -1;
     if ((st = device_check(&dev)) != QMV_OK) return st;
     if (r0 == r1) return QMV_OK;
-    const int32_t nb = W->cols / QMV_QK;
+    return gemm_passes(qtype, Y, W->q, W->d, nullptr, nullptr, W->rows, W->cols, X, r0, r1, dev, stream);
+}
+
+qmv_status gemm_packed(int qtype, float *Y, const qmv_packed *P, const qmv_qtensor *X, int32_t r0, int32_t r1,
+                       void *stream) {
+    if (P == nullptr || P->q == nullptr || P->d == nullptr) return QMV_E_ARG;
+    if (X == nullptr || X->q == nullptr || X->d == nullptr || Y == nullptr) return QMV_E_ARG;
+    if (P->type != qtype || X->type != QMV_Q8_0) return QMV_E_FORMAT;
+    if (P->rows < 0 || P->cols <= 0 || (P->cols % QMV_QK) != 0 || P->cols > 131072) return QMV_E_SHAPE;
+    if (X->rows < 1 || X->cols != P->cols) return QMV_E_SHAPE;
+    if (r0 < 0 || r1 > P->rows || r0 > r1 || (r0 % 16) != 0) return QMV_E_SHAPE;
+    if (!aligned(P->q, 16) || !aligned(P->d, 16) || !aligned(X->q, 16) || !aligned(X->d, 4) || !aligned(Y, 4))
+        return QMV_E_ARG;
+    int dev = -1;
+    qmv_status st = device_check(&dev);
+    if (st != QMV_OK) return st;
+    if (r0 == r1) return QMV_OK;
+    return gemm_passes(qtype, Y, nullptr, nullptr, P->q, P->d, P->rows, P->cols, X, r0, r1, dev, stream);
+}
+
+// ceil(M / 64) matrix-core passes over the weights (row-major wq / wd, or
+// packed pq / pd)
+qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, const void *pq, const float *pd,
+                       int32_t rows, int32_t K, const qmv_qtensor *X, int32_t r0, int32_t r1, int dev, void *stream) {
+    const int32_t nb = K / QMV_QK;
+    qmv_status st = QMV_OK;
     for (int32_t m0 = 0; m0 < X->rows; m0 += qmv::kGemmMaxRows) {
-        qmv::GemmArgs a;
+        qmv::GemmArgs a = {};
         a.qtype = qtype;
-        a.Y = Y + (size_t)m0 * W->rows;
-        a.wq = W->q;
-        a.wd = W->d;
-        a.rows = W->rows;
-        a.K = W->cols;
-        a.xq = X->q + (size_t)m0 * W->cols;
+        a.Y = Y + (size_t)m0 * rows;
+        a.wq = wq;
+        a.wd = wd;
+        a.pq = pq;
+        a.pd = pd;
+        a.rows = rows;
+        a.K = K;
+        a.xq = X->q + (size_t)m0 * K;
         a.xd = X->d + (size_t)m0 * nb;
         a.M = (X->rows - m0) < qmv::kGemmMaxRows ? (X->rows - m0) : qmv::kGemmMaxRows;
         a.r0 = r0;
@@ -303,6 +333,43 @@ qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int
 qmv_status qmv_gemm_q4(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
                        void *stream) {
     return gemm(QMV_Q4_0, Y, W, X, r0, r1, stream);
+}
+
+qmv_status qmv_pack_bytes(int32_t type, int32_t rows, int32_t cols, int64_t *q_bytes, int64_t *d_bytes) {
+    if (q_bytes == nullptr || d_bytes == nullptr) return QMV_E_ARG;
+    if (type != QMV_Q4_0 && type != QMV_Q8_0) return QMV_E_FORMAT;
+    if (rows < 0 || cols <= 0 || (cols % QMV_QK) != 0 || cols > 131072) return QMV_E_SHAPE;
+    *q_bytes = (int64_t)qmv::pack_q_bytes(type, rows, cols);
+    *d_bytes = (int64_t)qmv::pack_d_bytes(rows, cols);
+    return QMV_OK;
+}
+
+qmv_status qmv_pack_weights(qmv_packed *P, const qmv_qtensor *W, void *stream) {
+    if (P == nullptr || P->q == nullptr || P->d == nullptr) return QMV_E_ARG;
+    qmv_status st = check_weight(W, 0);
+    if (st != QMV_OK) return st;
+    if (W->cols > 131072) return QMV_E_SHAPE;
+    if ((st = check_weight_align(W)) != QMV_OK) return st;
+    if (!aligned(P->q, 16) || !aligned(P->d, 16)) return QMV_E_ARG;
+    if ((st = device_check(nullptr)) != QMV_OK) return st;
+    P->rows = W->rows;
+    P->cols = W->cols;
+    P->type = W->type;
+    if (W->rows == 0) return QMV_OK;
+    const char *name = "";
+    hipError_t e = qmv::launch_pack(W->type, P->q, P->d, W->q, W->d, W->rows, W->cols,
+                                    static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)((W->rows + 15) / 16));
+}
+
+qmv_status qmv_gemm_q8_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X, int32_t r0, int32_t r1,
+                              void *stream) {
+    return gemm_packed(QMV_Q8_0, Y, P, X, r0, r1, stream);
+}
+
+qmv_status qmv_gemm_q4_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X, int32_t r0, int32_t r1,
+                              void *stream) {
+    return gemm_packed(QMV_Q4_0, Y, P, X, r0, r1, stream);
 }
 
 const char *qmv_status_str(qmv_status s) {

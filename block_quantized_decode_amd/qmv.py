@@ -43,6 +43,11 @@ class QAct(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("n", ctypes.c_int32)]
 
 
+class Packed(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("type", ctypes.c_uint8)]
+
+
 _lib = None
 
 # name -> argtypes (restype c_int = qmv_status)
@@ -64,6 +69,11 @@ _SIGS = {
                                   ctypes.c_int32, _P],
     "qmv_gemm_q8": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_gemm_q4": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_pack_bytes": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                       ctypes.POINTER(ctypes.c_int64)],
+    "qmv_pack_weights": [ctypes.POINTER(Packed), ctypes.POINTER(QTensor), _P],
+    "qmv_gemm_q8_packed": [_P, ctypes.POINTER(Packed), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_gemm_q4_packed": [_P, ctypes.POINTER(Packed), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_device_check": [],
 }
 
@@ -292,6 +302,60 @@ def qmv_gemm_q4(wq, wd, xq, xd, r0=None, r1=None, Y=None):
     return _gemm(QMV_Q4_0, "qmv_gemm_q4", wq, wd, xq, xd, r0, r1, Y)
 
 
+def qmv_pack_bytes(qtype: int, rows: int, cols: int) -> tuple[int, int]:
+    """Bytes of the packed quants and scales of a rows x cols matrix (host only)."""
+    qb, db = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().qmv_pack_bytes(qtype, rows, cols, ctypes.byref(qb), ctypes.byref(db)), "qmv_pack_bytes")
+    return qb.value, db.value
+
+
+class PackedWeights:
+    """Device weights in the pack-once layout (q: uint8 [q_bytes], d: float32
+    [d_bytes / 4]) with their shape; desc is the qmv_packed descriptor."""
+
+    def __init__(self, q: torch.Tensor, d: torch.Tensor, rows: int, cols: int, qtype: int):
+        self.q, self.d, self.rows, self.cols, self.qtype = q, d, rows, cols, qtype
+        self.desc = Packed(q.data_ptr(), d.data_ptr(), rows, cols, qtype)
+
+
+def qmv_pack_weights(wq, wd, qtype: int, q: torch.Tensor | None = None,
+                     d: torch.Tensor | None = None) -> PackedWeights:
+    """Pack a row-major Q4_0 / Q8_0 device matrix (wq, wd) once (see include/qmv.h)."""
+    W = qtensor(wq, wd, qtype)
+    qb, db = qmv_pack_bytes(qtype, W.rows, W.cols)
+    if q is None:
+        q = torch.empty(max(qb, 16), dtype=torch.uint8, device=wd.device)
+    if d is None:
+        d = torch.empty(max(db // 4, 4), dtype=torch.float32, device=wd.device)
+    _dev(q, (torch.uint8, torch.int8))
+    _dev(d, torch.float32)
+    if q.numel() < qb or d.numel() * 4 < db:
+        raise ValueError(f"packed buffers too small: need {qb} and {db} bytes")
+    P = Packed(q.data_ptr(), d.data_ptr(), 0, 0, 0)
+    _check(lib().qmv_pack_weights(ctypes.byref(P), ctypes.byref(W), _stream()), "qmv_pack_weights")
+    return PackedWeights(q, d, P.rows, P.cols, P.type)
+
+
+def _gemm_packed(qtype, fname, P: PackedWeights, xq, xd, r0, r1, Y):
+    X = qtensor(xq, xd, QMV_Q8_0)
+    r0 = 0 if r0 is None else r0
+    r1 = P.rows if r1 is None else r1
+    if Y is None:
+        Y = torch.zeros((X.rows, P.rows), dtype=torch.float32, device=xd.device)
+    _dev(Y, torch.float32)
+    _check(getattr(lib(), fname)(Y.data_ptr(), ctypes.byref(P.desc), ctypes.byref(X), r0, r1, _stream()), fname)
+    return Y
+
+
+def qmv_gemm_q8_packed(P: PackedWeights, xq, xd, r0=None, r1=None, Y=None):
+    """qmv_gemm_q8 on packed weights (r0 a multiple of 16)."""
+    return _gemm_packed(QMV_Q8_0, "qmv_gemm_q8_packed", P, xq, xd, r0, r1, Y)
+
+
+def qmv_gemm_q4_packed(P: PackedWeights, xq, xd, r0=None, r1=None, Y=None):
+    return _gemm_packed(QMV_Q4_0, "qmv_gemm_q4_packed", P, xq, xd, r0, r1, Y)
+
+
 class Prepared:
     """A libqmv call with its arguments marshalled once: calling it costs one
     ctypes call (on the stream current at preparation time unless another
@@ -376,3 +440,14 @@ def prepare_gemm(qtype, wq, wd, xq, xd, Y, r0=None, r1=None, stream=None) -> Pre
     fname = "qmv_gemm_q4" if qtype == QMV_Q4_0 else "qmv_gemm_q8"
     args = [Y.data_ptr(), ctypes.byref(W), ctypes.byref(X), r0, r1]
     return Prepared(fname, args, [W, X, wq, wd, xq, xd, Y], stream)
+
+
+def prepare_gemm_packed(P: PackedWeights, xq, xd, Y, r0=None, r1=None, stream=None) -> Prepared:
+    """Prepared qmv_gemm_q4_packed / qmv_gemm_q8_packed."""
+    X = qtensor(xq, xd, QMV_Q8_0)
+    _dev(Y, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = P.rows if r1 is None else r1
+    fname = "qmv_gemm_q4_packed" if P.qtype == QMV_Q4_0 else "qmv_gemm_q8_packed"
+    args = [Y.data_ptr(), ctypes.byref(P.desc), ctypes.byref(X), r0, r1]
+    return Prepared(fname, args, [P, X, xq, xd, Y], stream)

@@ -233,6 +233,58 @@ qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
 qmv_status qmv_gemm_q4(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
                        int32_t r0, int32_t r1, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Pack-once weight layout for the matrix-core product.  The spec stores
+ * weights row-major (section 4 table); its companion write-ups on
+ * block-quantized products re-lay the weights once, ahead of time, into the
+ * order the multiply instruction consumes them.  Here the unit is a tile of
+ * 16 weight rows by 4 blocks (128 elements), units of one tile consecutive
+ * (nq = ceil(cols / 128) of them), tiles in row order:
+ *   q of unit u = T * nq + Q (tile T, block quad Q): 1024 bytes (Q4_0) or
+ *     2048 bytes (Q8_0) at u * 1024 or u * 2048.  Lane l = 16 g + i (row
+ *     16 T + i, elements 8 g .. 8 g + 7 of each block) owns, for block
+ *     4 Q + b, Q4_0: the 4 bytes at 16 l + 4 b, byte j holding element
+ *     8 g + j in its low nibble and 8 g + 4 + j in its high nibble (nibble =
+ *     value + 8, as stored); Q8_0: the 8 bytes at 1024 (b / 2) + 16 l +
+ *     8 (b % 2), elements 8 g .. 8 g + 7.
+ *   d of unit u: 64 floats at 64 u, row 16 T + r and block 4 Q + b at 4 r + b.
+ * Rows past the matrix and blocks past cols hold value 0 and scale 0.
+ * Packing is a permutation of the stored bytes and scales; the packed
+ * product computes the same sums in the same order as qmv_gemm_* on the
+ * row-major weights for M > 8, so the two give the same bits.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    void *q;           /* packed quants, 16-byte aligned */
+    float *d;          /* packed scales, 16-byte aligned */
+    int32_t rows;      /* set by qmv_pack_weights */
+    int32_t cols;
+    uint8_t type;      /* QMV_Q4_0 or QMV_Q8_0 */
+} qmv_packed;
+
+/* Bytes the packed form of a type x rows x cols matrix needs: q_bytes =
+ * ceil(rows / 16) * ceil(cols / 128) * (1024 or 2048), d_bytes =
+ * ceil(rows / 16) * ceil(cols / 128) * 256.  Host only (no device call).
+ * Errors: QMV_E_ARG (null outputs), QMV_E_FORMAT (type), QMV_E_SHAPE
+ * (rows < 0, cols <= 0, cols % 32 != 0 or cols > 131072). */
+qmv_status qmv_pack_bytes(int32_t type, int32_t rows, int32_t cols, int64_t *q_bytes, int64_t *d_bytes);
+
+/* Writes W (row-major, as qmv_quantize_weights leaves it) into P->q / P->d
+ * (caller-allocated, sizes from qmv_pack_bytes) in the layout above, and
+ * sets P->rows, P->cols and P->type from W.  Enqueued on stream; W is
+ * unchanged.  Errors as qmv_quantize_weights, plus QMV_E_ARG for a null or
+ * misaligned P->q / P->d and QMV_E_SHAPE for cols > 131072. */
+qmv_status qmv_pack_weights(qmv_packed *P, const qmv_qtensor *W, void *stream);
+
+/* The product of qmv_gemm_q8 / qmv_gemm_q4 on packed weights, on the
+ * matrix-core path for every M >= 1 (for M <= 8 the row-major call's
+ * dot-product path reads the weights at a higher rate).  r0 must be a
+ * multiple of 16 (r1 is free).  Y, X, limits and errors as qmv_gemm_*, with
+ * QMV_E_FORMAT when P->type is not the call's type. */
+qmv_status qmv_gemm_q8_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X,
+                              int32_t r0, int32_t r1, void *stream);
+qmv_status qmv_gemm_q4_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X,
+                              int32_t r0, int32_t r1, void *stream);
+
 /* Text of a status code (static storage). */
 const char *qmv_status_str(qmv_status s);
 

@@ -49,6 +49,7 @@ def test_header_declares_the_product_calls():
               "qmv_matvec_q8_fx", "qmv_matvec_q4_fx", "qmv_gemm_q8", "qmv_gemm_q4",
               "qmv_matvec_q8_fx_rmsnorm", "qmv_matvec_q4_fx_rmsnorm",
               "qmv_matvec_q8_fx_silu_mul", "qmv_matvec_q4_fx_silu_mul",
+              "qmv_pack_bytes", "qmv_pack_weights", "qmv_gemm_q8_packed", "qmv_gemm_q4_packed",
               "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
         assert n in names
 
@@ -166,6 +167,44 @@ def test_gemm_validation(lib, fn, t):
     assert f(Y, ctypes.byref(W), ctypes.byref(QT(A + 4, B, 4, 64, Q8)), 0, 8, None) == E_ARG
 
 
+def test_pack_bytes(lib):
+    """Sizes of the packed layout: ceil(rows / 16) tiles x ceil(cols / 128)
+    units of 1024 (Q4_0) or 2048 (Q8_0) bytes of quants and 256 of scales."""
+    qb, db = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    f = lib.qmv_pack_bytes
+    for t, rows, cols, want_q, want_d in ((Q4, 16, 128, 1024, 256), (Q8, 16, 128, 2048, 256),
+                                          (Q4, 17, 160, 4 * 1024, 4 * 256), (Q8, 1, 32, 2048, 256),
+                                          (Q4, 11008, 4096, 688 * 32 * 1024, 688 * 32 * 256),
+                                          (Q8, 0, 64, 0, 0)):
+        assert f(t, rows, cols, ctypes.byref(qb), ctypes.byref(db)) == OK
+        assert (qb.value, db.value) == (want_q, want_d), (t, rows, cols)
+    assert f(Q4, 16, 128, None, ctypes.byref(db)) == E_ARG
+    assert f(5, 16, 128, ctypes.byref(qb), ctypes.byref(db)) == E_FORMAT
+    for rows, cols in ((-1, 128), (16, 0), (16, 100), (16, 131072 + 32)):
+        assert f(Q4, rows, cols, ctypes.byref(qb), ctypes.byref(db)) == E_SHAPE, (rows, cols)
+
+
+@pytest.mark.parametrize("fn,t", [("qmv_gemm_q8_packed", Q8), ("qmv_gemm_q4_packed", Q4)])
+def test_gemm_packed_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    P = QT(A + 0x4000, B + 0x4000, 40, 64, t)  # qmv_packed has the layout of qmv_qtensor
+    X = QT(A + 0x1000, B + 0x1000, 20, 64, Q8)
+    assert f(None, ctypes.byref(P), ctypes.byref(X), 0, 40, None) == E_ARG
+    assert f(Y, None, ctypes.byref(X), 0, 40, None) == E_ARG
+    assert f(Y, ctypes.byref(QT(0, B, 40, 64, t)), ctypes.byref(X), 0, 40, None) == E_ARG
+    assert f(Y, ctypes.byref(QT(A, B, 40, 64, 12 - t)), ctypes.byref(X), 0, 40, None) == E_FORMAT
+    assert f(Y, ctypes.byref(P), ctypes.byref(QT(A, B, 20, 64, Q4)), 0, 40, None) == E_FORMAT
+    assert f(Y, ctypes.byref(P), ctypes.byref(QT(A, B, 20, 96, Q8)), 0, 40, None) == E_SHAPE  # K mismatch
+    assert f(Y, ctypes.byref(P), ctypes.byref(X), 8, 40, None) == E_SHAPE   # r0 not a multiple of 16
+    assert f(Y, ctypes.byref(P), ctypes.byref(X), 0, 41, None) == E_SHAPE
+    assert f(Y, ctypes.byref(QT(A, B + 4, 40, 64, t)), ctypes.byref(X), 0, 40, None) == E_ARG  # scales 16-aligned
+    W = _w(t=t)
+    assert lib.qmv_pack_weights(None, ctypes.byref(W), None) == E_ARG
+    assert lib.qmv_pack_weights(ctypes.byref(QT(A + 8, B, 0, 0, 0)), ctypes.byref(W), None) == E_ARG
+    assert lib.qmv_pack_weights(ctypes.byref(P), ctypes.byref(_w(t=5)), None) == E_FORMAT
+    assert lib.qmv_pack_weights(ctypes.byref(P), ctypes.byref(_w(t=t, cols=33)), None) == E_SHAPE
+
+
 def test_quantize_validation(lib):
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(None, ctypes.c_void_p(Y), ctypes.c_int64(64), None) == E_ARG
@@ -203,4 +242,9 @@ def test_no_device_is_an_error_not_a_crash(lib):
     assert f(Y, ctypes.byref(W), A + 0x1000, A + 0x2000, None, 0, 8, None) == st
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(64), None) == st
+    P = QT(A + 0x4000, B + 0x4000, 0, 0, 0)
+    assert lib.qmv_pack_weights(ctypes.byref(P), ctypes.byref(W), None) == st
+    P = QT(A + 0x4000, B + 0x4000, 8, 64, Q8)
+    assert lib.qmv_gemm_q8_packed(Y, ctypes.byref(P), ctypes.byref(QT(A + 0x1000, B + 0x1000, 20, 64, Q8)),
+                                  0, 8, None) == st
     assert lib.qmv_last_kernel().decode() == ""
