@@ -64,6 +64,12 @@ constexpr int kMinus8 = (int)0xF8F8F8F8;
 #ifndef QMV_MM_D4
 #define QMV_MM_D4 2
 #endif
+#ifndef QMV_MM_W1  // wavefronts per workgroup: packed weights, one activation tile
+#define QMV_MM_W1 8
+#endif
+#ifndef QMV_MM_RTMAX  // weight-row tiles per workgroup, at most
+#define QMV_MM_RTMAX 4
+#endif
 
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -91,11 +97,11 @@ struct Stage {
     v4f dw, dx;
 };
 
-// Per-wavefront LDS region (bytes): activation image, weight image, weight
-// scales [4][64] and activation scales [4][64].
-template <int MT, int RT>
+// Per-wavefront LDS region (bytes): activation image, weight image (none for
+// packed weights), weight scales [4][64] and activation scales [4][64].
+template <int MT, int RT, bool PK>
 struct Region {
-    static constexpr int X = 0, W = X + MT * 16 * 128, DW = W + RT * 16 * 128, DX = DW + 4 * 64 * 4;
+    static constexpr int X = 0, W = X + MT * 16 * 128, DW = W + (PK ? 0 : RT * 16 * 128), DX = DW + 4 * 64 * 4;
     static constexpr int BYTES = DX + 4 * 64 * 4;
 };
 
@@ -108,7 +114,7 @@ template <int QT, int MT, int RT, int WPB, int D, bool PK>
 __global__ void __launch_bounds__(64 * WPB)
 k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
      const int8_t *__restrict__ xq, const float *__restrict__ xd, int32_t M, int32_t r0, int32_t r1) {
-    typedef Region<MT, RT> Rg;
+    typedef Region<MT, RT, PK> Rg;
     typedef Stage<QT, MT, RT> St;
     constexpr int QB = (QT == 8) ? 32 : 16;
     static_assert(RT * 16 <= 64 && MT * 16 <= 64, "scale loads: one row per lane");
@@ -312,8 +318,8 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
     // register stages in the ring (D - 1 in flight) by activation tiles
     // (measured: deeper rings for one tile lose more to registers than they
     // gain in flight; four tiles leave no room for a third stage)
-    constexpr int WPB = 8, D = MT == 1 ? QMV_MM_D1 : MT == 2 ? QMV_MM_D2 : QMV_MM_D4;
-    typedef Region<MT, RT> Rg;
+    constexpr int WPB = (PK && MT == 1) ? QMV_MM_W1 : 8, D = MT == 1 ? QMV_MM_D1 : MT == 2 ? QMV_MM_D2 : QMV_MM_D4;
+    typedef Region<MT, RT, PK> Rg;
     constexpr int lds_stage = WPB * Rg::BYTES, lds_part = WPB * RT * MT * 1024;
     constexpr int lds = lds_stage > lds_part ? lds_stage : lds_part;
     static_assert(lds <= 160 * 1024, "LDS budget");
@@ -337,7 +343,7 @@ hipError_t launch_mt(const GemmArgs &a, int num_cu, hipStream_t s, const char **
     // weight-row tiles per workgroup: enough that one workgroup per compute
     // unit covers the range, at most 4
     const int tiles = (a.r1 - a.r0 + 15) / 16;
-    const int rt = (tiles + num_cu - 1) / num_cu;
+    const int rt = min((tiles + num_cu - 1) / num_cu, QMV_MM_RTMAX);
     if (rt <= 1) return launch_cfg<QT, MT, 1, PK>(a, s, name);
     if (rt <= 2) return launch_cfg<QT, MT, 2, PK>(a, s, name);
     if (rt <= 3) return launch_cfg<QT, MT, 3, PK>(a, s, name);
