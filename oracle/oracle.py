@@ -56,6 +56,10 @@ class _Lib:
             "orc_tol_abs": [ctypes.c_int, P, P, i32, P, P, i32, i32, P],
             "orc_rmsnorm": [P, P, P, i64, ctypes.c_float],
             "orc_silu_mul": [P, P, P, i64],
+            "orc_quantize_q8_b128": [P, i64, P, P],
+            "orc_block_sums_zp": [ctypes.c_int, P, P, i32, P, i32, i32, P],
+            "orc_matvec_zp": [P, ctypes.c_int, P, P, P, i32, P, P, i32, i32],
+            "orc_tol_abs_zp": [ctypes.c_int, P, P, P, i32, P, P, i32, i32, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -252,3 +256,85 @@ def silu_mul(g, u):
     o = np.empty_like(g)
     lib().orc_silu_mul(_p(o), _p(g), _p(u), g.size)
     return o
+
+
+# ---------------------------------------------------------------------------
+# Block length 128 with a zero point (rules in the C file: "ONNX Runtime"
+# page, sections 3 and 4).  Weights: codes uint8 [rows, K] (bits 8) or
+# [rows, K/2] (bits 4), scales float32 [rows, K/128], zero points uint8
+# [rows, K/128] or None (the midpoint 2^(bits-1)).
+BL = 128
+
+
+def quantize_q8_b128(x):
+    """The Q8_0 rule on 128-element blocks: (q int8 of x.shape, d float32
+    [..., n/128])."""
+    x = _f32(x)
+    assert x.shape[-1] % BL == 0
+    q = np.empty(x.shape, np.int8)
+    d = np.empty(x.shape[:-1] + (x.shape[-1] // BL,), np.float32)
+    lib().orc_quantize_q8_b128(_p(x), x.size, _p(q), _p(d))
+    return q, d
+
+
+def _check_zp(bits, wq, wd, wzp):
+    rows, nb = wd.shape
+    cols = nb * BL
+    assert bits in (4, 8)
+    assert wq.dtype == np.uint8 and wq.shape == (rows, cols if bits == 8 else cols // 2)
+    assert wd.dtype == np.float32
+    if wzp is not None:
+        assert wzp.dtype == np.uint8 and wzp.shape == (rows, nb)
+    return rows, cols
+
+
+def _zp_ptr(wzp):
+    return None if wzp is None else _p(wzp)
+
+
+def block_sums_zp(bits, wq, wzp, xq, r0=None, r1=None):
+    """int32 sumi[r - r0, b] = sum over the block of (code - zp) * q."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    cols = xq.size
+    rows = wq.shape[0]
+    if wzp is not None:
+        wzp = np.ascontiguousarray(wzp, dtype=np.uint8)
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    out = np.zeros((r1 - r0, cols // BL), np.int32)
+    lib().orc_block_sums_zp(bits, _p(wq), _zp_ptr(wzp), cols, _p(xq), r0, r1, _p(out))
+    return out
+
+
+def matvec_zp(bits, wq, wd, wzp, xq, xd, r0=None, r1=None, y=None):
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    wd = _f32(wd)
+    if wzp is not None:
+        wzp = np.ascontiguousarray(wzp, dtype=np.uint8)
+    rows, cols = _check_zp(bits, wq, wd, wzp)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    xd = _f32(xd).reshape(-1)
+    assert xq.size == cols and xd.size == cols // BL
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    if y is None:
+        y = np.zeros(rows, np.float32)
+    lib().orc_matvec_zp(_p(y), bits, _p(wq), _p(wd), _zp_ptr(wzp), cols, _p(xq), _p(xd), r0, r1)
+    return y
+
+
+def tolerance_zp(bits, wq, wd, wzp, xq, xd, r0=None, r1=None):
+    """Per-row bound 1e-5 * sum_b |sumi * dw * dx| + 1e-6 for rows [r0, r1)."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    wd = _f32(wd)
+    if wzp is not None:
+        wzp = np.ascontiguousarray(wzp, dtype=np.uint8)
+    rows, cols = _check_zp(bits, wq, wd, wzp)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    xd = _f32(xd).reshape(-1)
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    out = np.zeros(r1 - r0, np.float64)
+    lib().orc_tol_abs_zp(bits, _p(wq), _p(wd), _zp_ptr(wzp), cols, _p(xq), _p(xd), r0, r1, _p(out))
+    return 1e-5 * out + 1e-6

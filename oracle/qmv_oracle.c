@@ -33,6 +33,22 @@
  *                       power-of-two invariants, fp64 brute force)
  *   orc_silu_mul        pinned (closed forms at 0 and at saturation, the
  *                       identity silu(g) - silu(-g) = g, fp64 brute force)
+ *   orc_quantize_q8_b128  pinned (equal to orc_quantize_q8 where each
+ *                       128-block's four 32-blocks share one maximum;
+ *                       closed forms; one scale per 128 elements)
+ *   orc_block_sums_zp   pinned (closed forms at the code extremes, the
+ *                       nibble order by one-hot activations, reduction to
+ *                       the Q8_0 / Q4_0 sums at the default zero point,
+ *                       int64 brute force)
+ *   orc_matvec_zp       pinned (fp64 brute force within the error bound,
+ *                       exact sums at unit scales, reduction to the
+ *                       symmetric formats)
+ *   orc_tol_abs_zp      pinned (closed forms)
+ *
+ * The zero-point format (the orc_*_zp functions) follows a second page:
+ * "ONNX Runtime" (opensolvers.com/apps/onnx.html), sections 3 (BlkLen=128
+ * CompInt8) and 4 (SQ8Bit: B' = B - 128, block sums scaled by
+ * -scale * (zp - 128), zp = 128 when the export gives none).
  */
 #include <math.h>
 #include <stdint.h>
@@ -342,5 +358,127 @@ void orc_silu_mul(float *o, const float *g, const float *u, int64_t n)
         float s = 1.0f / (1.0f + expf(-v));
         v = v * s;
         o[j] = v * u[j];
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Block length 128 with a zero point ("ONNX Runtime" page, sections 3 and
+ * 4: the real exports use 128-element blocks; 8-bit weights are unsigned
+ * codes B with a per-block zero point zp, the weight value being B - zp,
+ * and the activation is quantized to int8 per block of the same length
+ * (CompInt8)).
+ *
+ * Readings where the page is silent:
+ *   - a weight value is (code - zp) * scale, fp32 scale per block; zp is one
+ *     byte per block, and a missing zp array means the midpoint 2^(bits-1)
+ *     (the page: zp = 128 when the export omits it; the same midpoint rule
+ *     for 4 bits gives 8);
+ *   - 4-bit codes: two per byte, element 2i in the low nibble of byte i and
+ *     element 2i + 1 in the high nibble;
+ *   - the activation rule is the spec's Q8_0 rule applied to 128-element
+ *     blocks (one scale per 128 elements);
+ *   - the accumulation is the spec's, per 128-element block:
+ *       y[r] = sum over blocks, ascending, of ((float)sumi * dw) * dx,
+ *       sumi = sum over the block of (code - zp) * q, exact in int32.
+ * ---------------------------------------------------------------------- */
+#define BL 128
+
+void orc_quantize_q8_b128(const float *x, int64_t n, int8_t *q, float *d)
+{
+    for (int64_t b = 0; b < n / BL; ++b) {
+        const float *xb = x + b * BL;
+        float amax = 0.0f;
+        for (int i = 0; i < BL; ++i) {
+            float a = fabsf(xb[i]);
+            if (a > amax)
+                amax = a;
+        }
+        float db = amax / 127.0f;
+        float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+        for (int i = 0; i < BL; ++i) {
+            float v = xb[i] * id;
+            float t = v + copysignf(0.5f, xb[i]);
+            int qi = (int)truncf(t);
+            if (qi > 127)
+                qi = 127;
+            if (qi < -127)
+                qi = -127;
+            q[b * BL + i] = (int8_t)qi;
+        }
+        d[b] = db;
+    }
+}
+
+/* Code of element i of a row (bits 8: byte i; bits 4: see above). */
+static int zp_code(const uint8_t *row, int bits, int64_t i)
+{
+    if (bits == 8)
+        return row[i];
+    uint8_t byte = row[i / 2];
+    return (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+static int zp_of(const uint8_t *wzp, int bits, int32_t nb, int32_t r, int32_t b)
+{
+    if (wzp == 0)
+        return 1 << (bits - 1);
+    return wzp[(int64_t)r * nb + b];
+}
+
+static int32_t zp_block_sum(int bits, const uint8_t *wq, const uint8_t *wzp,
+                            int32_t cols, const int8_t *xq, int32_t r, int32_t b)
+{
+    int32_t nb = cols / BL;
+    const uint8_t *row = wq + (int64_t)r * (bits == 8 ? cols : cols / 2);
+    int zp = zp_of(wzp, bits, nb, r, b);
+    int32_t s = 0;
+    for (int i = 0; i < BL; ++i) {
+        int64_t e = (int64_t)b * BL + i;
+        s += (int32_t)(zp_code(row, bits, e) - zp) * (int32_t)xq[e];
+    }
+    return s;
+}
+
+/* out has (r1 - r0) * (cols / 128) entries, row-major. */
+void orc_block_sums_zp(int bits, const uint8_t *wq, const uint8_t *wzp, int32_t cols,
+                       const int8_t *xq, int32_t r0, int32_t r1, int32_t *out)
+{
+    int32_t nb = cols / BL;
+    for (int32_t r = r0; r < r1; ++r)
+        for (int32_t b = 0; b < nb; ++b)
+            out[(int64_t)(r - r0) * nb + b] = zp_block_sum(bits, wq, wzp, cols, xq, r, b);
+}
+
+void orc_matvec_zp(float *y, int bits, const uint8_t *wq, const float *wd,
+                   const uint8_t *wzp, int32_t cols, const int8_t *xq,
+                   const float *xd, int32_t r0, int32_t r1)
+{
+    int32_t nb = cols / BL;
+    for (int32_t r = r0; r < r1; ++r) {
+        float s = 0.0f;
+        for (int32_t b = 0; b < nb; ++b) {
+            int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);
+            float t = (float)sumi * wd[(int64_t)r * nb + b];
+            t = t * xd[b];
+            s = s + t;
+        }
+        y[r] = s;
+    }
+}
+
+/* A(r) = sum over blocks of |sumi * dw * dx| in binary64 (the scale of the
+ * tolerance |y - y_ref| <= 1e-5 * A + 1e-6). */
+void orc_tol_abs_zp(int bits, const uint8_t *wq, const float *wd, const uint8_t *wzp,
+                    int32_t cols, const int8_t *xq, const float *xd, int32_t r0,
+                    int32_t r1, double *out)
+{
+    int32_t nb = cols / BL;
+    for (int32_t r = r0; r < r1; ++r) {
+        double a = 0.0;
+        for (int32_t b = 0; b < nb; ++b) {
+            int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);
+            a += fabs((double)sumi * (double)wd[(int64_t)r * nb + b] * (double)xd[b]);
+        }
+        out[r - r0] = a;
     }
 }

@@ -442,6 +442,173 @@ def check_silu_mul():
     assert np.all(np.abs(o - o64) <= 6 * np.finfo(np.float32).eps * np.abs(o64) + 1e-37)
 
 
+# ---------------------------------------------------------------------------
+# Block length 128 with a zero point ("ONNX Runtime" page, sections 3 and 4;
+# the readings are listed in the oracle's C file)
+# ---------------------------------------------------------------------------
+
+BL = 128
+
+
+def zp_codes(bits, wq):
+    """[rows, K or K/2] uint8 -> [rows, K] int64 codes; 4 bits: element 2i
+    from the low nibble of byte i, element 2i + 1 from the high nibble."""
+    if bits == 8:
+        return wq.astype(np.int64)
+    lo = (wq & 0x0F).astype(np.int64)
+    hi = (wq >> 4).astype(np.int64)
+    return np.stack([lo, hi], axis=2).reshape(wq.shape[0], -1)
+
+
+def zp_values(bits, wq, wzp):
+    c = zp_codes(bits, wq)
+    rows, k = c.shape
+    z = np.full((rows, k // BL), 1 << (bits - 1), np.int64) if wzp is None else wzp.astype(np.int64)
+    return c - np.repeat(z, BL, axis=1)
+
+
+def _zp_problem(rng, bits, rows, k, with_zp=True):
+    nb = k // BL
+    wq = rng.integers(0, 256, size=(rows, k if bits == 8 else k // 2), dtype=np.uint8)
+    wzp = rng.integers(0, 1 << bits, size=(rows, nb), dtype=np.uint8) if with_zp else None
+    wd = (np.exp2(rng.uniform(-8, 0, size=(rows, nb))) * rng.uniform(0.5, 2, size=(rows, nb))).astype(np.float32)
+    xq, xd = orc.quantize_q8_b128(rng.standard_normal(k).astype(np.float32))
+    return wq, wd, wzp, xq, xd
+
+
+def check_b128_quantize():
+    rng = np.random.default_rng(30)
+    # every 32-sub-block carries the same largest magnitude: the rule on
+    # 128-element blocks gives the (pinned) Q8_0 codes and four equal scales
+    x = rng.uniform(-1, 1, size=512).astype(np.float32)
+    x[::32] = np.where(rng.random(16) < 0.5, -1.5, 1.5).astype(np.float32)
+    q, d = orc.quantize_q8_b128(x)
+    q8, d8 = orc.quantize_q8(x)
+    assert q.shape == (512,) and d.shape == (4,)
+    assert np.array_equal(q, q8) and np.array_equal(np.repeat(d, 4), d8)
+    # one scale per 128 elements: integers with a single 127 per block give
+    # id = 1 and q = x in every sub-block, where Q8_0 would rescale the others
+    x = rng.integers(-60, 61, size=256).astype(np.float32)
+    x[5] = 127.0
+    x[128 + 100] = -127.0
+    q, d = orc.quantize_q8_b128(x)
+    assert np.array_equal(q, x.astype(np.int8)) and np.array_equal(d, np.float32([1.0, 1.0]))
+    q8, _ = orc.quantize_q8(x)
+    assert not np.array_equal(q8, q)
+    # zero block
+    x[128:] = 0.0
+    q, d = orc.quantize_q8_b128(x)
+    assert d[1] == 0 and not np.any(q[128:])
+
+
+def check_zp_block_sum_closed_forms():
+    k = 256
+    x127 = np.full(k, 127, np.int8)
+    w = np.full((1, k), 255, np.uint8)
+    s = orc.block_sums_zp(8, w, np.zeros((1, 2), np.uint8), x127)
+    assert np.array_equal(s, [[128 * 255 * 127] * 2])                    # largest |sumi|, 8 bits
+    s = orc.block_sums_zp(8, np.zeros((1, k), np.uint8), None, x127)
+    assert np.array_equal(s, [[-128 * 128 * 127] * 2])                   # default zp = 128
+    s = orc.block_sums_zp(8, np.full((1, k), 128, np.uint8), None, x127)
+    assert not np.any(s)
+    zp = np.uint8([[17, 250]])
+    w = np.repeat(zp, BL, axis=1)
+    assert not np.any(orc.block_sums_zp(8, w, zp, x127))                 # codes equal to zp
+    w4 = np.full((1, k // 2), 0xFF, np.uint8)
+    s = orc.block_sums_zp(4, w4, np.zeros((1, 2), np.uint8), -x127)
+    assert np.array_equal(s, [[-128 * 15 * 127] * 2])
+    s = orc.block_sums_zp(4, np.zeros((1, k // 2), np.uint8), None, x127)
+    assert np.array_equal(s, [[-128 * 8 * 127] * 2])                     # default zp = 8
+    w4 = np.full((1, k // 2), 0x88, np.uint8)
+    assert not np.any(orc.block_sums_zp(4, w4, None, x127))
+
+
+def check_zp_nibble_order():
+    """One-hot activations read single elements: element 2i is the low
+    nibble of byte i, element 2i + 1 the high nibble."""
+    k = 128
+    b = np.arange(64, dtype=np.uint8)
+    w4 = ((b % 16) | ((15 - (b % 16)) << 4)).astype(np.uint8).reshape(1, 64)
+    zp = np.uint8([[3]])
+    for e in (0, 1, 2, 7, 64, 127):
+        x = np.zeros(k, np.int8)
+        x[e] = 1
+        s = orc.block_sums_zp(4, w4, zp, x)
+        byte = int(w4[0, e // 2])
+        want = ((byte & 0x0F) if e % 2 == 0 else (byte >> 4)) - 3
+        assert s[0, 0] == want, e
+
+
+def check_zp_reduces_to_symmetric():
+    """At the default zero point the values are those of the symmetric
+    formats: 8 bits, B - 128 = the int8 with the top bit flipped (Q8_0);
+    4 bits, nibble - 8 (Q4_0 after moving each element to its Q4_0 byte).
+    The sums over the four 32-sub-blocks equal the (pinned) Q8_0 / Q4_0
+    block sums."""
+    rng = np.random.default_rng(31)
+    rows, k = 3, 384
+    xq = rng.integers(-127, 128, size=k, dtype=np.int16).astype(np.int8)
+    B = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
+    s = orc.block_sums_zp(8, B, None, xq)
+    s8 = orc.block_sums(8, (B ^ 0x80).view(np.int8), xq)
+    assert np.array_equal(s, s8.reshape(rows, -1, 4).sum(axis=2))
+    w4 = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    nib = zp_codes(4, w4).reshape(rows, k // QK, QK)           # stored nibble per element
+    q40 = (nib[:, :, :16] | (nib[:, :, 16:] << 4)).astype(np.uint8).reshape(rows, k // 2)
+    s = orc.block_sums_zp(4, w4, None, xq)
+    s4 = orc.block_sums(4, q40, xq)
+    assert np.array_equal(s, s4.reshape(rows, -1, 4).sum(axis=2))
+
+
+def check_zp_block_sums_brute():
+    rng = np.random.default_rng(32)
+    for bits in (8, 4):
+        for with_zp in (True, False):
+            rows, k = 6, 128 * 5
+            wq, _, wzp, _, _ = _zp_problem(rng, bits, rows, k, with_zp)
+            xq = rng.integers(-128, 128, size=k, dtype=np.int16).astype(np.int8)
+            got = orc.block_sums_zp(bits, wq, wzp, xq)
+            v = zp_values(bits, wq, wzp).reshape(rows, k // BL, BL)
+            want = (v * xq.astype(np.int64).reshape(1, k // BL, BL)).sum(axis=2)
+            assert np.array_equal(got.astype(np.int64), want)
+            assert np.array_equal(orc.block_sums_zp(bits, wq, wzp, xq, 1, 4).astype(np.int64), want[1:4])
+
+
+def check_zp_matvec_brute64():
+    rng = np.random.default_rng(33)
+    for bits in (8, 4):
+        for rows, k in ((1, 128), (7, 384), (3, 128 * 38)):
+            wq, wd, wzp, xq, xd = _zp_problem(rng, bits, rows, k, with_zp=(rows != 3))
+            y = orc.matvec_zp(bits, wq, wd, wzp, xq, xd)
+            v = zp_values(bits, wq, wzp)
+            nb = k // BL
+            wdeq = (v.reshape(rows, nb, BL) * wd.astype(np.float64)[:, :, None]).reshape(rows, k)
+            xdeq = (xq.astype(np.float64).reshape(nb, BL) * xd.astype(np.float64)[:, None]).reshape(k)
+            y64 = wdeq @ xdeq
+            sums = (v.reshape(rows, nb, BL) * xq.astype(np.int64).reshape(1, nb, BL)).sum(axis=2)
+            a64 = np.abs(sums * wd.astype(np.float64) * xd.astype(np.float64)[None, :]).sum(axis=1)
+            assert np.all(np.abs(y.astype(np.float64) - y64) <= 1e-5 * a64 + 1e-6), "fp64 brute force"
+            assert np.allclose(orc.tolerance_zp(bits, wq, wd, wzp, xq, xd), 1e-5 * a64 + 1e-6, rtol=1e-12, atol=0)
+
+
+def check_zp_matvec_unit_scales():
+    """dw = dx = 1: y is the exact sum of the block sums; rows outside
+    [r0, r1) keep their value."""
+    rng = np.random.default_rng(34)
+    for bits in (8, 4):
+        rows, k = 5, 128 * 6
+        wq, _, wzp, _, _ = _zp_problem(rng, bits, rows, k)
+        xq = rng.integers(-20, 21, size=k, dtype=np.int16).astype(np.int8)
+        ones_w = np.ones((rows, k // BL), np.float32)
+        ones_x = np.ones(k // BL, np.float32)
+        want = (zp_values(bits, wq, wzp) * xq.astype(np.int64)).sum(axis=1)
+        assert np.abs(want).max() < 2 ** 24
+        y = orc.matvec_zp(bits, wq, ones_w, wzp, xq, ones_x)
+        assert np.array_equal(y.astype(np.int64), want)
+        y = orc.matvec_zp(bits, wq, ones_w, wzp, xq, ones_x, 1, 3, y=np.full(rows, -7.5, np.float32))
+        assert np.all(y[[0, 3, 4]] == -7.5) and np.array_equal(y[1:3].astype(np.int64), want[1:3])
+
+
 ALL_CHECKS = [
     check_q8_zero_block, check_q8_equal_block, check_q8_clamp_and_range,
     check_q8_unit_scale_textbook, check_q8_ties, check_q8_detectors,
@@ -452,6 +619,9 @@ ALL_CHECKS = [
     check_gemm_rows,
     check_sumsq_pairwise_order, check_rmsnorm_closed_forms, check_rmsnorm_invariants_and_brute,
     check_silu_mul,
+    check_b128_quantize, check_zp_block_sum_closed_forms, check_zp_nibble_order,
+    check_zp_reduces_to_symmetric, check_zp_block_sums_brute, check_zp_matvec_brute64,
+    check_zp_matvec_unit_scales,
 ]
 
 

@@ -53,6 +53,20 @@ MUTANTS = [
     ("silu_no_gate", "o[j] = v * u[j];", "o[j] = v;", 1),
     ("silu_sigmoid_only", "v = v * s;\n        o[j] = v * u[j];", "v = s;\n        o[j] = v * u[j];", 1),
     ("rms_weight_shift", "o[j] = w[j] * (inv * x[j]);", "o[j] = w[(j + 1) % n] * (inv * x[j]);", 1),
+    ("b128_max_first_32", "for (int i = 0; i < BL; ++i) {\n            float a = fabsf(xb[i]);",
+     "for (int i = 0; i < 32; ++i) {\n            float a = fabsf(xb[i]);", 1),
+    ("b128_scale_128", "float db = amax / 127.0f;\n        float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;\n        for (int i = 0; i < BL; ++i) {",
+     "float db = amax / 128.0f;\n        float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;\n        for (int i = 0; i < BL; ++i) {", 1),
+    ("zp_dropped", "s += (int32_t)(zp_code(row, bits, e) - zp) * (int32_t)xq[e];", "s += (int32_t)zp_code(row, bits, e) * (int32_t)xq[e];", 1),
+    ("zp_default_127", "return 1 << (bits - 1);", "return (1 << (bits - 1)) - 1;", 1),
+    ("zp_nibbles_swapped", "return (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);", "return (i % 2 == 0) ? (byte >> 4) : (byte & 0x0F);", 1),
+    ("zp_nibbles_halves", "uint8_t byte = row[i / 2];\n    return (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+     "uint8_t byte = row[(i / 128) * 64 + (i % 64)];\n    return (i % 128 < 64) ? (byte & 0x0F) : (byte >> 4);", 1),
+    ("zp_q4_row_stride", "const uint8_t *row = wq + (int64_t)r * (bits == 8 ? cols : cols / 2);", "const uint8_t *row = wq + (int64_t)r * cols / 2;", 1),
+    ("zp_per_block_only", "return wzp[(int64_t)r * nb + b];", "return wzp[b];", 1),
+    ("zp_sign", "s += (int32_t)(zp_code(row, bits, e) - zp) * (int32_t)xq[e];", "s += (int32_t)(zp - zp_code(row, bits, e)) * (int32_t)xq[e];", 1),
+    ("zp_acc_skips_last", "for (int32_t b = 0; b < nb; ++b) {\n            int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);\n            float t",
+     "for (int32_t b = 0; b + 1 < nb; ++b) {\n            int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);\n            float t", 1),
 ]
 
 
