@@ -1,0 +1,325 @@
+// kernels_zp.hip -- the decode matvec on 128-element blocks with a zero
+// point (gfx950).
+//
+// What is computed ("ONNX Runtime" page, section 3 "Match real exports --
+// BlkLen=128 CompInt8" and section 4 "SQ8Bit"): weights are unsigned codes
+// B (one byte, or one nibble: element 2i in the low nibble of byte i,
+// 2i + 1 in the high nibble) with an fp32 scale dw and a zero point zp per
+// 128-element block (a null zp array means 2^(bits-1)); the float
+// activation is quantized to int8 per 128-element block with the Q8_0 rule
+// of the Legacy-ISA ML Inference Runtime -- Design Spec (section 4 "Q8
+// quantization", section 5 rounding), and
+//   y[r] = sum over blocks b of sumi(r, b) * dw(r, b) * dx(b),
+//   sumi = sum over the block of (B - zp) * q, exact in int32.
+// gfx950 has no signed x unsigned byte dot, so sumi is evaluated through the
+// page's identity: with B' = B - 128 (the code with its top bit flipped, a
+// signed byte), sumi = sum B' q - (zp - 128) * sum q; 4-bit codes are
+// already non-negative bytes, so sumi = sum B q - zp * sum q.  sum q is
+// computed once per block when the activation is quantized.
+//
+// Work layout.  One workgroup of 8 wavefronts per compute unit.
+//   Phase A: the workgroup quantizes the whole activation into LDS (one
+//   wavefront per 128-element block, 2 elements per lane), with the block
+//   scales and the block sums of the quants.  For 4-bit weights the quants
+//   of each 8-element group are stored as (x0, x2, x4, x6, x1, x3, x5, x7),
+//   so that the masked low and high nibbles of a weight dword meet their
+//   activation bytes in one v_dot4 each.
+//   Phase B: groups of L lanes (L = 16, 32 or 64) stream whole weight rows:
+//   lane c of a group reads 16-byte chunk c, c + L, ... of the row (J
+//   chunks per window, double-buffered in registers, non-temporal), so the
+//   LB = 8 (8-bit) or 4 (4-bit) lanes of one block are adjacent.  Their
+//   partial dots are added by DPP within the block's lanes, giving the exact
+//   block sum in every lane; the block is scaled in fp32 and added to the
+//   lane's slot accumulator in ascending block order; at the end of a row
+//   the slots are added by a fixed butterfly and the group's first lane
+//   writes y.  The result does not depend on timing.
+//
+// Every variable part of an address is in the range-checked offset of a raw
+// buffer load: chunks past the row, and rows past r1, read zeros and are
+// not used.
+#include <stdio.h>
+
+#include "launch.h"
+
+namespace qmv {
+namespace {
+
+typedef int v4i_zp __attribute__((ext_vector_type(4)));
+
+constexpr int BLK = 128;               // elements per block
+constexpr int kWpb = 8;                // wavefronts per workgroup
+constexpr int kOOBz = 0x7FFFFFF0;      // an offset beyond every descriptor range used here
+constexpr int kBufFlagsZ = 0x00020000; // buffer descriptor word 3: raw 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kBufFlagsZ);
+}
+
+// The Q8_0 rounding of one element (spec section 5): v = x * id,
+// t = v + copysign(0.5, x), q = trunc(t), each operation rounded on its own.
+__device__ __forceinline__ int q8_round(float x, float id) {
+#pragma clang fp contract(off)
+    float v = x * id;
+    float t = v + copysignf(0.5f, x);
+    int q = (int)t;
+    return min(max(q, -127), 127);
+}
+
+__device__ __forceinline__ float wave_max(float a) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    return a;
+}
+
+__device__ __forceinline__ int wave_sum(int a) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+    return a;
+}
+
+// Quantize 128-element block b of x (one wavefront, lane l holding elements
+// 2l and 2l + 1).  Returns the two quants; d and qsum are wave-uniform.
+__device__ __forceinline__ void quant_block128(const float *x, int b, int lane, int &q0, int &q1, float &d,
+                                               int &qsum) {
+    const float2 v = *reinterpret_cast<const float2 *>(x + (int64_t)b * BLK + 2 * lane);
+    const float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
+    d = amax / 127.0f;
+    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
+    q0 = q8_round(v.x, id);
+    q1 = q8_round(v.y, id);
+    qsum = wave_sum(q0 + q1);
+}
+
+// position of element e of a block in the 4-bit activation order
+__device__ __forceinline__ int perm4(int e) { return (e & ~7) + ((e & 1) << 2) + ((e & 7) >> 1); }
+
+__device__ __forceinline__ int dpp_x1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_x2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_m8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+
+template <int BITS, int L, int J>
+__global__ void __launch_bounds__(64 * kWpb)
+k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restrict__ wd,
+     const uint8_t *__restrict__ wzp, int32_t rows, int32_t K, const float *__restrict__ x,
+     int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1) {
+    constexpr int LB = BITS == 8 ? 8 : 4;  // lanes (16-byte chunks) per block
+    constexpr int GPW = 64 / L;            // row groups per wavefront
+    static_assert(L >= LB && (L & (L - 1)) == 0 && L <= 64, "group size");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nb = K / BLK;
+    int8_t *xs = reinterpret_cast<int8_t *>(smem);
+    float *sd = reinterpret_cast<float *>(smem + K);
+    int *sq = reinterpret_cast<int *>(smem + K + 4 * nb);
+
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+
+    // ---- phase A: the activation, quantized into LDS
+    for (int b = wid; b < nb; b += kWpb) {
+        int q0, q1, qs;
+        float d;
+        quant_block128(x, b, lane, q0, q1, d, qs);
+        const int e = 2 * lane;
+        if constexpr (BITS == 8) {
+            *reinterpret_cast<short *>(xs + b * BLK + e) = (short)((q0 & 0xFF) | (q1 << 8));
+        } else {
+            xs[b * BLK + perm4(e)] = (int8_t)q0;
+            xs[b * BLK + perm4(e + 1)] = (int8_t)q1;
+        }
+        if (lane == 0) {
+            sd[b] = d;
+            sq[b] = qs;
+        }
+        if (xq_out != nullptr && blockIdx.x == 0) {
+            *reinterpret_cast<short *>(xq_out + (int64_t)b * BLK + e) = (short)((q0 & 0xFF) | (q1 << 8));
+            if (lane == 0) xd_out[b] = d;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase B: rows
+    const int row_bytes = BITS == 8 ? K : K / 2;
+    const int chunks = row_bytes >> 4;
+    const int W = (chunks + L * J - 1) / (L * J);  // windows per row
+    const int gl = lane & (L - 1);
+    const int G = gridDim.x * kWpb * GPW;               // row groups in the grid
+    const int g0 = (blockIdx.x * kWpb + wid) * GPW;     // this wavefront's first group
+    const int g = g0 + lane / L;
+    const int nrow = r1 - r0;
+    const int rows_g = g < nrow ? (nrow - g + G - 1) / G : 0;
+    const int rows_w = g0 < nrow ? (nrow - g0 + G - 1) / G : 0;  // the wavefront's first group has the most
+    const int items = rows_w * W;                                // wave-uniform loop count
+
+    const __amdgpu_buffer_rsrc_t rq = rsrc(wq, (int64_t)rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t rd = rsrc(wd, (int64_t)rows * nb * 4);
+    const __amdgpu_buffer_rsrc_t rz = rsrc(wzp, wzp != nullptr ? (int64_t)rows * nb : 0);
+    const int zdef = 1 << (BITS - 1);
+    constexpr int off = BITS == 8 ? 128 : 0;  // bias of the dotted codes
+
+    struct Buf {
+        v4i_zp w[J];
+        float dw[J];
+        int zp[J];
+    };
+    auto load = [&](Buf &bf, int t) __attribute__((always_inline)) {
+        const int rl = t / W, win = t - rl * W;
+        const bool live = rl < rows_g;
+        const int r = r0 + g + rl * G;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = (win * J + j) * L + gl;  // chunk of the row
+            const bool ok = live && c < chunks;
+            const int b = c / LB;
+            bf.w[j] = __builtin_bit_cast(
+                v4i_zp, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? r * row_bytes + 16 * c : kOOBz, 0, 2));
+            bf.dw[j] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (r * nb + b) : kOOBz, 0, 0));
+            if (wzp != nullptr)
+                bf.zp[j] = (int)__builtin_amdgcn_raw_buffer_load_b8(rz, ok ? r * nb + b : kOOBz, 0, 0);
+            else
+                bf.zp[j] = zdef;
+        }
+    };
+
+    float acc = 0.0f;
+    auto compute = [&](const Buf &bf, int t) __attribute__((always_inline)) {
+        const int rl = t / W, win = t - rl * W;
+        const bool live = rl < rows_g;
+        if (win == 0) acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = (win * J + j) * L + gl;
+            const bool ok = live && c < chunks;
+            const int b = ok ? c / LB : 0;
+            const int sub = c % LB;
+            int p = 0;
+            if constexpr (BITS == 8) {
+                const v4i_zp xv = *reinterpret_cast<const v4i_zp *>(xs + b * BLK + 16 * sub);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) p = __builtin_amdgcn_sdot4(bf.w[j][k] ^ (int)0x80808080, xv[k], p, false);
+            } else {
+                const v4i_zp xe = *reinterpret_cast<const v4i_zp *>(xs + b * BLK + 32 * sub);
+                const v4i_zp xo = *reinterpret_cast<const v4i_zp *>(xs + b * BLK + 32 * sub + 16);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // dword k covers elements 8k .. 8k + 7 of the chunk: even ones in the
+                    // low nibbles, odd ones in the high nibbles
+                    const int lo = bf.w[j][k] & 0x0F0F0F0F, hi = (bf.w[j][k] >> 4) & 0x0F0F0F0F;
+                    const int xe_k = k < 2 ? xe[2 * k] : xo[2 * k - 4];
+                    const int xo_k = k < 2 ? xe[2 * k + 1] : xo[2 * k - 3];
+                    p = __builtin_amdgcn_sdot4(lo, xe_k, p, false);
+                    p = __builtin_amdgcn_sdot4(hi, xo_k, p, false);
+                }
+            }
+            // exact block sum in every lane of the block
+            p += dpp_x1(p);
+            p += dpp_x2(p);
+            if constexpr (LB == 8) p += dpp_m8(p);
+            if (ok) {
+#pragma clang fp contract(off)
+                const int sumi = p - (bf.zp[j] - off) * sq[b];
+                float tt = (float)sumi * bf.dw[j];
+                tt = tt * sd[b];
+                acc = acc + tt;
+            }
+        }
+        if (win == W - 1) {
+            float s = acc;
+#pragma unroll
+            for (int o = LB; o < L; o <<= 1) s += __shfl_xor(s, o);
+            if (live && gl == 0) y[r0 + g + rl * G] = s;
+        }
+    };
+
+    Buf b0, b1;
+    load(b0, 0);
+    for (int t = 0; t < items; t += 2) {
+        load(b1, t + 1);
+        compute(b0, t);
+        if (t + 1 < items) {
+            load(b0, t + 2);
+            compute(b1, t + 1);
+        }
+    }
+}
+
+template <int BITS, int L, int J>
+hipError_t launch_cfg(const ZpArgs &a, int grid, size_t lds, hipStream_t s, const char **name) {
+    auto kern = k_zp<BITS, L, J>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWpb), lds, s, a.y, a.wq, a.wd, a.wzp, a.rows, a.K, a.x,
+                       a.xq_out, a.xd_out, a.r0, a.r1);
+    static char kname[48];
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "zp%d_l%d_j%d", BITS, L, J);
+    *name = kname;
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
+    const int chunks = (BITS == 8 ? a.K : a.K / 2) / 16;
+    const size_t lds = (size_t)a.K + 8 * (size_t)(a.K / BLK);
+    // lanes per row: the fewest power of two (16 .. 64) that covers a row
+    int L = 64;
+    if (chunks <= 16) L = 16;
+    else if (chunks <= 32) L = 32;
+    const int nrow = a.r1 - a.r0;
+    const int groups_per_wg = kWpb * (64 / L);
+    int grid = (nrow + groups_per_wg - 1) / groups_per_wg;
+    if (grid > num_cu) grid = num_cu;
+    if (grid < 1) grid = 1;
+    if (L == 16) return launch_cfg<BITS, 16, 1>(a, grid, lds, s, name);
+    if (L == 32) return launch_cfg<BITS, 32, 1>(a, grid, lds, s, name);
+    // L = 64: J chunks per lane per window, at most 8, windows as even as possible
+    const int win = (chunks + 64 * 8 - 1) / (64 * 8);
+    const int J = (chunks + 64 * win - 1) / (64 * win);
+    switch (J) {
+        case 1: return launch_cfg<BITS, 64, 1>(a, grid, lds, s, name);
+        case 2: return launch_cfg<BITS, 64, 2>(a, grid, lds, s, name);
+        case 3: return launch_cfg<BITS, 64, 3>(a, grid, lds, s, name);
+        case 4: return launch_cfg<BITS, 64, 4>(a, grid, lds, s, name);
+        case 5: return launch_cfg<BITS, 64, 5>(a, grid, lds, s, name);
+        case 6: return launch_cfg<BITS, 64, 6>(a, grid, lds, s, name);
+        case 7: return launch_cfg<BITS, 64, 7>(a, grid, lds, s, name);
+        default: return launch_cfg<BITS, 64, 8>(a, grid, lds, s, name);
+    }
+}
+
+__global__ void __launch_bounds__(256)
+k_quant_b128(int8_t *__restrict__ q, float *__restrict__ d, const float *__restrict__ x, int64_t nblk) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * 256) >> 6;
+    for (int64_t b = w0; b < nblk; b += nw) {  // one wavefront per block
+        int q0, q1, qs;
+        float dd;
+        quant_block128(x + b * BLK, 0, lane, q0, q1, dd, qs);
+        *reinterpret_cast<short *>(q + b * BLK + 2 * lane) = (short)((q0 & 0xFF) | (q1 << 8));
+        if (lane == 0) d[b] = dd;
+    }
+}
+
+}  // namespace
+
+size_t zp_lds_bytes(int32_t K) { return (size_t)K + 8 * (size_t)(K / BLK); }
+
+hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
+    if (a.K % BLK != 0 || zp_lds_bytes(a.K) > 160 * 1024) return hipErrorNotSupported;
+    return a.bits == 8 ? launch_bits<8>(a, num_cu, s, name) : launch_bits<4>(a, num_cu, s, name);
+}
+
+hipError_t launch_quant_b128(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name) {
+    int64_t g = (nblk + 3) / 4;
+    if (g > 4096) g = 4096;
+    if (g < 1) g = 1;
+    hipLaunchKernelGGL(k_quant_b128, dim3((unsigned)g), dim3(256), 0, s, q, d, x, nblk);
+    *name = "quant_q8_b128";
+    return hipGetLastError();
+}
+
+}  // namespace qmv

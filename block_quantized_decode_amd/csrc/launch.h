@@ -57,6 +57,23 @@ constexpr int kGemmMaxRows = 64;  // activation rows per matrix-core launch
 // dimension split over its wavefronts (num_cu sizes the row tiles).
 hipError_t launch_mm(const GemmArgs &a, int num_cu, hipStream_t s, const char **name);
 
+// The matvec on 128-element blocks with a zero point (kernels_zp.hip).
+struct ZpArgs {
+    int bits;                  // 4 or 8
+    float *y;
+    const uint8_t *wq;         // codes, rows x K (8 bits) or rows x K/2 (4 bits)
+    const float *wd;           // rows x K/128
+    const uint8_t *wzp;        // rows x K/128, or null: 2^(bits-1)
+    int32_t rows, K;
+    const float *x;            // float32 activation, K
+    int8_t *xq_out;            // optional: the quantized activation (K) ...
+    float *xd_out;             // ... and its scales (K/128)
+    int32_t r0, r1;
+};
+size_t zp_lds_bytes(int32_t K);
+hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name);
+hipError_t launch_quant_b128(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name);
+
 // Pack-once layout of Q4_0 / Q8_0 weights for the matrix-core product (units
 // of 16 rows x 4 blocks in the A operand's lane order): sizes in bytes of the
 // packed quants and scales, and the packing launch (a pure permutation).

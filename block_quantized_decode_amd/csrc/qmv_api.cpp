@@ -217,6 +217,43 @@ qmv_status gemm_packed(int qtype, float *Y, const qmv_packed *P, const qmv_qtens
     return gemm_passes(qtype, Y, nullptr, nullptr, P->q, P->d, P->rows, P->cols, X, r0, r1, dev, stream);
 }
 
+qmv_status matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qact *xq_out, int32_t r0, int32_t r1,
+                        void *stream) {
+    if (W == nullptr || W->q == nullptr || W->d == nullptr || x == nullptr || y == nullptr) return QMV_E_ARG;
+    if (W->bits != 4 && W->bits != 8) return QMV_E_FORMAT;
+    if (W->rows < 0 || W->cols <= 0 || (W->cols % QMV_ZP_BLOCK) != 0 || W->cols > QMV_ZP_MAX_COLS)
+        return QMV_E_SHAPE;
+    const int64_t row_bytes = W->bits == 8 ? W->cols : W->cols / 2;
+    if ((int64_t)W->rows * row_bytes > INT32_MAX) return QMV_E_SHAPE;
+    if (r0 < 0 || r1 > W->rows || r0 > r1) return QMV_E_SHAPE;
+    if (!aligned(W->q, 16) || !aligned(W->d, 4) || !aligned(x, 16) || !aligned(y, 4)) return QMV_E_ARG;
+    if (xq_out != nullptr && (xq_out->q == nullptr || xq_out->d == nullptr || !aligned(xq_out->q, 16) ||
+                              !aligned(xq_out->d, 4)))
+        return QMV_E_ARG;
+    int dev = -1;
+    qmv_status st = device_check(&dev);
+    if (st != QMV_OK) return st;
+    if (xq_out != nullptr) xq_out->n = W->cols;
+    if (r0 == r1 && xq_out == nullptr) return QMV_OK;
+    qmv::ZpArgs a = {};
+    a.bits = W->bits;
+    a.y = y;
+    a.wq = W->q;
+    a.wd = W->d;
+    a.wzp = W->zp;
+    a.rows = W->rows;
+    a.K = W->cols;
+    a.x = x;
+    a.xq_out = xq_out != nullptr ? xq_out->q : nullptr;
+    a.xd_out = xq_out != nullptr ? xq_out->d : nullptr;
+    a.r0 = r0;
+    a.r1 = r1;
+    const char *name = "";
+    const int ncu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+    hipError_t e = qmv::launch_zp(a, ncu, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)(r1 - r0));
+}
+
 // ceil(M / 64) matrix-core passes over the weights (row-major wq / wd, or
 // packed pq / pd)
 qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, const void *pq, const float *pd,
@@ -333,6 +370,29 @@ qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int
 qmv_status qmv_gemm_q4(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
                        void *stream) {
     return gemm(QMV_Q4_0, Y, W, X, r0, r1, stream);
+}
+
+qmv_status qmv_quantize_q8_b128(qmv_qact *out, const float *x, int64_t k, void *stream) {
+    if (out == nullptr) return QMV_E_ARG;
+    if (k < 0 || (k % QMV_ZP_BLOCK) != 0 || k > INT32_MAX) return QMV_E_SHAPE;
+    if (k == 0) {
+        out->n = 0;
+        return QMV_OK;
+    }
+    if (out->q == nullptr || out->d == nullptr || x == nullptr) return QMV_E_ARG;
+    if (!aligned(x, 16) || !aligned(out->q, 16) || !aligned(out->d, 4)) return QMV_E_ARG;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    out->n = (int32_t)k;
+    const char *name = "";
+    hipError_t e =
+        qmv::launch_quant_b128(out->q, out->d, x, k / QMV_ZP_BLOCK, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)(k / QMV_ZP_BLOCK));
+}
+
+qmv_status qmv_matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qact *xq, int32_t r0, int32_t r1,
+                            void *stream) {
+    return matvec_zp_fx(y, W, x, xq, r0, r1, stream);
 }
 
 qmv_status qmv_pack_bytes(int32_t type, int32_t rows, int32_t cols, int64_t *q_bytes, int64_t *d_bytes) {

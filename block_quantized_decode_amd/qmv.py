@@ -43,6 +43,11 @@ class QAct(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("n", ctypes.c_int32)]
 
 
+class ZpTensor(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("zp", ctypes.c_void_p), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("bits", ctypes.c_uint8)]
+
+
 class Packed(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("rows", ctypes.c_int32),
                 ("cols", ctypes.c_int32), ("type", ctypes.c_uint8)]
@@ -74,6 +79,8 @@ _SIGS = {
     "qmv_pack_weights": [ctypes.POINTER(Packed), ctypes.POINTER(QTensor), _P],
     "qmv_gemm_q8_packed": [_P, ctypes.POINTER(Packed), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_gemm_q4_packed": [_P, ctypes.POINTER(Packed), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_quantize_q8_b128": [ctypes.POINTER(QAct), _P, ctypes.c_int64, _P],
+    "qmv_matvec_zp_fx": [_P, ctypes.POINTER(ZpTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_device_check": [],
 }
 
@@ -356,6 +363,51 @@ def qmv_gemm_q4_packed(P: PackedWeights, xq, xd, r0=None, r1=None, Y=None):
     return _gemm_packed(QMV_Q4_0, "qmv_gemm_q4_packed", P, xq, xd, r0, r1, Y)
 
 
+ZP_BLOCK = 128
+
+
+def zptensor(q: torch.Tensor, d: torch.Tensor, zp: torch.Tensor | None, bits: int) -> ZpTensor:
+    """Describe a device matrix of the 128-block zero-point format: q uint8
+    [rows, K] (bits 8) or [rows, K/2] (bits 4), d float32 [rows, K/128], zp
+    uint8 [rows, K/128] or None."""
+    _dev(q, (torch.uint8, torch.int8))
+    _dev(d, torch.float32)
+    if zp is not None:
+        _dev(zp, (torch.uint8, torch.int8))
+    rows = d.shape[0]
+    cols = d.shape[-1] * ZP_BLOCK
+    return ZpTensor(q.data_ptr(), d.data_ptr(), None if zp is None else zp.data_ptr(), rows, cols, bits)
+
+
+def qmv_quantize_q8_b128(x: torch.Tensor):
+    """The Q8_0 rule on 128-element blocks: (q int8 like x, d float32 [..., K/128])."""
+    _dev(x, torch.float32)
+    q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    d = torch.empty(x.shape[:-1] + (x.shape[-1] // ZP_BLOCK,), dtype=torch.float32, device=x.device)
+    act = QAct(q.data_ptr(), d.data_ptr(), 0)
+    _check(lib().qmv_quantize_q8_b128(ctypes.byref(act), x.data_ptr(), x.numel(), _stream()), "qmv_quantize_q8_b128")
+    return q, d
+
+
+def qmv_matvec_zp_fx(wq, wd, wzp, bits, x, r0=None, r1=None, y=None, xq_out=None):
+    """y = W q8_b128(x) on the 128-block zero-point format (see include/qmv.h)."""
+    W = zptensor(wq, wd, wzp, bits)
+    _dev(x, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    if y is None:
+        y = torch.zeros(W.rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32)
+    act = None
+    if xq_out is not None:
+        q, d = xq_out
+        act = QAct(_dev(q, torch.int8).data_ptr(), _dev(d, torch.float32).data_ptr(), 0)
+    code = lib().qmv_matvec_zp_fx(y.data_ptr(), ctypes.byref(W), x.data_ptr(),
+                                  ctypes.byref(act) if act is not None else None, r0, r1, _stream())
+    _check(code, "qmv_matvec_zp_fx")
+    return y
+
+
 class Prepared:
     """A libqmv call with its arguments marshalled once: calling it costs one
     ctypes call (on the stream current at preparation time unless another
@@ -451,3 +503,14 @@ def prepare_gemm_packed(P: PackedWeights, xq, xd, Y, r0=None, r1=None, stream=No
     fname = "qmv_gemm_q4_packed" if P.qtype == QMV_Q4_0 else "qmv_gemm_q8_packed"
     args = [Y.data_ptr(), ctypes.byref(P.desc), ctypes.byref(X), r0, r1]
     return Prepared(fname, args, [P, X, xq, xd, Y], stream)
+
+
+def prepare_matvec_zp_fx(wq, wd, wzp, bits, x, y, r0=None, r1=None, stream=None) -> Prepared:
+    """Prepared qmv_matvec_zp_fx."""
+    W = zptensor(wq, wd, wzp, bits)
+    _dev(x, torch.float32)
+    _dev(y, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), None, r0, r1]
+    return Prepared("qmv_matvec_zp_fx", args, [W, wq, wd, wzp, x, y], stream)

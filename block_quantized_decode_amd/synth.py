@@ -207,6 +207,16 @@ def raw_q8(rng: np.random.Generator, rows: int, cols: int, lo: int = -127, hi: i
     return q, d
 
 
+def raw_zp(rng: np.random.Generator, bits: int, rows: int, cols: int, with_zp: bool = True, block: int = 128):
+    """Uniform random storage of the 128-block zero-point format: codes over
+    every value (bytes 0..255, or both nibbles 0..15), zero points uniform
+    over the code range (or None), scales as raw_q4."""
+    q = rng.integers(0, 256, size=(rows, cols if bits == 8 else cols // 2), dtype=np.uint8)
+    zp = rng.integers(0, 1 << bits, size=(rows, cols // block), dtype=np.uint8) if with_zp else None
+    d = raw_scales(rng, (rows, cols // block))
+    return q, d, zp
+
+
 def raw_scales(rng: np.random.Generator, shape):
     e = rng.uniform(-8.0, 0.0, size=shape)
     u = rng.uniform(0.5, 2.0, size=shape)

@@ -234,6 +234,47 @@ qmv_status qmv_gemm_q4(float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
                        int32_t r0, int32_t r1, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Exported-model format: 128-element blocks with a zero point ("ONNX
+ * Runtime" page, section 3 "Match real exports -- BlkLen=128 CompInt8" and
+ * section 4 "SQ8Bit").  A weight is (code - zp) * scale:
+ *   q  : codes, rows x cols bytes (bits = 8) or rows x cols/2 bytes
+ *        (bits = 4: element 2i in the low nibble of byte i, 2i + 1 in the
+ *        high nibble), row-major, 16-byte aligned;
+ *   d  : rows x cols/128 float32 scales, row-major, 4-byte aligned;
+ *   zp : rows x cols/128 zero points, one byte each (for bits = 4 only the
+ *        values 0..15 make sense, but any byte is taken as given), or NULL
+ *        for the midpoint 2^(bits-1) (128 or 8).
+ * ------------------------------------------------------------------------- */
+#define QMV_ZP_BLOCK 128
+#define QMV_ZP_MAX_COLS 65536
+
+typedef struct {
+    uint8_t *q;
+    float *d;
+    uint8_t *zp;
+    int32_t rows;
+    int32_t cols;
+    uint8_t bits;      /* 4 or 8 */
+} qmv_zptensor;
+
+/* The Q8_0 rule of qmv_quantize_q8 applied to 128-element blocks (the
+ * activation format of this product): out->q = k bytes, out->d = k/128
+ * floats.  k % 128 == 0; otherwise as qmv_quantize_q8. */
+qmv_status qmv_quantize_q8_b128(qmv_qact *out, const float *x, int64_t k, void *stream);
+
+/* y[r] = sum over 128-element blocks b of sumi(r, b) * d(r, b) * dx(b) for r
+ * in [r0, r1), sumi = sum over the block of (code - zp) * q exact in int32,
+ * with (q, dx) the 128-block Q8_0 quantization of the float32 activation x
+ * (W->cols floats, 16-byte aligned), done inside the kernel.  If xq is not
+ * NULL it receives that quantized activation (q: cols bytes, 16-byte
+ * aligned; d: cols/128 floats) and xq->n = cols.  Other entries of y are not
+ * written.  Limits: cols % 128 == 0, cols <= QMV_ZP_MAX_COLS, rows * (bytes
+ * per row) <= INT32_MAX.  Errors: QMV_E_ARG (null or misaligned pointers),
+ * QMV_E_FORMAT (bits not 4 or 8), QMV_E_SHAPE (sizes, row range). */
+qmv_status qmv_matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qact *xq,
+                            int32_t r0, int32_t r1, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Pack-once weight layout for the matrix-core product.  The spec stores
  * weights row-major (section 4 table); its companion write-ups on
  * block-quantized products re-lay the weights once, ahead of time, into the

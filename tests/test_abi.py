@@ -50,6 +50,7 @@ def test_header_declares_the_product_calls():
               "qmv_matvec_q8_fx_rmsnorm", "qmv_matvec_q4_fx_rmsnorm",
               "qmv_matvec_q8_fx_silu_mul", "qmv_matvec_q4_fx_silu_mul",
               "qmv_pack_bytes", "qmv_pack_weights", "qmv_gemm_q8_packed", "qmv_gemm_q4_packed",
+              "qmv_quantize_q8_b128", "qmv_matvec_zp_fx",
               "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
         assert n in names
 
@@ -205,6 +206,42 @@ def test_gemm_packed_validation(lib, fn, t):
     assert lib.qmv_pack_weights(ctypes.byref(P), ctypes.byref(_w(t=t, cols=33)), None) == E_SHAPE
 
 
+class ZT(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("zp", ctypes.c_void_p), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("bits", ctypes.c_uint8)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matvec_zp_validation(lib, bits):
+    f = lib.qmv_matvec_zp_fx
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    Wz = ZT(A, B, A + 0x8000, 8, 256, bits)
+    X = A + 0x1000
+    assert f(None, ctypes.byref(Wz), X, None, 0, 8, None) == E_ARG
+    assert f(Y, None, X, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(Wz), None, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(ZT(0, B, 0, 8, 256, bits)), X, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(ZT(A, B, 0, 8, 256, 5)), X, None, 0, 8, None) == E_FORMAT
+    for cols in (0, 64, 200, 65536 + 128):
+        assert f(Y, ctypes.byref(ZT(A, B, 0, 8, cols, bits)), X, None, 0, 8, None) == E_SHAPE, cols
+    big = (1 << 31) // (65536 if bits == 8 else 32768) + 1   # rows * row bytes past INT32_MAX
+    assert f(Y, ctypes.byref(ZT(A, B, 0, big, 65536, bits)), X, None, 0, 8, None) == E_SHAPE
+    assert f(Y, ctypes.byref(Wz), X, None, 0, 9, None) == E_SHAPE
+    assert f(Y, ctypes.byref(Wz), X, None, 5, 4, None) == E_SHAPE
+    assert f(Y, ctypes.byref(ZT(A + 8, B, 0, 8, 256, bits)), X, None, 0, 8, None) == E_ARG   # q 16-aligned
+    assert f(Y, ctypes.byref(Wz), X + 8, None, 0, 8, None) == E_ARG                         # x 16-aligned
+    act = QA(A + 8, B, 0)
+    assert f(Y, ctypes.byref(Wz), X, ctypes.byref(act), 0, 8, None) == E_ARG
+    g = lib.qmv_quantize_q8_b128
+    g.argtypes = [P, P, ctypes.c_int64, P]
+    act = QA(A, B, 0)
+    assert g(ctypes.byref(act), Y, 96, None) == E_SHAPE
+    assert g(None, Y, 128, None) == E_ARG
+    empty = QA(0, 0, 7)
+    assert g(ctypes.byref(empty), None, 0, None) == OK and empty.n == 0
+
+
 def test_quantize_validation(lib):
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(None, ctypes.c_void_p(Y), ctypes.c_int64(64), None) == E_ARG
@@ -242,9 +279,15 @@ def test_no_device_is_an_error_not_a_crash(lib):
     assert f(Y, ctypes.byref(W), A + 0x1000, A + 0x2000, None, 0, 8, None) == st
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(ctypes.byref(act), ctypes.c_void_p(Y), ctypes.c_int64(64), None) == st
-    P = QT(A + 0x4000, B + 0x4000, 0, 0, 0)
-    assert lib.qmv_pack_weights(ctypes.byref(P), ctypes.byref(W), None) == st
-    P = QT(A + 0x4000, B + 0x4000, 8, 64, Q8)
-    assert lib.qmv_gemm_q8_packed(Y, ctypes.byref(P), ctypes.byref(QT(A + 0x1000, B + 0x1000, 20, 64, Q8)),
+    PK = QT(A + 0x4000, B + 0x4000, 0, 0, 0)
+    assert lib.qmv_pack_weights(ctypes.byref(PK), ctypes.byref(W), None) == st
+    PK = QT(A + 0x4000, B + 0x4000, 8, 64, Q8)
+    assert lib.qmv_gemm_q8_packed(Y, ctypes.byref(PK), ctypes.byref(QT(A + 0x1000, B + 0x1000, 20, 64, Q8)),
                                   0, 8, None) == st
+    f = lib.qmv_matvec_zp_fx
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(Y, ctypes.byref(ZT(A, B, 0, 8, 256, 8)), A + 0x1000, None, 0, 8, None) == st
+    g = lib.qmv_quantize_q8_b128
+    g.argtypes = [P, P, ctypes.c_int64, P]
+    assert g(ctypes.byref(QA(A, B, 0)), Y, 128, None) == st
     assert lib.qmv_last_kernel().decode() == ""
