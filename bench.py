@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-batched", action="store_true", help="skip the M >= 16 matrix-core measurement")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the per-call timings of the other configurations (keeps kernel traces to the step)")
+    ap.add_argument("--zp-only", action="store_true",
+                    help="only the 128-block zero-point format measurement (for profiling)")
     ap.add_argument("--batched-only", action="store_true",
                     help="only the M >= 16 matrix-core measurement (one JSON object; for profiling that path)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -112,6 +114,13 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.zp_only:
+        import torch
+        from block_quantized_decode_amd import qmv
+        torch.cuda.set_device(0)
+        qmv.qmv_device_check()
+        print(json.dumps(zp_bench(torch.cuda.Stream())), flush=True)
         return
     if args.batched_only:
         import torch
@@ -232,9 +241,11 @@ def main():
     # ---- the other configurations: per call and per layer, cold
     others = None
     fusion = None
+    zp = None
     if not args.no_others:
         others = other_workloads_bench(stream)
         fusion = fusion_bench(stream)
+        zp = zp_bench(stream)
 
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
@@ -289,6 +300,7 @@ def main():
         "small_batch": small,
         "other_workloads": others,
         "fusion": fusion,
+        "zp_b128": zp,
         "batched": batched,
     }
     print(json.dumps(line), flush=True)
@@ -468,6 +480,55 @@ def other_workloads_bench(stream):
     torch.cuda.empty_cache()
     out[wl.name] = {"per_matrix_us": per, "per_matrix_weight_gb_s": gbs, "ffn_us": round(ffn_us, 3),
                     "lm_head_pct_hbm_peak": round(100.0 * gbs["lm_head"] / HBM_PEAK_GBS, 2), "copies": copies}
+    return out
+
+
+def zp_bench(stream):
+    """The exported-model format (128-element blocks with a zero point,
+    qmv_matvec_zp_fx, the activation quantized in the launch), 8 and 4 bits,
+    on the Qwen2.5-0.5B FFN and lm_head shapes of the ONNX page's real
+    export and on the Llama-7B FFN matrices.  Codes, scales and zero points
+    are uniform random draws on the GPU (seeded); each matrix is rotated
+    over copies totalling more than 600 MB, so every launch streams from
+    HBM, and timed as a graph of prepared calls.  Weight bytes = codes +
+    scales + zero points."""
+    import torch
+
+    from block_quantized_decode_amd import qmv
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    shapes = {
+        "qwen05b_ffn_lmhead": [("W_gate", 4864, 896), ("W_up", 4864, 896), ("W_down", 896, 4864),
+                               ("lm_head", 151936, 896)],
+        "llama7b_ffn": [("W_up", 11008, 4096), ("W_down", 4096, 11008)],
+    }
+    out = {}
+    for bits in (8, 4):
+        for wname, mats in shapes.items():
+            per = {}
+            for name, rows, cols in mats:
+                nb = cols // 128
+                rb = cols if bits == 8 else cols // 2
+                wbytes = rows * rb + rows * nb * 5
+                copies = max(2, (600 << 20) // wbytes + 1)
+                x = torch.randn(cols, device=dev, generator=gen)
+                calls = []
+                for _ in range(copies):
+                    q = torch.randint(0, 256, (rows, rb), dtype=torch.uint8, device=dev, generator=gen)
+                    d = torch.rand(rows, nb, device=dev, generator=gen) * 0.01 + 0.001
+                    zp = torch.randint(0, 1 << bits, (rows, nb), dtype=torch.uint8, device=dev, generator=gen)
+                    y = torch.zeros(rows, device=dev)
+                    calls.append(qmv.prepare_matvec_zp_fx(q, d, zp, bits, x, y, stream=stream.cuda_stream))
+                us = _graph_us(calls, stream) / len(calls)
+                gbs = wbytes / (us * 1e-6) / 1e9
+                per[name] = {"shape": f"{rows}x{cols}", "us": round(us, 3), "weight_gb_s": round(gbs, 1),
+                             "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "kernel": qmv.last_kernel(),
+                             "copies": copies}
+                del calls
+                torch.cuda.empty_cache()
+            out[f"{wname}_int{bits}_b128"] = per
     return out
 
 

@@ -46,7 +46,24 @@ namespace {
 
 typedef int v4i_zp __attribute__((ext_vector_type(4)));
 
+#ifndef QMV_ZP_D12  // register ring depth for 1-2 chunks per lane
+#define QMV_ZP_D12 4
+#endif
+#ifndef QMV_ZP_D34  // ... and for 3-4 chunks per lane
+#define QMV_ZP_D34 3
+#endif
+#ifndef QMV_ZP_WG_PER_CU_SCALE  // scales the workgroups per compute unit
+#define QMV_ZP_WG_PER_CU_SCALE 1
+#endif
+#ifndef QMV_ZP_FORCE_P  // 0: wavefronts per row chosen by shape
+#define QMV_ZP_FORCE_P 0
+#endif
+
 constexpr int BLK = 128;               // elements per block
+#ifndef QMV_ZP_QBATCH
+#define QMV_ZP_QBATCH 2
+#endif
+constexpr int kQBatch = QMV_ZP_QBATCH;  // block pairs whose loads a wavefront issues together
 constexpr int kWpb = 8;                // wavefronts per workgroup
 constexpr int kOOBz = 0x7FFFFFF0;      // an offset beyond every descriptor range used here
 constexpr int kBufFlagsZ = 0x00020000; // buffer descriptor word 3: raw 32-bit data
@@ -91,6 +108,38 @@ __device__ __forceinline__ void quant_block128(const float *x, int b, int lane, 
     qsum = wave_sum(q0 + q1);
 }
 
+// Reductions over each half-wavefront (lanes 0-31 and 32-63): DPP within
+// rows of 16 lanes (swap neighbours, swap pairs, mirror 8, mirror 16), then
+// the four row values read out and combined per half.  Max is exact and the
+// integer sum is exact, so the order does not matter.
+template <typename F>
+__device__ __forceinline__ int half_reduce(int v, F op) {
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const int lane = threadIdx.x & 63;
+    return lane < 32 ? op(r0, r1) : op(r2, r3);
+}
+
+// Quantize the 128-element block held by this half-wavefront (lane c of the
+// half holds elements 4c .. 4c + 3): the same operations as quant_block128.
+__device__ __forceinline__ void quant_half(float4 v, int lane, int (&q)[4], float &d, int &qsum) {
+    (void)lane;
+    const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    // non-negative floats order like their bit patterns
+    const float amax = __int_as_float(half_reduce(__float_as_int(m), [](int a, int b) { return max(a, b); }));
+    d = amax / 127.0f;
+    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
+    q[0] = q8_round(v.x, id);
+    q[1] = q8_round(v.y, id);
+    q[2] = q8_round(v.z, id);
+    q[3] = q8_round(v.w, id);
+    qsum = half_reduce(q[0] + q[1] + q[2] + q[3], [](int a, int b) { return a + b; });
+}
+
 // position of element e of a block in the 4-bit activation order
 __device__ __forceinline__ int perm4(int e) { return (e & ~7) + ((e & 1) << 2) + ((e & 7) >> 1); }
 
@@ -98,14 +147,15 @@ __device__ __forceinline__ int dpp_x1(int v) { return __builtin_amdgcn_update_dp
 __device__ __forceinline__ int dpp_x2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_m8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
 
-template <int BITS, int L, int J>
+template <int BITS, int L, int J, int D, int P>
 __global__ void __launch_bounds__(64 * kWpb)
 k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restrict__ wd,
      const uint8_t *__restrict__ wzp, int32_t rows, int32_t K, const float *__restrict__ x,
-     int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1) {
+     int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1, int32_t rows_wg) {
     constexpr int LB = BITS == 8 ? 8 : 4;  // lanes (16-byte chunks) per block
     constexpr int GPW = 64 / L;            // row groups per wavefront
     static_assert(L >= LB && (L & (L - 1)) == 0 && L <= 64, "group size");
+    static_assert(P == 1 || (L == 64 && kWpb % P == 0), "teams of P wavefronts share rows of 64-lane groups");
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = K / BLK;
     int8_t *xs = reinterpret_cast<int8_t *>(smem);
@@ -115,41 +165,60 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
 
-    // ---- phase A: the activation, quantized into LDS
-    for (int b = wid; b < nb; b += kWpb) {
-        int q0, q1, qs;
-        float d;
-        quant_block128(x, b, lane, q0, q1, d, qs);
-        const int e = 2 * lane;
-        if constexpr (BITS == 8) {
-            *reinterpret_cast<short *>(xs + b * BLK + e) = (short)((q0 & 0xFF) | (q1 << 8));
-        } else {
-            xs[b * BLK + perm4(e)] = (int8_t)q0;
-            xs[b * BLK + perm4(e + 1)] = (int8_t)q1;
-        }
-        if (lane == 0) {
-            sd[b] = d;
-            sq[b] = qs;
-        }
-        if (xq_out != nullptr && blockIdx.x == 0) {
-            *reinterpret_cast<short *>(xq_out + (int64_t)b * BLK + e) = (short)((q0 & 0xFF) | (q1 << 8));
-            if (lane == 0) xd_out[b] = d;
-        }
-    }
-    __syncthreads();
-
     // ---- phase B: rows
+    //   P = 1: group g of L lanes takes rows r0 + g, r0 + g + G, ... (G groups
+    //   in the grid), each row in W windows of L * J chunks, in order.
+    //   P > 1: workgroup b takes rows_wg consecutive rows; its 8 / P teams of P
+    //   wavefronts take every (8 / P)-th of them, and wavefront q of a team
+    //   takes windows q, q + P, ... of the team's rows.  The P partial sums of
+    //   a row meet in LDS and are added in wavefront order at the end.
     const int row_bytes = BITS == 8 ? K : K / 2;
     const int chunks = row_bytes >> 4;
     const int W = (chunks + L * J - 1) / (L * J);  // windows per row
     const int gl = lane & (L - 1);
-    const int G = gridDim.x * kWpb * GPW;               // row groups in the grid
+    const int nrow = r1 - r0;
+    constexpr int TPW = kWpb / P;                  // teams per workgroup (P > 1)
+    const int tm = wid / P, pw = wid % P;
+    const int rb0 = r0 + blockIdx.x * rows_wg;     // P > 1: this workgroup's rows
+    const int rows_here = P > 1 ? max(0, min(rows_wg, r1 - rb0)) : 0;
+    const int rows_team = P > 1 ? (rows_here - tm + TPW - 1) / TPW : 0;
+    const int rows_team_max = P > 1 ? (rows_wg + TPW - 1) / TPW : 0;  // workgroup-uniform
+    const int wpw = (W + P - 1) / P;                                   // windows per wavefront and row
+    const int G = gridDim.x * kWpb * GPW;               // P = 1: row groups in the grid
     const int g0 = (blockIdx.x * kWpb + wid) * GPW;     // this wavefront's first group
     const int g = g0 + lane / L;
-    const int nrow = r1 - r0;
     const int rows_g = g < nrow ? (nrow - g + G - 1) / G : 0;
     const int rows_w = g0 < nrow ? (nrow - g0 + G - 1) / G : 0;  // the wavefront's first group has the most
-    const int items = rows_w * W;                                // wave-uniform loop count
+    const int items = P > 1 ? rows_team_max * wpw : rows_w * W;   // wave-uniform loop count
+    float *part = reinterpret_cast<float *>(smem + ((K + 8 * nb + 15) & ~15));  // P > 1: [rows_wg][P]
+
+    // item t of this lane group: its row, window, and whether it starts or
+    // ends the row's accumulation
+    struct Item {
+        int r, win, li;
+        bool live, first, last;
+    };
+    auto item = [&](int t) __attribute__((always_inline)) {
+        Item it;
+        if constexpr (P == 1) {
+            const int rl = t / W;
+            it.win = t - rl * W;
+            it.live = rl < rows_g;
+            it.r = r0 + g + rl * G;
+            it.li = 0;
+            it.first = it.win == 0;
+            it.last = it.win == W - 1;
+        } else {
+            const int i = t / wpw, k = t - i * wpw;
+            it.win = pw + P * k;
+            it.li = tm + TPW * i;
+            it.live = i < rows_team && it.win < W;
+            it.r = rb0 + it.li;
+            it.first = k == 0;
+            it.last = k == wpw - 1;
+        }
+        return it;
+    };
 
     const __amdgpu_buffer_rsrc_t rq = rsrc(wq, (int64_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t rd = rsrc(wd, (int64_t)rows * nb * 4);
@@ -163,13 +232,12 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
         int zp[J];
     };
     auto load = [&](Buf &bf, int t) __attribute__((always_inline)) {
-        const int rl = t / W, win = t - rl * W;
-        const bool live = rl < rows_g;
-        const int r = r0 + g + rl * G;
+        const Item it = item(t);
+        const int r = it.r;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int c = (win * J + j) * L + gl;  // chunk of the row
-            const bool ok = live && c < chunks;
+            const int c = (it.win * J + j) * L + gl;  // chunk of the row
+            const bool ok = it.live && c < chunks;
             const int b = c / LB;
             bf.w[j] = __builtin_bit_cast(
                 v4i_zp, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? r * row_bytes + 16 * c : kOOBz, 0, 2));
@@ -184,13 +252,12 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 
     float acc = 0.0f;
     auto compute = [&](const Buf &bf, int t) __attribute__((always_inline)) {
-        const int rl = t / W, win = t - rl * W;
-        const bool live = rl < rows_g;
-        if (win == 0) acc = 0.0f;
+        const Item it = item(t);
+        if (it.first) acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int c = (win * J + j) * L + gl;
-            const bool ok = live && c < chunks;
+            const int c = (it.win * J + j) * L + gl;
+            const bool ok = it.live && c < chunks;
             const int b = ok ? c / LB : 0;
             const int sub = c % LB;
             int p = 0;
@@ -224,70 +291,168 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
                 acc = acc + tt;
             }
         }
-        if (win == W - 1) {
+        if (it.last) {
             float s = acc;
 #pragma unroll
             for (int o = LB; o < L; o <<= 1) s += __shfl_xor(s, o);
-            if (live && gl == 0) y[r0 + g + rl * G] = s;
+            if constexpr (P == 1) {
+                if (it.live && gl == 0) y[it.r] = s;
+            } else {
+                // this wavefront's share of the row (0 if it had no window of it)
+                if (it.li < rows_here && gl == 0) part[it.li * P + pw] = s;
+            }
         }
     };
 
-    Buf b0, b1;
-    load(b0, 0);
-    for (int t = 0; t < items; t += 2) {
-        load(b1, t + 1);
-        compute(b0, t);
-        if (t + 1 < items) {
-            load(b0, t + 2);
-            compute(b1, t + 1);
+    // ring of D register buffers, D - 1 items in flight ahead of the one
+    // being computed (unrolled by D so that each buffer has fixed registers)
+    Buf ring[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
+
+    // ---- phase A: the activation, quantized into LDS.  Each half-wavefront
+    // takes one block (4 elements per lane); a wavefront first issues the
+    // loads of up to kQBatch block pairs, then quantizes them.
+    for (int base = 2 * wid; base < nb; base += 2 * kWpb * kQBatch) {
+        float4 v[kQBatch];
+#pragma unroll
+        for (int u = 0; u < kQBatch; ++u) {
+            const int b = base + 2 * kWpb * u + (lane >> 5);
+            v[u] = b < nb ? *reinterpret_cast<const float4 *>(x + (int64_t)b * BLK + 4 * (lane & 31))
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < kQBatch; ++u) {
+            const int b0 = base + 2 * kWpb * u;
+            if (b0 >= nb) break;  // wave-uniform
+            const int b = b0 + (lane >> 5);
+            int q[4], qs;
+            float d;
+            quant_half(v[u], lane, q, d, qs);
+            if (b < nb) {
+                const int e = 4 * (lane & 31);
+                const int pk = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | (q[3] << 24);
+                if constexpr (BITS == 8) {
+                    *reinterpret_cast<int *>(xs + b * BLK + e) = pk;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xs[b * BLK + perm4(e + i)] = (int8_t)q[i];
+                }
+                if ((lane & 31) == 0) {
+                    sd[b] = d;
+                    sq[b] = qs;
+                }
+                if (xq_out != nullptr && blockIdx.x == 0) {
+                    *reinterpret_cast<int *>(xq_out + (int64_t)b * BLK + e) = pk;
+                    if ((lane & 31) == 0) xd_out[b] = d;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int t0 = 0; t0 < items; t0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int t = t0 + d;
+            if (t < items) {  // wave-uniform
+                load(ring[(d + D - 1) % D], t + D - 1);
+                compute(ring[d], t);
+            }
+        }
+    }
+    if constexpr (P > 1) {
+        __syncthreads();
+        for (int li = threadIdx.x; li < rows_here; li += 64 * kWpb) {
+            float s = part[li * P];
+#pragma unroll
+            for (int q = 1; q < P; ++q) s += part[li * P + q];
+            y[rb0 + li] = s;
         }
     }
 }
 
-template <int BITS, int L, int J>
-hipError_t launch_cfg(const ZpArgs &a, int grid, size_t lds, hipStream_t s, const char **name) {
-    auto kern = k_zp<BITS, L, J>;
+template <int BITS, int L, int J, int P>
+hipError_t launch_cfg(const ZpArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
+    constexpr int D = J <= 2 ? QMV_ZP_D12 : J <= 4 ? QMV_ZP_D34 : 2;
+    auto kern = k_zp<BITS, L, J, D, P>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWpb), lds, s, a.y, a.wq, a.wd, a.wzp, a.rows, a.K, a.x,
-                       a.xq_out, a.xd_out, a.r0, a.r1);
+                       a.xq_out, a.xd_out, a.r0, a.r1, rows_wg);
     static char kname[48];
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "zp%d_l%d_j%d", BITS, L, J);
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "zp%d_l%d_j%d_d%d_p%d", BITS, L, J, D, P);
     *name = kname;
     return hipGetLastError();
+}
+
+template <int BITS, int P>
+hipError_t launch_j(const ZpArgs &a, int J, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
+    switch (J) {
+        case 1: return launch_cfg<BITS, 64, 1, P>(a, grid, rows_wg, lds, s, name);
+        case 2: return launch_cfg<BITS, 64, 2, P>(a, grid, rows_wg, lds, s, name);
+        case 3: return launch_cfg<BITS, 64, 3, P>(a, grid, rows_wg, lds, s, name);
+        case 4: return launch_cfg<BITS, 64, 4, P>(a, grid, rows_wg, lds, s, name);
+        case 5: return launch_cfg<BITS, 64, 5, P>(a, grid, rows_wg, lds, s, name);
+        case 6: return launch_cfg<BITS, 64, 6, P>(a, grid, rows_wg, lds, s, name);
+        case 7: return launch_cfg<BITS, 64, 7, P>(a, grid, rows_wg, lds, s, name);
+        default: return launch_cfg<BITS, 64, 8, P>(a, grid, rows_wg, lds, s, name);
+    }
+}
+
+// J chunks per lane per window (at most 8) for rows of `chunks` chunks split
+// over P wavefronts: the windows of a row as even as possible.
+int pick_j(int chunks, int P) {
+    const int per = (chunks + P - 1) / P;  // chunks per wavefront and row
+    const int win = (per + 64 * 8 - 1) / (64 * 8);
+    return (per + 64 * win - 1) / (64 * win);
 }
 
 template <int BITS>
 hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
     const int chunks = (BITS == 8 ? a.K : a.K / 2) / 16;
-    const size_t lds = (size_t)a.K + 8 * (size_t)(a.K / BLK);
+    const size_t lds_x = ((size_t)a.K + 8 * (size_t)(a.K / BLK) + 15) & ~(size_t)15;
+    const int nrow = a.r1 - a.r0;
     // lanes per row: the fewest power of two (16 .. 64) that covers a row
     int L = 64;
     if (chunks <= 16) L = 16;
     else if (chunks <= 32) L = 32;
-    const int nrow = a.r1 - a.r0;
-    const int groups_per_wg = kWpb * (64 / L);
-    int grid = (nrow + groups_per_wg - 1) / groups_per_wg;
-    if (grid > num_cu) grid = num_cu;
-    if (grid < 1) grid = 1;
-    if (L == 16) return launch_cfg<BITS, 16, 1>(a, grid, lds, s, name);
-    if (L == 32) return launch_cfg<BITS, 32, 1>(a, grid, lds, s, name);
-    // L = 64: J chunks per lane per window, at most 8, windows as even as possible
-    const int win = (chunks + 64 * 8 - 1) / (64 * 8);
-    const int J = (chunks + 64 * win - 1) / (64 * win);
-    switch (J) {
-        case 1: return launch_cfg<BITS, 64, 1>(a, grid, lds, s, name);
-        case 2: return launch_cfg<BITS, 64, 2>(a, grid, lds, s, name);
-        case 3: return launch_cfg<BITS, 64, 3>(a, grid, lds, s, name);
-        case 4: return launch_cfg<BITS, 64, 4>(a, grid, lds, s, name);
-        case 5: return launch_cfg<BITS, 64, 5>(a, grid, lds, s, name);
-        case 6: return launch_cfg<BITS, 64, 6>(a, grid, lds, s, name);
-        case 7: return launch_cfg<BITS, 64, 7>(a, grid, lds, s, name);
-        default: return launch_cfg<BITS, 64, 8>(a, grid, lds, s, name);
+    const int wgpc = L < 64 || pick_j(chunks, 1) == 1 ? 4 : 2;  // workgroups per compute unit
+    const int waves = QMV_ZP_WG_PER_CU_SCALE * wgpc * num_cu * kWpb;
+    // rows shared by a team of P wavefronts when there are fewer than two
+    // rows per wavefront and each row has at least two windows' worth
+    int P = 1;
+    if (L == 64 && chunks >= 128) {
+        while (P < kWpb && (int64_t)nrow * P < 2 * (int64_t)waves && chunks / (2 * P) >= 64) P *= 2;
     }
+#if QMV_ZP_FORCE_P
+    if (L == 64) P = QMV_ZP_FORCE_P;
+#endif
+    if (P == 1) {
+        const int groups_per_wg = kWpb * (64 / L);
+        int grid = (nrow + groups_per_wg - 1) / groups_per_wg;
+        if (grid > waves / kWpb) grid = waves / kWpb;
+        if (grid < 1) grid = 1;
+        if (L == 16) return launch_cfg<BITS, 16, 1, 1>(a, grid, 0, lds_x, s, name);
+        if (L == 32) return launch_cfg<BITS, 32, 1, 1>(a, grid, 0, lds_x, s, name);
+        return launch_j<BITS, 1>(a, pick_j(chunks, 1), grid, 0, lds_x, s, name);
+    }
+    // P > 1: consecutive rows per workgroup, enough workgroups to give each
+    // wavefront work, partial sums in LDS (at most 8 KiB of them)
+    int grid = waves / kWpb;
+    int rows_wg = (nrow + grid - 1) / grid;
+    if (rows_wg < 1) rows_wg = 1;
+    if (rows_wg * P > 2048) rows_wg = 2048 / P;
+    grid = (nrow + rows_wg - 1) / rows_wg;
+    if (grid < 1) grid = 1;
+    const size_t lds = lds_x + (size_t)rows_wg * P * 4;
+    const int J = pick_j(chunks, P);
+    if (P == 2) return launch_j<BITS, 2>(a, J, grid, rows_wg, lds, s, name);
+    if (P == 4) return launch_j<BITS, 4>(a, J, grid, rows_wg, lds, s, name);
+    return launch_j<BITS, 8>(a, J, grid, rows_wg, lds, s, name);
 }
 
 __global__ void __launch_bounds__(256)
@@ -306,7 +471,7 @@ k_quant_b128(int8_t *__restrict__ q, float *__restrict__ d, const float *__restr
 
 }  // namespace
 
-size_t zp_lds_bytes(int32_t K) { return (size_t)K + 8 * (size_t)(K / BLK); }
+size_t zp_lds_bytes(int32_t K) { return (((size_t)K + 8 * (size_t)(K / BLK) + 15) & ~(size_t)15) + 8192; }
 
 hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
     if (a.K % BLK != 0 || zp_lds_bytes(a.K) > 160 * 1024) return hipErrorNotSupported;
