@@ -142,3 +142,55 @@ def test_zp_full_size(bits, rows, k):
     assert np.array_equal(qo, xq) and np.array_equal(do.view(np.uint32), xd.view(np.uint32))
     for r0 in (0, rows // 2 - 5, rows - 11):
         _check(bits, y, wq, wd, wzp, xq, xd, r0, r0 + 11, f"full {rows}x{k} [{r0},{r0 + 11})")
+
+
+def test_zp_and_packed_graph_replay():
+    """Prepared zero-point matvecs (8- and 4-bit) and a packed matrix-core
+    product captured in one HIP graph: every replay, with eager work and
+    synchronisations in between, gives the eager result bit for bit."""
+    announce("zp and packed graph replay")
+    rng = np.random.default_rng(5500)
+    stream = torch.cuda.Stream()
+    s = stream.cuda_stream
+    k8, n8 = 896, 4864
+    q8, d8, z8 = synth.raw_zp(rng, 8, n8, k8)
+    k4, n4 = 4864, 896
+    q4, d4, _ = synth.raw_zp(rng, 4, n4, k4, with_zp=False)
+    x8 = dev(_x(rng, k8))
+    x4 = dev(_x(rng, k4))
+    y8 = torch.zeros(n8, dtype=torch.float32, device="cuda:0")
+    y4 = torch.zeros(n4, dtype=torch.float32, device="cuda:0")
+    wq, wd = synth.raw_q4(rng, 300, 2048)
+    xq, xd = orc.quantize_q8(synth.normal(rng, (24, 2048)))
+    P = qmv.qmv_pack_weights(dev(wq), dev(wd), 4)
+    Y = torch.zeros((24, 300), dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    calls = [qmv.prepare_matvec_zp_fx(dev(q8), dev(d8), dev(z8), 8, x8, y8, stream=s),
+             qmv.prepare_matvec_zp_fx(dev(q4), dev(d4), None, 4, x4, y4, stream=s),
+             qmv.prepare_gemm_packed(P, dev(xq), dev(xd), Y, stream=s)]
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    outs = (y8, y4, Y)
+    eager = [host(t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(outs, eager):
+            assert np.array_equal(host(t), e), f"replay {rep} differs from the eager result"
+    # the eager results against the oracle
+    xq8, xd8 = orc.quantize_q8_b128(host(x8))
+    _check(8, eager[0], q8, d8, z8, xq8, xd8, 0, n8, "graph zp8")
+    xq4, xd4 = orc.quantize_q8_b128(host(x4))
+    _check(4, eager[1], q4, d4, None, xq4, xd4, 0, n4, "graph zp4")
+    Yref = orc.gemm(4, wq, wd, xq, xd)
+    tol = np.stack([orc.tolerance(4, wq, wd, xq[i], xd[i]) for i in range(24)])
+    assert np.all(np.abs(eager[2].astype(np.float64) - Yref) <= tol), "graph packed product"
