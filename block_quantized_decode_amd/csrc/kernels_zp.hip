@@ -147,6 +147,31 @@ __device__ __forceinline__ int dpp_x1(int v) { return __builtin_amdgcn_update_dp
 __device__ __forceinline__ int dpp_x2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_m8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of L lanes (16, 32 or 64), the same value in
+// every lane of the group, in a fixed order: DPP within each 16-lane row
+// (neighbour swap, pair swap, mirror 8, mirror 16: after each step the value
+// is uniform over 2, 4, 8, 16 lanes), then the rows' values read out and
+// added ((r0 + r1) + (r2 + r3) for L = 64).
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    v = v + dppf<0xB1>(v);
+    v = v + dppf<0x4E>(v);
+    v = v + dppf<0x141>(v);
+    v = v + dppf<0x140>(v);
+    if constexpr (L == 16) return v;
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 48));
+    if constexpr (L == 32) return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+    return (r0 + r1) + (r2 + r3);
+}
+
 template <int BITS, int L, int J, int D, int P>
 __global__ void __launch_bounds__(64 * kWpb)
 k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restrict__ wd,
@@ -226,10 +251,15 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     const int zdef = 1 << (BITS - 1);
     constexpr int off = BITS == 8 ? 128 : 0;  // bias of the dotted codes
 
+    // Scales and zero points: lane `sub` of a block's LB lanes loads those of
+    // the slot's blocks at iterations sub, sub + LB, ... of the window, and
+    // scales those blocks itself (one load per LB blocks instead of one per
+    // block and lane).
+    constexpr int JM = (J + LB - 1) / LB;
     struct Buf {
         v4i_zp w[J];
-        float dw[J];
-        int zp[J];
+        float dw[JM];
+        int zp[JM];
     };
     auto load = [&](Buf &bf, int t) __attribute__((always_inline)) {
         const Item it = item(t);
@@ -238,15 +268,22 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
         for (int j = 0; j < J; ++j) {
             const int c = (it.win * J + j) * L + gl;  // chunk of the row
             const bool ok = it.live && c < chunks;
-            const int b = c / LB;
             bf.w[j] = __builtin_bit_cast(
                 v4i_zp, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? r * row_bytes + 16 * c : kOOBz, 0, 2));
-            bf.dw[j] = __builtin_bit_cast(
+        }
+        const int sub = gl % LB;
+#pragma unroll
+        for (int m = 0; m < JM; ++m) {
+            const int jj = sub + LB * m;  // the iteration whose block this lane scales
+            const int c = (it.win * J + jj) * L + (gl - sub);
+            const bool ok = it.live && jj < J && c < chunks;
+            const int b = c / LB;
+            bf.dw[m] = __builtin_bit_cast(
                 float, __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (r * nb + b) : kOOBz, 0, 0));
             if (wzp != nullptr)
-                bf.zp[j] = (int)__builtin_amdgcn_raw_buffer_load_b8(rz, ok ? r * nb + b : kOOBz, 0, 0);
+                bf.zp[m] = (int)__builtin_amdgcn_raw_buffer_load_b8(rz, ok ? r * nb + b : kOOBz, 0, 0);
             else
-                bf.zp[j] = zdef;
+                bf.zp[m] = zdef;
         }
     };
 
@@ -283,18 +320,16 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             p += dpp_x1(p);
             p += dpp_x2(p);
             if constexpr (LB == 8) p += dpp_m8(p);
-            if (ok) {
+            if (ok && sub == j % LB) {
 #pragma clang fp contract(off)
-                const int sumi = p - (bf.zp[j] - off) * sq[b];
-                float tt = (float)sumi * bf.dw[j];
+                const int sumi = p - (bf.zp[j / LB] - off) * sq[b];
+                float tt = (float)sumi * bf.dw[j / LB];
                 tt = tt * sd[b];
                 acc = acc + tt;
             }
         }
         if (it.last) {
-            float s = acc;
-#pragma unroll
-            for (int o = LB; o < L; o <<= 1) s += __shfl_xor(s, o);
+            const float s = group_sum<L>(acc);
             if constexpr (P == 1) {
                 if (it.live && gl == 0) y[it.r] = s;
             } else {
