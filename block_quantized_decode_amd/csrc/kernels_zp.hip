@@ -17,22 +17,27 @@
 // already non-negative bytes, so sumi = sum B q - zp * sum q.  sum q is
 // computed once per block when the activation is quantized.
 //
-// Work layout.  One workgroup of 8 wavefronts per compute unit.
-//   Phase A: the workgroup quantizes the whole activation into LDS (one
-//   wavefront per 128-element block, 2 elements per lane), with the block
-//   scales and the block sums of the quants.  For 4-bit weights the quants
-//   of each 8-element group are stored as (x0, x2, x4, x6, x1, x3, x5, x7),
-//   so that the masked low and high nibbles of a weight dword meet their
-//   activation bytes in one v_dot4 each.
+// Work layout.  Workgroups of 8 wavefronts, 2 or 4 per compute unit.
+//   Phase A: the workgroup quantizes the whole activation into LDS: each
+//   half-wavefront one 128-element block, 4 elements per lane, maximum and
+//   sum reduced by DPP within rows of 16 lanes and lane reads across rows;
+//   the block scales and the block sums of the quants go to LDS as well.
+//   For 4-bit weights the quants of each 8-element group are stored as
+//   (x0, x2, x4, x6, x1, x3, x5, x7), so that the masked low and high
+//   nibbles of a weight dword meet their activation bytes in one v_dot4
+//   each.  The first weight loads are issued before this phase.
 //   Phase B: groups of L lanes (L = 16, 32 or 64) stream whole weight rows:
-//   lane c of a group reads 16-byte chunk c, c + L, ... of the row (J
-//   chunks per window, double-buffered in registers, non-temporal), so the
+//   lane c of a group reads 16-byte chunk c, c + L, ... of the row (J chunks
+//   per window, a ring of D windows in registers, non-temporal), so the
 //   LB = 8 (8-bit) or 4 (4-bit) lanes of one block are adjacent.  Their
-//   partial dots are added by DPP within the block's lanes, giving the exact
-//   block sum in every lane; the block is scaled in fp32 and added to the
-//   lane's slot accumulator in ascending block order; at the end of a row
-//   the slots are added by a fixed butterfly and the group's first lane
-//   writes y.  The result does not depend on timing.
+//   partial dots are added by DPP, giving the exact block sum in every lane
+//   of the block; one of those lanes, the one that loaded the block's scale
+//   and zero point, scales it in fp32 and adds it to its accumulator, in
+//   ascending block order.  At the end of a row the group's lanes are added
+//   in a fixed order and the group's first lane writes y.  Rows too few to
+//   give every wavefront work are shared by teams of P wavefronts, which
+//   take interleaved windows and add their partial sums in LDS in
+//   wavefront order.  The result does not depend on timing.
 //
 // Every variable part of an address is in the range-checked offset of a raw
 // buffer load: chunks past the row, and rows past r1, read zeros and are
@@ -83,31 +88,6 @@ __device__ __forceinline__ int q8_round(float x, float id) {
     return min(max(q, -127), 127);
 }
 
-__device__ __forceinline__ float wave_max(float a) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-    return a;
-}
-
-__device__ __forceinline__ int wave_sum(int a) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
-    return a;
-}
-
-// Quantize 128-element block b of x (one wavefront, lane l holding elements
-// 2l and 2l + 1).  Returns the two quants; d and qsum are wave-uniform.
-__device__ __forceinline__ void quant_block128(const float *x, int b, int lane, int &q0, int &q1, float &d,
-                                               int &qsum) {
-    const float2 v = *reinterpret_cast<const float2 *>(x + (int64_t)b * BLK + 2 * lane);
-    const float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
-    d = amax / 127.0f;
-    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
-    q0 = q8_round(v.x, id);
-    q1 = q8_round(v.y, id);
-    qsum = wave_sum(q0 + q1);
-}
-
 // Reductions over each half-wavefront (lanes 0-31 and 32-63): DPP within
 // rows of 16 lanes (swap neighbours, swap pairs, mirror 8, mirror 16), then
 // the four row values read out and combined per half.  Max is exact and the
@@ -125,9 +105,9 @@ __device__ __forceinline__ int half_reduce(int v, F op) {
 }
 
 // Quantize the 128-element block held by this half-wavefront (lane c of the
-// half holds elements 4c .. 4c + 3): the same operations as quant_block128.
-__device__ __forceinline__ void quant_half(float4 v, int lane, int (&q)[4], float &d, int &qsum) {
-    (void)lane;
+// half holds elements 4c .. 4c + 3): amax exact, d = amax / 127,
+// id = 127 / amax (both correctly rounded divisions), then q8_round.
+__device__ __forceinline__ void quant_half(float4 v, int (&q)[4], float &d, int &qsum) {
     const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     // non-negative floats order like their bit patterns
     const float amax = __int_as_float(half_reduce(__float_as_int(m), [](int a, int b) { return max(a, b); }));
@@ -363,7 +343,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             const int b = b0 + (lane >> 5);
             int q[4], qs;
             float d;
-            quant_half(v[u], lane, q, d, qs);
+            quant_half(v[u], q, d, qs);
             if (b < nb) {
                 const int e = 4 * (lane & 31);
                 const int pk = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | (q[3] << 24);
@@ -492,15 +472,23 @@ hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **
 
 __global__ void __launch_bounds__(256)
 k_quant_b128(int8_t *__restrict__ q, float *__restrict__ d, const float *__restrict__ x, int64_t nblk) {
+    // one block per half-wavefront, 4 elements per lane (as the matvec's
+    // activation phase, hence the same bits)
     const int lane = threadIdx.x & 63;
-    const int64_t w0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t h0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;  // wavefront
     const int64_t nw = ((int64_t)gridDim.x * 256) >> 6;
-    for (int64_t b = w0; b < nblk; b += nw) {  // one wavefront per block
-        int q0, q1, qs;
+    for (int64_t b0 = 2 * h0; b0 < nblk; b0 += 2 * nw) {  // wave-uniform
+        const int64_t b = b0 + (lane >> 5);
+        const float4 v = b < nblk ? *reinterpret_cast<const float4 *>(x + b * BLK + 4 * (lane & 31))
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        int qv[4], qs;
         float dd;
-        quant_block128(x + b * BLK, 0, lane, q0, q1, dd, qs);
-        *reinterpret_cast<short *>(q + b * BLK + 2 * lane) = (short)((q0 & 0xFF) | (q1 << 8));
-        if (lane == 0) d[b] = dd;
+        quant_half(v, qv, dd, qs);
+        if (b < nblk) {
+            *reinterpret_cast<int *>(q + b * BLK + 4 * (lane & 31)) =
+                (qv[0] & 0xFF) | ((qv[1] & 0xFF) << 8) | ((qv[2] & 0xFF) << 16) | (qv[3] << 24);
+            if ((lane & 31) == 0) d[b] = dd;
+        }
     }
 }
 
@@ -514,7 +502,7 @@ hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **na
 }
 
 hipError_t launch_quant_b128(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name) {
-    int64_t g = (nblk + 3) / 4;
+    int64_t g = (nblk + 7) / 8;  // 8 blocks per workgroup of 4 wavefronts
     if (g > 4096) g = 4096;
     if (g < 1) g = 1;
     hipLaunchKernelGGL(k_quant_b128, dim3((unsigned)g), dim3(256), 0, s, q, d, x, nblk);
