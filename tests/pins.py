@@ -604,9 +604,11 @@ def check_zp_matvec_unit_scales():
         want = (zp_values(bits, wq, wzp) * xq.astype(np.int64)).sum(axis=1)
         assert np.abs(want).max() < 2 ** 24
         y = orc.matvec_zp(bits, wq, ones_w, wzp, xq, ones_x)
+        assert np.all(np.abs(y) < 2 ** 24), "sums at unit scales are exact integers below 2^24"
         assert np.array_equal(y.astype(np.int64), want)
         y = orc.matvec_zp(bits, wq, ones_w, wzp, xq, ones_x, 1, 3, y=np.full(rows, -7.5, np.float32))
-        assert np.all(y[[0, 3, 4]] == -7.5) and np.array_equal(y[1:3].astype(np.int64), want[1:3])
+        assert np.all(y[[0, 3, 4]] == -7.5) and np.all(np.abs(y[1:3]) < 2 ** 24)
+        assert np.array_equal(y[1:3].astype(np.int64), want[1:3])
 
 
 ALL_CHECKS = [
