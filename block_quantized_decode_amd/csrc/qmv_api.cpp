@@ -73,8 +73,10 @@ qmv_status finish(hipError_t e, const char *name, long grid_hint) {
     return QMV_OK;
 }
 
+// A matrix with no rows may have null data pointers: nothing is read.
 qmv_status check_weight(const qmv_qtensor *W, int want_type) {
-    if (W == nullptr || W->q == nullptr || W->d == nullptr) return QMV_E_ARG;
+    if (W == nullptr) return QMV_E_ARG;
+    if (W->rows != 0 && (W->q == nullptr || W->d == nullptr)) return QMV_E_ARG;
     if (W->type != QMV_Q4_0 && W->type != QMV_Q8_0) return QMV_E_FORMAT;
     if (want_type != 0 && W->type != want_type) return QMV_E_FORMAT;
     if (W->rows < 0 || W->cols <= 0 || (W->cols % QMV_QK) != 0) return QMV_E_SHAPE;
@@ -94,9 +96,9 @@ qmv_status check_weight_align(const qmv_qtensor *W) {
 qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, const float *x,
                        const int8_t *xq, const float *xd, qmv_qact *xq_out, int32_t r0, int32_t r1,
                        void *stream, const float *xn = nullptr, float eps = 0.0f, const float *xu = nullptr) {
-    if (y == nullptr) return QMV_E_ARG;
     qmv_status st = check_weight(W, qtype);
     if (st != QMV_OK) return st;
+    if (y == nullptr && W->rows != 0) return QMV_E_ARG;
     if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
     if (W->cols > 131072 || qmv::rows_lds_bytes(M, W->cols, x != nullptr) > (size_t)QMV_LDS_BYTES)
         return QMV_E_SHAPE;
@@ -181,9 +183,10 @@ qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, c
 
 qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
                 void *stream) {
-    if (X == nullptr || X->q == nullptr || X->d == nullptr || Y == nullptr) return QMV_E_ARG;
+    if (X == nullptr || X->q == nullptr || X->d == nullptr) return QMV_E_ARG;
     qmv_status st = check_weight(W, qtype);
     if (st != QMV_OK) return st;
+    if (Y == nullptr && W->rows != 0) return QMV_E_ARG;
     if (X->type != QMV_Q8_0) return QMV_E_FORMAT;
     if (X->rows < 1 || X->cols != W->cols) return QMV_E_SHAPE;
     if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
@@ -202,8 +205,8 @@ qmv_status gemm(int qtype, float *Y, const qmv_qtensor *W, const qmv_qtensor *X,
 
 qmv_status gemm_packed(int qtype, float *Y, const qmv_packed *P, const qmv_qtensor *X, int32_t r0, int32_t r1,
                        void *stream) {
-    if (P == nullptr || P->q == nullptr || P->d == nullptr) return QMV_E_ARG;
-    if (X == nullptr || X->q == nullptr || X->d == nullptr || Y == nullptr) return QMV_E_ARG;
+    if (P == nullptr || (P->rows != 0 && (P->q == nullptr || P->d == nullptr))) return QMV_E_ARG;
+    if (X == nullptr || X->q == nullptr || X->d == nullptr || (Y == nullptr && P->rows != 0)) return QMV_E_ARG;
     if (P->type != qtype || X->type != QMV_Q8_0) return QMV_E_FORMAT;
     if (P->rows < 0 || P->cols <= 0 || (P->cols % QMV_QK) != 0 || P->cols > 131072) return QMV_E_SHAPE;
     if (X->rows < 1 || X->cols != P->cols) return QMV_E_SHAPE;
@@ -219,7 +222,8 @@ qmv_status gemm_packed(int qtype, float *Y, const qmv_packed *P, const qmv_qtens
 
 qmv_status matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qact *xq_out, int32_t r0, int32_t r1,
                         void *stream) {
-    if (W == nullptr || W->q == nullptr || W->d == nullptr || x == nullptr || y == nullptr) return QMV_E_ARG;
+    if (W == nullptr || x == nullptr) return QMV_E_ARG;
+    if (W->rows != 0 && (W->q == nullptr || W->d == nullptr || y == nullptr)) return QMV_E_ARG;
     if (W->bits != 4 && W->bits != 8) return QMV_E_FORMAT;
     if (W->rows < 0 || W->cols <= 0 || (W->cols % QMV_ZP_BLOCK) != 0 || W->cols > QMV_ZP_MAX_COLS)
         return QMV_E_SHAPE;
@@ -307,9 +311,9 @@ qmv_status qmv_quantize_q8(qmv_qact *out, const float *x, int64_t k, void *strea
 }
 
 qmv_status qmv_quantize_weights(const qmv_qtensor *W, const float *w, void *stream) {
-    if (w == nullptr) return QMV_E_ARG;
     qmv_status st = check_weight(W, 0);
     if (st != QMV_OK) return st;
+    if (w == nullptr && W->rows != 0) return QMV_E_ARG;
     if (!aligned(w, 16)) return QMV_E_ARG;
     if ((st = check_weight_align(W)) != QMV_OK) return st;
     if ((st = device_check(nullptr)) != QMV_OK) return st;
@@ -405,9 +409,10 @@ qmv_status qmv_pack_bytes(int32_t type, int32_t rows, int32_t cols, int64_t *q_b
 }
 
 qmv_status qmv_pack_weights(qmv_packed *P, const qmv_qtensor *W, void *stream) {
-    if (P == nullptr || P->q == nullptr || P->d == nullptr) return QMV_E_ARG;
+    if (P == nullptr) return QMV_E_ARG;
     qmv_status st = check_weight(W, 0);
     if (st != QMV_OK) return st;
+    if (W->rows != 0 && (P->q == nullptr || P->d == nullptr)) return QMV_E_ARG;
     if (W->cols > 131072) return QMV_E_SHAPE;
     if ((st = check_weight_align(W)) != QMV_OK) return st;
     if (!aligned(P->q, 16) || !aligned(P->d, 16)) return QMV_E_ARG;

@@ -83,7 +83,9 @@ enum { QMV_Q4_0 = 4, QMV_Q8_0 = 8 };
 /* A quantized weight matrix (spec section 4, ml_qtensor): rows x cols,
  * q = rows * cols bytes (Q8_0) or rows * cols / 2 bytes (Q4_0),
  * d = rows * cols / 32 floats.  q must be 16-byte aligned, d 4-byte
- * aligned. */
+ * aligned.  Matrices with rows = 0 (here and in qmv_zptensor and
+ * qmv_packed) may have null data pointers, and so may the (empty) outputs
+ * y / Y of the calls on them: nothing is read or written. */
 typedef struct {
     int8_t *q;
     float *d;

@@ -242,6 +242,27 @@ def test_matvec_zp_validation(lib, bits):
     assert g(ctypes.byref(empty), None, 0, None) == OK and empty.n == 0
 
 
+def test_zero_rows_accept_null_pointers(lib):
+    """A matrix without rows may have null data pointers (and a null output):
+    the calls get past argument checking, to the device check (QMV_E_DEVICE
+    or QMV_E_ARCH here), or return QMV_OK where a gfx950 is present."""
+    P = ctypes.c_void_p
+    fine = (OK, E_DEVICE, E_ARCH)
+    W0 = QT(0, 0, 0, 64, Q8)
+    X = QT(A + 0x1000, B + 0x1000, 20, 64, Q8)
+    assert lib.qmv_matvec_q8(None, ctypes.byref(W0), ctypes.byref(_x()), 0, 0, None) in fine
+    assert lib.qmv_gemm_q8(None, ctypes.byref(W0), ctypes.byref(X), 0, 0, None) in fine
+    assert lib.qmv_quantize_weights(ctypes.byref(W0), None, None) in fine
+    assert lib.qmv_pack_weights(ctypes.byref(QT(0, 0, 0, 0, 0)), ctypes.byref(W0), None) in fine
+    assert lib.qmv_gemm_q8_packed(None, ctypes.byref(QT(0, 0, 0, 64, Q8)), ctypes.byref(X), 0, 0, None) in fine
+    f = lib.qmv_matvec_zp_fx
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(None, ctypes.byref(ZT(0, 0, 0, 0, 256, 8)), A + 0x1000, None, 0, 0, None) in fine
+    # with rows, null pointers are still refused
+    assert lib.qmv_matvec_q8(Y, ctypes.byref(QT(0, 0, 8, 64, Q8)), ctypes.byref(_x()), 0, 0, None) == E_ARG
+    assert lib.qmv_matvec_q8(None, ctypes.byref(_w()), ctypes.byref(_x()), 0, 0, None) == E_ARG
+
+
 def test_quantize_validation(lib):
     act = QA(A, B, 0)
     assert lib.qmv_quantize_q8(None, ctypes.c_void_p(Y), ctypes.c_int64(64), None) == E_ARG

@@ -194,3 +194,34 @@ def test_zp_and_packed_graph_replay():
     Yref = orc.gemm(4, wq, wd, xq, xd)
     tol = np.stack([orc.tolerance(4, wq, wd, xq[i], xd[i]) for i in range(24)])
     assert np.all(np.abs(eager[2].astype(np.float64) - Yref) <= tol), "graph packed product"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zp_and_packed_empty(bits):
+    """Zero-row matrices and empty ranges: nothing is written to y, the
+    activation output is still produced, packing zero rows is a no-op.  The
+    zero-row tensors have null data pointers (torch gives empty tensors
+    none), which the calls accept for matrices without rows."""
+    announce(f"zp{bits} and packed, empty cases")
+    rng = np.random.default_rng(5600 + bits)
+    k = 896
+    wq = torch.zeros((0, k if bits == 8 else k // 2), dtype=torch.uint8, device="cuda:0")
+    wd = torch.zeros((0, k // 128), dtype=torch.float32, device="cuda:0")
+    x = _x(rng, k)
+    qo = torch.full((k,), 99, dtype=torch.int8, device="cuda:0")
+    do = torch.full((k // 128,), -1.0, dtype=torch.float32, device="cuda:0")
+    y = torch.full((4,), float(SENTINEL), dtype=torch.float32, device="cuda:0")
+    qmv.qmv_matvec_zp_fx(wq, wd, None, bits, dev(x), 0, 0, y, xq_out=(qo, do))
+    xq, xd = orc.quantize_q8_b128(x)
+    assert np.array_equal(host(qo), xq) and np.array_equal(host(do).view(np.uint32), xd.view(np.uint32))
+    assert np.all(host(y) == SENTINEL)
+    q4 = torch.zeros((0, 1024), dtype=torch.uint8, device="cuda:0")
+    d4 = torch.zeros((0, 64), dtype=torch.float32, device="cuda:0")
+    P = qmv.qmv_pack_weights(q4, d4, 4)
+    assert (P.rows, P.cols) == (0, 2048)
+    wq4, wd4 = synth.raw_q4(rng, 40, 2048)
+    P = qmv.qmv_pack_weights(dev(wq4), dev(wd4), 4)
+    xq2, xd2 = orc.quantize_q8(synth.normal(rng, (20, 2048)))
+    Y = torch.full((20, 40), float(SENTINEL), dtype=torch.float32, device="cuda:0")
+    qmv.qmv_gemm_q4_packed(P, dev(xq2), dev(xd2), 16, 16, Y)
+    assert np.all(host(Y) == SENTINEL)
