@@ -60,6 +60,10 @@ class _Lib:
             "orc_block_sums_zp": [ctypes.c_int, P, P, i32, P, i32, i32, P],
             "orc_matvec_zp": [P, ctypes.c_int, P, P, P, i32, P, P, i32, i32],
             "orc_tol_abs_zp": [ctypes.c_int, P, P, P, i32, P, P, i32, i32, P],
+            "orc_quantize_q8_b256": [P, i64, P, P],
+            "orc_superblock_sums_q4k": [P, P, P, i32, P, i32, i32, P, P],
+            "orc_matvec_q4k": [P, P, P, P, P, P, i32, P, P, i32, i32],
+            "orc_tol_abs_q4k": [P, P, P, P, P, i32, P, P, i32, i32, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -337,4 +341,74 @@ def tolerance_zp(bits, wq, wd, wzp, xq, xd, r0=None, r1=None):
     r1 = rows if r1 is None else r1
     out = np.zeros(r1 - r0, np.float64)
     lib().orc_tol_abs_zp(bits, _p(wq), _p(wd), _zp_ptr(wzp), cols, _p(xq), _p(xd), r0, r1, _p(out))
+    return 1e-5 * out + 1e-6
+
+
+# ---------------------------------------------------------------------------
+# K-quant super-blocks (rules in the C file: "SKaiNET-native-kernels" page).
+# Weights: nibbles uint8 [rows, K/2], sub-block scales and minima uint8
+# [rows, K/32] (0..63), super-block scales d and dmin float32 [rows, K/256].
+SBK = 256
+
+
+def quantize_q8_b256(x):
+    """The Q8_0 rule on 256-element blocks: (q int8 of x.shape, d float32 [..., n/256])."""
+    x = _f32(x)
+    assert x.shape[-1] % SBK == 0
+    q = np.empty(x.shape, np.int8)
+    d = np.empty(x.shape[:-1] + (x.shape[-1] // SBK,), np.float32)
+    lib().orc_quantize_q8_b256(_p(x), x.size, _p(q), _p(d))
+    return q, d
+
+
+def _q4k_args(wq, sc, mn, d=None, dmin=None):
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    sc = np.ascontiguousarray(sc, dtype=np.uint8)
+    mn = np.ascontiguousarray(mn, dtype=np.uint8)
+    rows, nsub = sc.shape
+    cols = nsub * QK
+    assert cols % SBK == 0 and wq.shape == (rows, cols // 2) and mn.shape == (rows, nsub)
+    if d is not None:
+        d = _f32(d)
+        dmin = _f32(dmin)
+        assert d.shape == dmin.shape == (rows, cols // SBK)
+    return wq, sc, mn, d, dmin, rows, cols
+
+
+def superblock_sums_q4k(wq, sc, mn, xq, r0=None, r1=None):
+    """(S1, S2) int32 [r1 - r0, K/256]: S1 = sum_b sc_b * sum_i w_i q_i,
+    S2 = sum_b mn_b * sum_i q_i."""
+    wq, sc, mn, _, _, rows, cols = _q4k_args(wq, sc, mn)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    assert xq.size == cols
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    s1 = np.zeros((r1 - r0, cols // SBK), np.int32)
+    s2 = np.zeros((r1 - r0, cols // SBK), np.int32)
+    lib().orc_superblock_sums_q4k(_p(wq), _p(sc), _p(mn), cols, _p(xq), r0, r1, _p(s1), _p(s2))
+    return s1, s2
+
+
+def matvec_q4k(wq, sc, mn, d, dmin, xq, xd, r0=None, r1=None, y=None):
+    wq, sc, mn, d, dmin, rows, cols = _q4k_args(wq, sc, mn, d, dmin)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    xd = _f32(xd).reshape(-1)
+    assert xq.size == cols and xd.size == cols // SBK
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    if y is None:
+        y = np.zeros(rows, np.float32)
+    lib().orc_matvec_q4k(_p(y), _p(wq), _p(sc), _p(mn), _p(d), _p(dmin), cols, _p(xq), _p(xd), r0, r1)
+    return y
+
+
+def tolerance_q4k(wq, sc, mn, d, dmin, xq, xd, r0=None, r1=None):
+    """Per-row bound 1e-5 * sum_k |dx| (|S1 d| + |S2 dmin|) + 1e-6."""
+    wq, sc, mn, d, dmin, rows, cols = _q4k_args(wq, sc, mn, d, dmin)
+    xq = np.ascontiguousarray(xq, dtype=np.int8).reshape(-1)
+    xd = _f32(xd).reshape(-1)
+    r0 = 0 if r0 is None else r0
+    r1 = rows if r1 is None else r1
+    out = np.zeros(r1 - r0, np.float64)
+    lib().orc_tol_abs_q4k(_p(wq), _p(sc), _p(mn), _p(d), _p(dmin), cols, _p(xq), _p(xd), r0, r1, _p(out))
     return 1e-5 * out + 1e-6

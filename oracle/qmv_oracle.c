@@ -45,6 +45,22 @@
  *                       symmetric formats)
  *   orc_tol_abs_zp      pinned (closed forms)
  *
+ *   orc_quantize_q8_b256  pinned (equal to orc_quantize_q8 where each
+ *                       256-block's 32-blocks share one maximum; one scale
+ *                       per 256 elements)
+ *   orc_superblock_sums_q4k  pinned (the page's own bound 8*63*32*127*15 at
+ *                       the extremes, the nibble layout by one-hot
+ *                       activations, reduction to the Q4_0 sums, int64
+ *                       brute force)
+ *   orc_matvec_q4k      pinned (fp64 brute force within the error bound,
+ *                       exact at unit scales)
+ *   orc_tol_abs_q4k     pinned (fp64 brute force)
+ *
+ * The K-quant super-block functions (orc_*_q4k, orc_quantize_q8_b256)
+ * follow "SKaiNET-native-kernels" (devpost.com), sections "Proving an
+ * optimization is safe before writing it" and "Accomplishments that we're
+ * proud of".
+ *
  * The zero-point format (the orc_*_zp functions) follows a second page:
  * "ONNX Runtime" (opensolvers.com/apps/onnx.html), sections 3 (BlkLen=128
  * CompInt8) and 4 (SQ8Bit: B' = B - 128, block sums scaled by
@@ -478,6 +494,141 @@ void orc_tol_abs_zp(int bits, const uint8_t *wq, const float *wd, const uint8_t 
         for (int32_t b = 0; b < nb; ++b) {
             int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);
             a += fabs((double)sumi * (double)wd[(int64_t)r * nb + b] * (double)xd[b]);
+        }
+        out[r - r0] = a;
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * K-quant super-blocks ("SKaiNET-native-kernels", section "Proving an
+ * optimization is safe before writing it": 4-bit weights w in [0, 15],
+ * 32 elements per sub-block, a 6-bit sub-block scale s <= 63, 8 sub-blocks
+ * per block, int8 activations, and the sub-block scale folded in the
+ * integer domain, sum over b of s_b * (sum over i of a_i * w_i), before one
+ * conversion to float; section "Accomplishments that we're proud of": the
+ * format keeps per-32 asymmetric minima).
+ *
+ * Readings where the page is silent (it gives neither the storage nor the
+ * scale types):
+ *   - weight element i of sub-block b of super-block k of row r has the
+ *     value d[r,k] * sc[r,8k+b] * w_i - dmin[r,k] * mn[r,8k+b]: a 6-bit
+ *     scale and a 6-bit minimum per 32 elements (one byte each, 0..63), two
+ *     fp32 super-block scales per 256 elements;
+ *   - the nibbles of a sub-block take the spec's Q4_0 layout (16 bytes,
+ *     element j in the low nibble of byte j, element j + 16 in the high
+ *     nibble), stored as they are (no offset);
+ *   - the activation is quantized with the spec's Q8_0 rule on 256-element
+ *     blocks, so that one activation scale covers a super-block and the fold
+ *     is one exact integer:
+ *       S1 = sum_b sc_b * (sum_i w_i * q_i),   S2 = sum_b mn_b * (sum_i q_i),
+ *       y[r] = sum over super-blocks, ascending, of
+ *              (((float)S1 * d) - ((float)S2 * dmin)) * dx.
+ *     |S1| <= 8*63*32*127*15 = 30,723,840 and |S2| <= 8*63*32*127 =
+ *     2,048,256, both exact in int32.  S1 can exceed 2^24, so (float)S1
+ *     may round: that conversion is one of the rounded float operations of
+ *     the rule.
+ * ---------------------------------------------------------------------- */
+#define SBK 256
+#define SUBK 32
+
+void orc_quantize_q8_b256(const float *x, int64_t n, int8_t *q, float *d)
+{
+    for (int64_t b = 0; b < n / SBK; ++b) {
+        const float *xb = x + b * SBK;
+        float amax = 0.0f;
+        for (int i = 0; i < SBK; ++i) {
+            float a = fabsf(xb[i]);
+            if (a > amax)
+                amax = a;
+        }
+        float db = amax / 127.0f;
+        float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+        for (int i = 0; i < SBK; ++i) {
+            float v = xb[i] * id;
+            float t = v + copysignf(0.5f, xb[i]);
+            int qi = (int)truncf(t);
+            if (qi > 127)
+                qi = 127;
+            if (qi < -127)
+                qi = -127;
+            q[b * SBK + i] = (int8_t)qi;
+        }
+        d[b] = db;
+    }
+}
+
+/* nibble of element i (0..31) of a 16-byte sub-block, as stored */
+static int q4k_nib(const uint8_t *sub, int i)
+{
+    return (i < 16) ? (sub[i] & 0x0F) : (sub[i - 16] >> 4);
+}
+
+static void q4k_sums(const uint8_t *wq, const uint8_t *sc, const uint8_t *mn, int32_t cols,
+                     const int8_t *xq, int32_t r, int32_t k, int32_t *s1, int32_t *s2)
+{
+    int32_t nsub = cols / SUBK;
+    int64_t a = 0, m = 0;
+    for (int b = 0; b < SBK / SUBK; ++b) {
+        int32_t sb = k * (SBK / SUBK) + b;
+        const uint8_t *sub = wq + (int64_t)r * (cols / 2) + (int64_t)sb * 16;
+        const int8_t *xv = xq + (int64_t)sb * SUBK;
+        int64_t dot = 0, qs = 0;
+        for (int i = 0; i < SUBK; ++i) {
+            dot += (int64_t)q4k_nib(sub, i) * xv[i];
+            qs += xv[i];
+        }
+        a += (int64_t)sc[(int64_t)r * nsub + sb] * dot;
+        m += (int64_t)mn[(int64_t)r * nsub + sb] * qs;
+    }
+    *s1 = (int32_t)a;
+    *s2 = (int32_t)m;
+}
+
+/* s1, s2 each have (r1 - r0) * (cols / 256) entries, row-major. */
+void orc_superblock_sums_q4k(const uint8_t *wq, const uint8_t *sc, const uint8_t *mn, int32_t cols,
+                             const int8_t *xq, int32_t r0, int32_t r1, int32_t *s1, int32_t *s2)
+{
+    int32_t nk = cols / SBK;
+    for (int32_t r = r0; r < r1; ++r)
+        for (int32_t k = 0; k < nk; ++k)
+            q4k_sums(wq, sc, mn, cols, xq, r, k, s1 + (int64_t)(r - r0) * nk + k,
+                     s2 + (int64_t)(r - r0) * nk + k);
+}
+
+void orc_matvec_q4k(float *y, const uint8_t *wq, const uint8_t *sc, const uint8_t *mn,
+                    const float *d, const float *dmin, int32_t cols, const int8_t *xq,
+                    const float *xd, int32_t r0, int32_t r1)
+{
+    int32_t nk = cols / SBK;
+    for (int32_t r = r0; r < r1; ++r) {
+        float s = 0.0f;
+        for (int32_t k = 0; k < nk; ++k) {
+            int32_t s1, s2;
+            q4k_sums(wq, sc, mn, cols, xq, r, k, &s1, &s2);
+            float t = (float)s1 * d[(int64_t)r * nk + k];
+            float u = (float)s2 * dmin[(int64_t)r * nk + k];
+            float v = t - u;
+            v = v * xd[k];
+            s = s + v;
+        }
+        y[r] = s;
+    }
+}
+
+/* A(r) = sum over super-blocks of |dx| * (|S1 * d| + |S2 * dmin|) in binary64:
+ * the scale of the tolerance |y - y_ref| <= 1e-5 * A + 1e-6. */
+void orc_tol_abs_q4k(const uint8_t *wq, const uint8_t *sc, const uint8_t *mn, const float *d,
+                     const float *dmin, int32_t cols, const int8_t *xq, const float *xd,
+                     int32_t r0, int32_t r1, double *out)
+{
+    int32_t nk = cols / SBK;
+    for (int32_t r = r0; r < r1; ++r) {
+        double a = 0.0;
+        for (int32_t k = 0; k < nk; ++k) {
+            int32_t s1, s2;
+            q4k_sums(wq, sc, mn, cols, xq, r, k, &s1, &s2);
+            a += fabs((double)xd[k]) * (fabs((double)s1 * d[(int64_t)r * nk + k]) +
+                                        fabs((double)s2 * dmin[(int64_t)r * nk + k]));
         }
         out[r - r0] = a;
     }

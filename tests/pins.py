@@ -611,6 +611,153 @@ def check_zp_matvec_unit_scales():
         assert np.array_equal(y[1:3].astype(np.int64), want[1:3])
 
 
+# ---------------------------------------------------------------------------
+# K-quant super-blocks ("SKaiNET-native-kernels" page; readings in the
+# oracle's C file): value = d * sc_b * w - dmin * mn_b, 256-element
+# activation blocks, S1 = sum_b sc_b sum_i w_i q_i, S2 = sum_b mn_b sum_i q_i
+# ---------------------------------------------------------------------------
+
+SBK = 256
+
+
+def q4k_nibbles(wq):
+    """[rows, K/2] uint8 -> [rows, K] int64 stored nibbles, per 32-element
+    sub-block: element j < 16 from the low nibble of byte j, element j >= 16
+    from the high nibble of byte j - 16."""
+    rows = wq.shape[0]
+    b = wq.reshape(rows, -1, 16).astype(np.int64)
+    return np.concatenate([b & 0x0F, b >> 4], axis=2).reshape(rows, -1)
+
+
+def _q4k_problem(rng, rows, k):
+    nsub, nk = k // QK, k // SBK
+    wq = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(rows, nsub), dtype=np.uint8)
+    mn = rng.integers(0, 64, size=(rows, nsub), dtype=np.uint8)
+    d = (np.exp2(rng.uniform(-10, -4, size=(rows, nk)))).astype(np.float32)
+    dmin = (np.exp2(rng.uniform(-10, -4, size=(rows, nk)))).astype(np.float32)
+    xq, xd = orc.quantize_q8_b256(rng.standard_normal(k).astype(np.float32))
+    return wq, sc, mn, d, dmin, xq, xd
+
+
+def _q4k_brute_sums(wq, sc, mn, xq):
+    rows = wq.shape[0]
+    w = q4k_nibbles(wq).reshape(rows, -1, QK)
+    a = xq.astype(np.int64).reshape(1, -1, QK)
+    dots = (w * a).sum(axis=2)                        # [rows, nsub]
+    qs = a.sum(axis=2)                                # [1, nsub]
+    s1 = (sc.astype(np.int64) * dots).reshape(rows, -1, 8).sum(axis=2)
+    s2 = (mn.astype(np.int64) * qs).reshape(rows, -1, 8).sum(axis=2)
+    return s1, s2
+
+
+def check_b256_quantize():
+    rng = np.random.default_rng(40)
+    x = rng.uniform(-1, 1, size=512).astype(np.float32)
+    x[::32] = np.where(rng.random(16) < 0.5, -1.5, 1.5).astype(np.float32)
+    q, d = orc.quantize_q8_b256(x)
+    q8, d8 = orc.quantize_q8(x)
+    assert d.shape == (2,) and np.array_equal(q, q8) and np.array_equal(np.repeat(d, 8), d8)
+    x = rng.integers(-60, 61, size=512).astype(np.float32)
+    x[200] = 127.0
+    x[256 + 3] = -127.0
+    q, d = orc.quantize_q8_b256(x)
+    assert np.array_equal(q, x.astype(np.int8)) and np.array_equal(d, np.float32([1.0, 1.0]))
+
+
+def check_q4k_fold_bound():
+    """The page's bound, reached exactly: all nibbles 15, scales 63,
+    activations 127 give S1 = 8*63*32*127*15; minima 63 give S2 =
+    8*63*32*127; negated activations negate both."""
+    g = golden("q4k_fold_bound.json")
+    assert g["fold_bound"] == 8 * 63 * 32 * 127 * 15 and abs(g["fold_bound"] - g["fold_bound_as_printed"]) < 5e4
+    rows, k = 1, 512
+    wq = np.full((rows, k // 2), 0xFF, np.uint8)
+    sc = np.full((rows, k // QK), 63, np.uint8)
+    mn = np.full((rows, k // QK), 63, np.uint8)
+    x = np.full(k, 127, np.int8)
+    s1, s2 = orc.superblock_sums_q4k(wq, sc, mn, x)
+    assert np.all(s1 == g["fold_bound"]) and np.all(s2 == g["min_term_bound"])
+    s1, s2 = orc.superblock_sums_q4k(wq, sc, mn, -x)
+    assert np.all(s1 == -g["fold_bound"]) and np.all(s2 == -g["min_term_bound"])
+
+
+def check_q4k_layout_by_one_hot():
+    """A one-hot activation at element e reads sc_b * nibble(e) and mn_b."""
+    k = 256
+    b = np.arange(128, dtype=np.uint8)
+    wq = ((b % 16) | ((15 - (b % 16)) << 4)).astype(np.uint8).reshape(1, 128)
+    sc = (np.arange(8, dtype=np.uint8) + 1).reshape(1, 8)
+    mn = (np.arange(8, dtype=np.uint8) * 3 + 2).reshape(1, 8)
+    for e in (0, 5, 15, 16, 31, 32, 100, 255):
+        x = np.zeros(k, np.int8)
+        x[e] = 1
+        s1, s2 = orc.superblock_sums_q4k(wq, sc, mn, x)
+        sub, j = divmod(e, 32)
+        byte = int(wq[0, sub * 16 + (j % 16)])
+        nib = (byte & 0x0F) if j < 16 else (byte >> 4)
+        assert s1[0, 0] == int(sc[0, sub]) * nib and s2[0, 0] == int(mn[0, sub]), e
+
+
+def check_q4k_reduces_to_q4_0():
+    """Scales 1 and minima 8 give the values nibble - 8 of Q4_0 (same nibble
+    layout): S1 - S2 is the sum of the (pinned) Q4_0 block sums over the
+    super-block."""
+    rng = np.random.default_rng(41)
+    rows, k = 3, 768
+    wq = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    xq = rng.integers(-127, 128, size=k, dtype=np.int16).astype(np.int8)
+    ones = np.ones((rows, k // QK), np.uint8)
+    s1, s2 = orc.superblock_sums_q4k(wq, ones, 8 * ones, xq)
+    s40 = orc.block_sums(4, wq, xq).reshape(rows, -1, 8).sum(axis=2)
+    assert np.array_equal(s1.astype(np.int64) - s2, s40)
+
+
+def check_q4k_sums_brute():
+    rng = np.random.default_rng(42)
+    rows, k = 5, 1024
+    wq, sc, mn, _, _, _, _ = _q4k_problem(rng, rows, k)
+    xq = rng.integers(-128, 128, size=k, dtype=np.int16).astype(np.int8)
+    s1, s2 = orc.superblock_sums_q4k(wq, sc, mn, xq)
+    b1, b2 = _q4k_brute_sums(wq, sc, mn, xq)
+    assert np.array_equal(s1.astype(np.int64), b1) and np.array_equal(s2.astype(np.int64), b2)
+    s1, s2 = orc.superblock_sums_q4k(wq, sc, mn, xq, 1, 4)
+    assert np.array_equal(s1.astype(np.int64), b1[1:4]) and np.array_equal(s2.astype(np.int64), b2[1:4])
+
+
+def check_q4k_matvec_brute64():
+    rng = np.random.default_rng(43)
+    for rows, k in ((1, 256), (7, 768), (3, 256 * 22)):
+        wq, sc, mn, d, dmin, xq, xd = _q4k_problem(rng, rows, k)
+        y = orc.matvec_q4k(wq, sc, mn, d, dmin, xq, xd)
+        w = q4k_nibbles(wq).astype(np.float64).reshape(rows, -1, QK)
+        scale = (np.repeat(d.astype(np.float64), 8, axis=1) * sc)[:, :, None]
+        minv = (np.repeat(dmin.astype(np.float64), 8, axis=1) * mn)[:, :, None]
+        wdeq = (scale * w - minv).reshape(rows, k)
+        xdeq = (xq.astype(np.float64).reshape(-1, SBK) * xd.astype(np.float64)[:, None]).reshape(k)
+        y64 = wdeq @ xdeq
+        b1, b2 = _q4k_brute_sums(wq, sc, mn, xq)
+        a64 = (np.abs(xd.astype(np.float64))[None, :] *
+               (np.abs(b1 * d.astype(np.float64)) + np.abs(b2 * dmin.astype(np.float64)))).sum(axis=1)
+        assert np.all(np.abs(y.astype(np.float64) - y64) <= 1e-5 * a64 + 1e-6), "fp64 brute force"
+        assert np.allclose(orc.tolerance_q4k(wq, sc, mn, d, dmin, xq, xd), 1e-5 * a64 + 1e-6, rtol=1e-12, atol=0)
+
+
+def check_q4k_unit_scales():
+    """d = dmin = dx = 1: y = sum over super-blocks of S1 - S2, exact."""
+    rng = np.random.default_rng(44)
+    rows, k = 4, 512
+    wq, sc, mn, _, _, _, _ = _q4k_problem(rng, rows, k)
+    sc = (sc % 4).astype(np.uint8)
+    xq = rng.integers(-20, 21, size=k, dtype=np.int16).astype(np.int8)
+    one = np.ones((rows, k // SBK), np.float32)
+    y = orc.matvec_q4k(wq, sc, mn, one, one, xq, np.ones(k // SBK, np.float32))
+    b1, b2 = _q4k_brute_sums(wq, sc, mn, xq)
+    want = (b1 - b2).sum(axis=1)
+    assert np.abs(b1).max() < 2 ** 24 and np.all(np.abs(y) < 2 ** 24)
+    assert np.array_equal(y.astype(np.int64), want)
+
+
 ALL_CHECKS = [
     check_q8_zero_block, check_q8_equal_block, check_q8_clamp_and_range,
     check_q8_unit_scale_textbook, check_q8_ties, check_q8_detectors,
@@ -624,6 +771,8 @@ ALL_CHECKS = [
     check_b128_quantize, check_zp_block_sum_closed_forms, check_zp_nibble_order,
     check_zp_reduces_to_symmetric, check_zp_block_sums_brute, check_zp_matvec_brute64,
     check_zp_matvec_unit_scales,
+    check_b256_quantize, check_q4k_fold_bound, check_q4k_layout_by_one_hot, check_q4k_reduces_to_q4_0,
+    check_q4k_sums_brute, check_q4k_matvec_brute64, check_q4k_unit_scales,
 ]
 
 

@@ -65,6 +65,21 @@ MUTANTS = [
     ("zp_q4_row_stride", "const uint8_t *row = wq + (int64_t)r * (bits == 8 ? cols : cols / 2);", "const uint8_t *row = wq + (int64_t)r * cols / 2;", 1),
     ("zp_per_block_only", "return wzp[(int64_t)r * nb + b];", "return wzp[b];", 1),
     ("zp_sign", "s += (int32_t)(zp_code(row, bits, e) - zp) * (int32_t)xq[e];", "s += (int32_t)(zp - zp_code(row, bits, e)) * (int32_t)xq[e];", 1),
+    ("b256_max_first_32", "for (int i = 0; i < SBK; ++i) {\n            float a = fabsf(xb[i]);",
+     "for (int i = 0; i < 32; ++i) {\n            float a = fabsf(xb[i]);", 1),
+    ("q4k_nibbles_swapped", "return (i < 16) ? (sub[i] & 0x0F) : (sub[i - 16] >> 4);",
+     "return (i < 16) ? (sub[i] >> 4) : (sub[i - 16] & 0x0F);", 1),
+    ("q4k_nibbles_interleaved", "return (i < 16) ? (sub[i] & 0x0F) : (sub[i - 16] >> 4);",
+     "return (i % 2 == 0) ? (sub[i / 2] & 0x0F) : (sub[i / 2] >> 4);", 1),
+    ("q4k_offset_8", "dot += (int64_t)q4k_nib(sub, i) * xv[i];", "dot += (int64_t)(q4k_nib(sub, i) - 8) * xv[i];", 1),
+    ("q4k_no_min", "float v = t - u;", "float v = t;", 1),
+    ("q4k_min_sign", "float v = t - u;", "float v = t + u;", 1),
+    ("q4k_d_dmin_swapped", "float t = (float)s1 * d[(int64_t)r * nk + k];\n            float u = (float)s2 * dmin[(int64_t)r * nk + k];",
+     "float t = (float)s1 * dmin[(int64_t)r * nk + k];\n            float u = (float)s2 * d[(int64_t)r * nk + k];", 1),
+    ("q4k_scale_per_superblock", "a += (int64_t)sc[(int64_t)r * nsub + sb] * dot;", "a += (int64_t)sc[(int64_t)r * nsub + k * 8] * dot;", 1),
+    ("q4k_min_times_nibbles", "qs += xv[i];", "qs += (int64_t)q4k_nib(sub, i) * xv[i];", 1),
+    ("q4k_min_from_scale", "m += (int64_t)mn[(int64_t)r * nsub + sb] * qs;", "m += (int64_t)sc[(int64_t)r * nsub + sb] * qs;", 1),
+    ("q4k_dx_dropped", "v = v * xd[k];", "v = v * 1.0f;", 1),
     ("zp_acc_skips_last", "for (int32_t b = 0; b < nb; ++b) {\n            int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);\n            float t",
      "for (int32_t b = 0; b + 1 < nb; ++b) {\n            int32_t sumi = zp_block_sum(bits, wq, wzp, cols, xq, r, b);\n            float t", 1),
 ]
