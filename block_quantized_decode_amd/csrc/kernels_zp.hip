@@ -45,11 +45,14 @@
 #include <stdio.h>
 
 #include "launch.h"
+#include "rowstream.h"
 
 namespace qmv {
 namespace {
 
-typedef int v4i_zp __attribute__((ext_vector_type(4)));
+using rs::kWpb;
+using rs::kOOB;
+using rs::v4i;
 
 #ifndef QMV_ZP_D12  // register ring depth for 1-2 chunks per lane
 #define QMV_ZP_D12 4
@@ -57,100 +60,35 @@ typedef int v4i_zp __attribute__((ext_vector_type(4)));
 #ifndef QMV_ZP_D34  // ... and for 3-4 chunks per lane
 #define QMV_ZP_D34 3
 #endif
-#ifndef QMV_ZP_WG_PER_CU_SCALE  // scales the workgroups per compute unit
-#define QMV_ZP_WG_PER_CU_SCALE 1
-#endif
-#ifndef QMV_ZP_FORCE_P  // 0: wavefronts per row chosen by shape
-#define QMV_ZP_FORCE_P 0
-#endif
 
-constexpr int BLK = 128;               // elements per block
-#ifndef QMV_ZP_QBATCH
-#define QMV_ZP_QBATCH 2
-#endif
-constexpr int kQBatch = QMV_ZP_QBATCH;  // block pairs whose loads a wavefront issues together
-constexpr int kWpb = 8;                // wavefronts per workgroup
-constexpr int kOOBz = 0x7FFFFFF0;      // an offset beyond every descriptor range used here
-constexpr int kBufFlagsZ = 0x00020000; // buffer descriptor word 3: raw 32-bit data
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
-    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kBufFlagsZ);
-}
-
-// The Q8_0 rounding of one element (spec section 5): v = x * id,
-// t = v + copysign(0.5, x), q = trunc(t), each operation rounded on its own.
-__device__ __forceinline__ int q8_round(float x, float id) {
-#pragma clang fp contract(off)
-    float v = x * id;
-    float t = v + copysignf(0.5f, x);
-    int q = (int)t;
-    return min(max(q, -127), 127);
-}
-
-// Reductions over each half-wavefront (lanes 0-31 and 32-63): DPP within
-// rows of 16 lanes (swap neighbours, swap pairs, mirror 8, mirror 16), then
-// the four row values read out and combined per half.  Max is exact and the
-// integer sum is exact, so the order does not matter.
-template <typename F>
-__device__ __forceinline__ int half_reduce(int v, F op) {
-    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
-    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
-    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
-    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
-    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    const int lane = threadIdx.x & 63;
-    return lane < 32 ? op(r0, r1) : op(r2, r3);
-}
+constexpr int BLK = 128;    // elements per block
+constexpr int kQBatch = 2;  // block pairs whose loads a wavefront issues together
 
 // Quantize the 128-element block held by this half-wavefront (lane c of the
-// half holds elements 4c .. 4c + 3): amax exact, d = amax / 127,
-// id = 127 / amax (both correctly rounded divisions), then q8_round.
+// half holds elements 4c .. 4c + 3): amax exact (maximum over the half by
+// DPP within rows and lane reads across them; non-negative floats order like
+// their bit patterns), d = amax / 127, id = 127 / amax (correctly rounded
+// divisions), then the spec's rounding; qsum = the sum of the 128 quants.
 __device__ __forceinline__ void quant_half(float4 v, int (&q)[4], float &d, int &qsum) {
     const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    // non-negative floats order like their bit patterns
-    const float amax = __int_as_float(half_reduce(__float_as_int(m), [](int a, int b) { return max(a, b); }));
+    const auto imax = [](int a, int b) { return max(a, b); };
+    const auto isum = [](int a, int b) { return a + b; };
+    int r0, r1, r2, r3;
+    rs::row_values(rs::row16_reduce(__float_as_int(m), imax), r0, r1, r2, r3);
+    const bool hi = (threadIdx.x & 32) != 0;
+    const float amax = __int_as_float(hi ? max(r2, r3) : max(r0, r1));
     d = amax / 127.0f;
     const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
-    q[0] = q8_round(v.x, id);
-    q[1] = q8_round(v.y, id);
-    q[2] = q8_round(v.z, id);
-    q[3] = q8_round(v.w, id);
-    qsum = half_reduce(q[0] + q[1] + q[2] + q[3], [](int a, int b) { return a + b; });
+    q[0] = rs::q8_round(v.x, id);
+    q[1] = rs::q8_round(v.y, id);
+    q[2] = rs::q8_round(v.z, id);
+    q[3] = rs::q8_round(v.w, id);
+    rs::row_values(rs::row16_reduce(q[0] + q[1] + q[2] + q[3], isum), r0, r1, r2, r3);
+    qsum = hi ? r2 + r3 : r0 + r1;
 }
 
 // position of element e of a block in the 4-bit activation order
 __device__ __forceinline__ int perm4(int e) { return (e & ~7) + ((e & 1) << 2) + ((e & 7) >> 1); }
-
-__device__ __forceinline__ int dpp_x1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
-__device__ __forceinline__ int dpp_x2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ int dpp_m8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
-
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over an aligned group of L lanes (16, 32 or 64), the same value in
-// every lane of the group, in a fixed order: DPP within each 16-lane row
-// (neighbour swap, pair swap, mirror 8, mirror 16: after each step the value
-// is uniform over 2, 4, 8, 16 lanes), then the rows' values read out and
-// added ((r0 + r1) + (r2 + r3) for L = 64).
-template <int L>
-__device__ __forceinline__ float group_sum(float v) {
-    v = v + dppf<0xB1>(v);
-    v = v + dppf<0x4E>(v);
-    v = v + dppf<0x141>(v);
-    v = v + dppf<0x140>(v);
-    if constexpr (L == 16) return v;
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 48));
-    if constexpr (L == 32) return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
-    return (r0 + r1) + (r2 + r3);
-}
 
 template <int BITS, int L, int J, int D, int P>
 __global__ void __launch_bounds__(64 * kWpb)
@@ -158,76 +96,25 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
      const uint8_t *__restrict__ wzp, int32_t rows, int32_t K, const float *__restrict__ x,
      int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1, int32_t rows_wg) {
     constexpr int LB = BITS == 8 ? 8 : 4;  // lanes (16-byte chunks) per block
-    constexpr int GPW = 64 / L;            // row groups per wavefront
     static_assert(L >= LB && (L & (L - 1)) == 0 && L <= 64, "group size");
     static_assert(P == 1 || (L == 64 && kWpb % P == 0), "teams of P wavefronts share rows of 64-lane groups");
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = K / BLK;
-    int8_t *xs = reinterpret_cast<int8_t *>(smem);
-    float *sd = reinterpret_cast<float *>(smem + K);
-    int *sq = reinterpret_cast<int *>(smem + K + 4 * nb);
+    int8_t *xs = reinterpret_cast<int8_t *>(smem);                          // [K]
+    float *sd = reinterpret_cast<float *>(smem + K);                        // [nb] block scales
+    int *sq = reinterpret_cast<int *>(smem + K + 4 * nb);                   // [nb] sums of the quants
+    float *part = reinterpret_cast<float *>(smem + ((K + 8 * nb + 15) & ~15));  // P > 1: [rows_wg][P]
 
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-
-    // ---- phase B: rows
-    //   P = 1: group g of L lanes takes rows r0 + g, r0 + g + G, ... (G groups
-    //   in the grid), each row in W windows of L * J chunks, in order.
-    //   P > 1: workgroup b takes rows_wg consecutive rows; its 8 / P teams of P
-    //   wavefronts take every (8 / P)-th of them, and wavefront q of a team
-    //   takes windows q, q + P, ... of the team's rows.  The P partial sums of
-    //   a row meet in LDS and are added in wavefront order at the end.
     const int row_bytes = BITS == 8 ? K : K / 2;
     const int chunks = row_bytes >> 4;
-    const int W = (chunks + L * J - 1) / (L * J);  // windows per row
     const int gl = lane & (L - 1);
-    const int nrow = r1 - r0;
-    constexpr int TPW = kWpb / P;                  // teams per workgroup (P > 1)
-    const int tm = wid / P, pw = wid % P;
-    const int rb0 = r0 + blockIdx.x * rows_wg;     // P > 1: this workgroup's rows
-    const int rows_here = P > 1 ? max(0, min(rows_wg, r1 - rb0)) : 0;
-    const int rows_team = P > 1 ? (rows_here - tm + TPW - 1) / TPW : 0;
-    const int rows_team_max = P > 1 ? (rows_wg + TPW - 1) / TPW : 0;  // workgroup-uniform
-    const int wpw = (W + P - 1) / P;                                   // windows per wavefront and row
-    const int G = gridDim.x * kWpb * GPW;               // P = 1: row groups in the grid
-    const int g0 = (blockIdx.x * kWpb + wid) * GPW;     // this wavefront's first group
-    const int g = g0 + lane / L;
-    const int rows_g = g < nrow ? (nrow - g + G - 1) / G : 0;
-    const int rows_w = g0 < nrow ? (nrow - g0 + G - 1) / G : 0;  // the wavefront's first group has the most
-    const int items = P > 1 ? rows_team_max * wpw : rows_w * W;   // wave-uniform loop count
-    float *part = reinterpret_cast<float *>(smem + ((K + 8 * nb + 15) & ~15));  // P > 1: [rows_wg][P]
+    const rs::RowMap<L, P> map(chunks, J, r0, r1, rows_wg);
 
-    // item t of this lane group: its row, window, and whether it starts or
-    // ends the row's accumulation
-    struct Item {
-        int r, win, li;
-        bool live, first, last;
-    };
-    auto item = [&](int t) __attribute__((always_inline)) {
-        Item it;
-        if constexpr (P == 1) {
-            const int rl = t / W;
-            it.win = t - rl * W;
-            it.live = rl < rows_g;
-            it.r = r0 + g + rl * G;
-            it.li = 0;
-            it.first = it.win == 0;
-            it.last = it.win == W - 1;
-        } else {
-            const int i = t / wpw, k = t - i * wpw;
-            it.win = pw + P * k;
-            it.li = tm + TPW * i;
-            it.live = i < rows_team && it.win < W;
-            it.r = rb0 + it.li;
-            it.first = k == 0;
-            it.last = k == wpw - 1;
-        }
-        return it;
-    };
-
-    const __amdgpu_buffer_rsrc_t rq = rsrc(wq, (int64_t)rows * row_bytes);
-    const __amdgpu_buffer_rsrc_t rd = rsrc(wd, (int64_t)rows * nb * 4);
-    const __amdgpu_buffer_rsrc_t rz = rsrc(wzp, wzp != nullptr ? (int64_t)rows * nb : 0);
+    const __amdgpu_buffer_rsrc_t rq = rs::rsrc(wq, (int64_t)rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t rd = rs::rsrc(wd, (int64_t)rows * nb * 4);
+    const __amdgpu_buffer_rsrc_t rz = rs::rsrc(wzp, wzp != nullptr ? (int64_t)rows * nb : 0);
     const int zdef = 1 << (BITS - 1);
     constexpr int off = BITS == 8 ? 128 : 0;  // bias of the dotted codes
 
@@ -237,19 +124,19 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     // block and lane).
     constexpr int JM = (J + LB - 1) / LB;
     struct Buf {
-        v4i_zp w[J];
+        v4i w[J];
         float dw[JM];
         int zp[JM];
     };
     auto load = [&](Buf &bf, int t) __attribute__((always_inline)) {
-        const Item it = item(t);
+        const rs::Item it = map.item(t);
         const int r = it.r;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int c = (it.win * J + j) * L + gl;  // chunk of the row
             const bool ok = it.live && c < chunks;
             bf.w[j] = __builtin_bit_cast(
-                v4i_zp, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? r * row_bytes + 16 * c : kOOBz, 0, 2));
+                v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? r * row_bytes + 16 * c : kOOB, 0, 2));
         }
         const int sub = gl % LB;
 #pragma unroll
@@ -259,9 +146,9 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             const bool ok = it.live && jj < J && c < chunks;
             const int b = c / LB;
             bf.dw[m] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (r * nb + b) : kOOBz, 0, 0));
+                float, __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (r * nb + b) : kOOB, 0, 0));
             if (wzp != nullptr)
-                bf.zp[m] = (int)__builtin_amdgcn_raw_buffer_load_b8(rz, ok ? r * nb + b : kOOBz, 0, 0);
+                bf.zp[m] = (int)__builtin_amdgcn_raw_buffer_load_b8(rz, ok ? r * nb + b : kOOB, 0, 0);
             else
                 bf.zp[m] = zdef;
         }
@@ -269,7 +156,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 
     float acc = 0.0f;
     auto compute = [&](const Buf &bf, int t) __attribute__((always_inline)) {
-        const Item it = item(t);
+        const rs::Item it = map.item(t);
         if (it.first) acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -279,12 +166,12 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             const int sub = c % LB;
             int p = 0;
             if constexpr (BITS == 8) {
-                const v4i_zp xv = *reinterpret_cast<const v4i_zp *>(xs + b * BLK + 16 * sub);
+                const v4i xv = *reinterpret_cast<const v4i *>(xs + b * BLK + 16 * sub);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) p = __builtin_amdgcn_sdot4(bf.w[j][k] ^ (int)0x80808080, xv[k], p, false);
             } else {
-                const v4i_zp xe = *reinterpret_cast<const v4i_zp *>(xs + b * BLK + 32 * sub);
-                const v4i_zp xo = *reinterpret_cast<const v4i_zp *>(xs + b * BLK + 32 * sub + 16);
+                const v4i xe = *reinterpret_cast<const v4i *>(xs + b * BLK + 32 * sub);
+                const v4i xo = *reinterpret_cast<const v4i *>(xs + b * BLK + 32 * sub + 16);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     // dword k covers elements 8k .. 8k + 7 of the chunk: even ones in the
@@ -297,9 +184,9 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
                 }
             }
             // exact block sum in every lane of the block
-            p += dpp_x1(p);
-            p += dpp_x2(p);
-            if constexpr (LB == 8) p += dpp_m8(p);
+            p += rs::dppi<rs::kX1>(p);
+            p += rs::dppi<rs::kX2>(p);
+            if constexpr (LB == 8) p += rs::dppi<rs::kM8>(p);
             if (ok && sub == j % LB) {
 #pragma clang fp contract(off)
                 const int sumi = p - (bf.zp[j / LB] - off) * sq[b];
@@ -309,12 +196,12 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             }
         }
         if (it.last) {
-            const float s = group_sum<L>(acc);
+            const float s = rs::group_sum<L>(acc);
             if constexpr (P == 1) {
                 if (it.live && gl == 0) y[it.r] = s;
             } else {
                 // this wavefront's share of the row (0 if it had no window of it)
-                if (it.li < rows_here && gl == 0) part[it.li * P + pw] = s;
+                if (it.li < map.rows_here && gl == 0) part[it.li * P + map.pw] = s;
             }
         }
     };
@@ -366,6 +253,8 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     }
     __syncthreads();
 
+    // ---- phase B: the rows
+    const int items = map.items;
     for (int t0 = 0; t0 < items; t0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -378,11 +267,11 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     }
     if constexpr (P > 1) {
         __syncthreads();
-        for (int li = threadIdx.x; li < rows_here; li += 64 * kWpb) {
+        for (int li = threadIdx.x; li < map.rows_here; li += 64 * kWpb) {
             float s = part[li * P];
 #pragma unroll
             for (int q = 1; q < P; ++q) s += part[li * P + q];
-            y[rb0 + li] = s;
+            y[map.rb0 + li] = s;
         }
     }
 }
@@ -418,56 +307,34 @@ hipError_t launch_j(const ZpArgs &a, int J, int grid, int rows_wg, size_t lds, h
     }
 }
 
-// J chunks per lane per window (at most 8) for rows of `chunks` chunks split
-// over P wavefronts: the windows of a row as even as possible.
-int pick_j(int chunks, int P) {
-    const int per = (chunks + P - 1) / P;  // chunks per wavefront and row
-    const int win = (per + 64 * 8 - 1) / (64 * 8);
-    return (per + 64 * win - 1) / (64 * win);
-}
-
 template <int BITS>
 hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
     const int chunks = (BITS == 8 ? a.K : a.K / 2) / 16;
     const size_t lds_x = ((size_t)a.K + 8 * (size_t)(a.K / BLK) + 15) & ~(size_t)15;
     const int nrow = a.r1 - a.r0;
-    // lanes per row: the fewest power of two (16 .. 64) that covers a row
-    int L = 64;
-    if (chunks <= 16) L = 16;
-    else if (chunks <= 32) L = 32;
-    const int wgpc = L < 64 || pick_j(chunks, 1) == 1 ? 4 : 2;  // workgroups per compute unit
-    const int waves = QMV_ZP_WG_PER_CU_SCALE * wgpc * num_cu * kWpb;
-    // rows shared by a team of P wavefronts when there are fewer than two
-    // rows per wavefront and each row has at least two windows' worth
-    int P = 1;
-    if (L == 64 && chunks >= 128) {
-        while (P < kWpb && (int64_t)nrow * P < 2 * (int64_t)waves && chunks / (2 * P) >= 64) P *= 2;
-    }
-#if QMV_ZP_FORCE_P
-    if (L == 64) P = QMV_ZP_FORCE_P;
-#endif
-    if (P == 1) {
-        const int groups_per_wg = kWpb * (64 / L);
+    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, BITS == 8 ? 8 : 4);
+    const int waves = sh.wgpc * num_cu * kWpb;
+    if (sh.P == 1) {
+        const int groups_per_wg = kWpb * (64 / sh.L);
         int grid = (nrow + groups_per_wg - 1) / groups_per_wg;
         if (grid > waves / kWpb) grid = waves / kWpb;
         if (grid < 1) grid = 1;
-        if (L == 16) return launch_cfg<BITS, 16, 1, 1>(a, grid, 0, lds_x, s, name);
-        if (L == 32) return launch_cfg<BITS, 32, 1, 1>(a, grid, 0, lds_x, s, name);
-        return launch_j<BITS, 1>(a, pick_j(chunks, 1), grid, 0, lds_x, s, name);
+        if (sh.L == 16) return launch_cfg<BITS, 16, 1, 1>(a, grid, 0, lds_x, s, name);
+        if (sh.L == 32) return launch_cfg<BITS, 32, 1, 1>(a, grid, 0, lds_x, s, name);
+        return launch_j<BITS, 1>(a, sh.J, grid, 0, lds_x, s, name);
     }
     // P > 1: consecutive rows per workgroup, enough workgroups to give each
     // wavefront work, partial sums in LDS (at most 8 KiB of them)
     int grid = waves / kWpb;
     int rows_wg = (nrow + grid - 1) / grid;
     if (rows_wg < 1) rows_wg = 1;
-    if (rows_wg * P > 2048) rows_wg = 2048 / P;
+    if (rows_wg * sh.P > 2048) rows_wg = 2048 / sh.P;
     grid = (nrow + rows_wg - 1) / rows_wg;
     if (grid < 1) grid = 1;
-    const size_t lds = lds_x + (size_t)rows_wg * P * 4;
-    const int J = pick_j(chunks, P);
-    if (P == 2) return launch_j<BITS, 2>(a, J, grid, rows_wg, lds, s, name);
-    if (P == 4) return launch_j<BITS, 4>(a, J, grid, rows_wg, lds, s, name);
-    return launch_j<BITS, 8>(a, J, grid, rows_wg, lds, s, name);
+    const size_t lds = lds_x + (size_t)rows_wg * sh.P * 4;
+    if (sh.P == 2) return launch_j<BITS, 2>(a, sh.J, grid, rows_wg, lds, s, name);
+    if (sh.P == 4) return launch_j<BITS, 4>(a, sh.J, grid, rows_wg, lds, s, name);
+    return launch_j<BITS, 8>(a, sh.J, grid, rows_wg, lds, s, name);
 }
 
 __global__ void __launch_bounds__(256)

@@ -74,6 +74,22 @@ size_t zp_lds_bytes(int32_t K);
 hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name);
 hipError_t launch_quant_b128(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name);
 
+// The matvec on K-quant super-blocks (kernels_q4k.hip).
+struct Q4kArgs {
+    float *y;
+    const uint8_t *wq;         // nibbles, rows x K/2
+    const uint8_t *sc, *mn;    // rows x K/32 sub-block scales and minima (0..63)
+    const float *d, *dmin;     // rows x K/256
+    int32_t rows, K;
+    const float *x;            // float32 activation, K
+    int8_t *xq_out;            // optional: the quantized activation (K) ...
+    float *xd_out;             // ... and its scales (K/256)
+    int32_t r0, r1;
+};
+size_t q4k_lds_bytes(int32_t K);
+hipError_t launch_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **name);
+hipError_t launch_quant_b256(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name);
+
 // Pack-once layout of Q4_0 / Q8_0 weights for the matrix-core product (units
 // of 16 rows x 4 blocks in the A operand's lane order): sizes in bytes of the
 // packed quants and scales, and the packing launch (a pure permutation).

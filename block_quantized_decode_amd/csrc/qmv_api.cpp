@@ -258,6 +258,46 @@ qmv_status matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qac
     return finish(e, name, (long)(r1 - r0));
 }
 
+qmv_status matvec_q4k_fx(float *y, const qmv_q4ktensor *W, const float *x, qmv_qact *xq_out, int32_t r0, int32_t r1,
+                         void *stream) {
+    if (W == nullptr || x == nullptr) return QMV_E_ARG;
+    if (W->rows != 0 && (W->q == nullptr || W->sc == nullptr || W->mn == nullptr || W->d == nullptr ||
+                         W->dmin == nullptr || y == nullptr))
+        return QMV_E_ARG;
+    if (W->rows < 0 || W->cols <= 0 || (W->cols % QMV_Q4K_BLOCK) != 0 || W->cols > QMV_Q4K_MAX_COLS)
+        return QMV_E_SHAPE;
+    if ((int64_t)W->rows * (W->cols / 2) > INT32_MAX) return QMV_E_SHAPE;
+    if (r0 < 0 || r1 > W->rows || r0 > r1) return QMV_E_SHAPE;
+    if (!aligned(W->q, 16) || !aligned(W->d, 4) || !aligned(W->dmin, 4) || !aligned(x, 16) || !aligned(y, 4))
+        return QMV_E_ARG;
+    if (xq_out != nullptr && (xq_out->q == nullptr || xq_out->d == nullptr || !aligned(xq_out->q, 16) ||
+                              !aligned(xq_out->d, 4)))
+        return QMV_E_ARG;
+    int dev = -1;
+    qmv_status st = device_check(&dev);
+    if (st != QMV_OK) return st;
+    if (xq_out != nullptr) xq_out->n = W->cols;
+    if (r0 == r1 && xq_out == nullptr) return QMV_OK;
+    qmv::Q4kArgs a = {};
+    a.y = y;
+    a.wq = W->q;
+    a.sc = W->sc;
+    a.mn = W->mn;
+    a.d = W->d;
+    a.dmin = W->dmin;
+    a.rows = W->rows;
+    a.K = W->cols;
+    a.x = x;
+    a.xq_out = xq_out != nullptr ? xq_out->q : nullptr;
+    a.xd_out = xq_out != nullptr ? xq_out->d : nullptr;
+    a.r0 = r0;
+    a.r1 = r1;
+    const char *name = "";
+    const int ncu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+    hipError_t e = qmv::launch_q4k(a, ncu, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)(r1 - r0));
+}
+
 // ceil(M / 64) matrix-core passes over the weights (row-major wq / wd, or
 // packed pq / pd)
 qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, const void *pq, const float *pd,
@@ -397,6 +437,29 @@ qmv_status qmv_quantize_q8_b128(qmv_qact *out, const float *x, int64_t k, void *
 qmv_status qmv_matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qact *xq, int32_t r0, int32_t r1,
                             void *stream) {
     return matvec_zp_fx(y, W, x, xq, r0, r1, stream);
+}
+
+qmv_status qmv_quantize_q8_b256(qmv_qact *out, const float *x, int64_t k, void *stream) {
+    if (out == nullptr) return QMV_E_ARG;
+    if (k < 0 || (k % QMV_Q4K_BLOCK) != 0 || k > INT32_MAX) return QMV_E_SHAPE;
+    if (k == 0) {
+        out->n = 0;
+        return QMV_OK;
+    }
+    if (out->q == nullptr || out->d == nullptr || x == nullptr) return QMV_E_ARG;
+    if (!aligned(x, 16) || !aligned(out->q, 16) || !aligned(out->d, 4)) return QMV_E_ARG;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    out->n = (int32_t)k;
+    const char *name = "";
+    hipError_t e =
+        qmv::launch_quant_b256(out->q, out->d, x, k / QMV_Q4K_BLOCK, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)(k / QMV_Q4K_BLOCK));
+}
+
+qmv_status qmv_matvec_q4k_fx(float *y, const qmv_q4ktensor *W, const float *x, qmv_qact *xq, int32_t r0, int32_t r1,
+                             void *stream) {
+    return matvec_q4k_fx(y, W, x, xq, r0, r1, stream);
 }
 
 qmv_status qmv_pack_bytes(int32_t type, int32_t rows, int32_t cols, int64_t *q_bytes, int64_t *d_bytes) {

@@ -48,6 +48,11 @@ class ZpTensor(ctypes.Structure):
                 ("cols", ctypes.c_int32), ("bits", ctypes.c_uint8)]
 
 
+class Q4kTensor(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("sc", ctypes.c_void_p), ("mn", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("dmin", ctypes.c_void_p), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
 class Packed(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("rows", ctypes.c_int32),
                 ("cols", ctypes.c_int32), ("type", ctypes.c_uint8)]
@@ -81,6 +86,9 @@ _SIGS = {
     "qmv_gemm_q4_packed": [_P, ctypes.POINTER(Packed), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_quantize_q8_b128": [ctypes.POINTER(QAct), _P, ctypes.c_int64, _P],
     "qmv_matvec_zp_fx": [_P, ctypes.POINTER(ZpTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_quantize_q8_b256": [ctypes.POINTER(QAct), _P, ctypes.c_int64, _P],
+    "qmv_matvec_q4k_fx": [_P, ctypes.POINTER(Q4kTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32,
+                          _P],
     "qmv_device_check": [],
 }
 
@@ -408,6 +416,50 @@ def qmv_matvec_zp_fx(wq, wd, wzp, bits, x, r0=None, r1=None, y=None, xq_out=None
     return y
 
 
+Q4K_BLOCK = 256
+
+
+def q4ktensor(q, sc, mn, d, dmin) -> Q4kTensor:
+    """Describe a device K-quant matrix: q uint8 [rows, K/2], sc and mn uint8
+    [rows, K/32], d and dmin float32 [rows, K/256]."""
+    for t in (q, sc, mn):
+        _dev(t, (torch.uint8, torch.int8))
+    _dev(d, torch.float32)
+    _dev(dmin, torch.float32)
+    rows = sc.shape[0]
+    cols = sc.shape[-1] * QK
+    return Q4kTensor(q.data_ptr(), sc.data_ptr(), mn.data_ptr(), d.data_ptr(), dmin.data_ptr(), rows, cols)
+
+
+def qmv_quantize_q8_b256(x: torch.Tensor):
+    """The Q8_0 rule on 256-element blocks: (q int8 like x, d float32 [..., K/256])."""
+    _dev(x, torch.float32)
+    q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    d = torch.empty(x.shape[:-1] + (x.shape[-1] // Q4K_BLOCK,), dtype=torch.float32, device=x.device)
+    act = QAct(q.data_ptr(), d.data_ptr(), 0)
+    _check(lib().qmv_quantize_q8_b256(ctypes.byref(act), x.data_ptr(), x.numel(), _stream()), "qmv_quantize_q8_b256")
+    return q, d
+
+
+def qmv_matvec_q4k_fx(q, sc, mn, d, dmin, x, r0=None, r1=None, y=None, xq_out=None):
+    """y = W q8_b256(x) on K-quant super-blocks (see include/qmv.h)."""
+    W = q4ktensor(q, sc, mn, d, dmin)
+    _dev(x, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    if y is None:
+        y = torch.zeros(W.rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32)
+    act = None
+    if xq_out is not None:
+        xq, xd = xq_out
+        act = QAct(_dev(xq, torch.int8).data_ptr(), _dev(xd, torch.float32).data_ptr(), 0)
+    code = lib().qmv_matvec_q4k_fx(y.data_ptr(), ctypes.byref(W), x.data_ptr(),
+                                   ctypes.byref(act) if act is not None else None, r0, r1, _stream())
+    _check(code, "qmv_matvec_q4k_fx")
+    return y
+
+
 class Prepared:
     """A libqmv call with its arguments marshalled once: calling it costs one
     ctypes call (on the stream current at preparation time unless another
@@ -514,3 +566,14 @@ def prepare_matvec_zp_fx(wq, wd, wzp, bits, x, y, r0=None, r1=None, stream=None)
     r1 = W.rows if r1 is None else r1
     args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), None, r0, r1]
     return Prepared("qmv_matvec_zp_fx", args, [W, wq, wd, wzp, x, y], stream)
+
+
+def prepare_matvec_q4k_fx(q, sc, mn, d, dmin, x, y, r0=None, r1=None, stream=None) -> Prepared:
+    """Prepared qmv_matvec_q4k_fx."""
+    W = q4ktensor(q, sc, mn, d, dmin)
+    _dev(x, torch.float32)
+    _dev(y, torch.float32)
+    r0 = 0 if r0 is None else r0
+    r1 = W.rows if r1 is None else r1
+    args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), None, r0, r1]
+    return Prepared("qmv_matvec_q4k_fx", args, [W, q, sc, mn, d, dmin, x, y], stream)

@@ -217,6 +217,17 @@ def raw_zp(rng: np.random.Generator, bits: int, rows: int, cols: int, with_zp: b
     return q, d, zp
 
 
+def raw_q4k(rng: np.random.Generator, rows: int, cols: int):
+    """Uniform random K-quant storage: every nibble value, scales and minima
+    over 0..63, super-block scales 2^U(-10,-4)."""
+    q = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(rows, cols // QK), dtype=np.uint8)
+    mn = rng.integers(0, 64, size=(rows, cols // QK), dtype=np.uint8)
+    d = np.exp2(rng.uniform(-10, -4, size=(rows, cols // 256))).astype(np.float32)
+    dmin = np.exp2(rng.uniform(-10, -4, size=(rows, cols // 256))).astype(np.float32)
+    return q, sc, mn, d, dmin
+
+
 def raw_scales(rng: np.random.Generator, shape):
     e = rng.uniform(-8.0, 0.0, size=shape)
     u = rng.uniform(0.5, 2.0, size=shape)

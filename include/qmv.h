@@ -277,6 +277,52 @@ qmv_status qmv_matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv
                             int32_t r0, int32_t r1, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * K-quant super-blocks with the sub-block scales folded in the integer
+ * domain ("SKaiNET-native-kernels" page, section "Proving an optimization
+ * is safe before writing it": 4-bit weights, a 6-bit scale per 32 elements,
+ * 8 sub-blocks per block, int8 activations; section "Accomplishments":
+ * per-32 asymmetric minima).  The page gives neither the storage nor the
+ * scale types; this library's reading: element i of sub-block b of
+ * super-block k of a row has the value d[k] * sc[b] * w_i - dmin[k] * mn[b]:
+ *   q    : rows x cols/2 bytes, 16 per 32-element sub-block in the Q4_0
+ *          order (element j in the low nibble of byte j, element j + 16 in
+ *          the high nibble), w_i the nibble as stored; 16-byte aligned;
+ *   sc,mn: rows x cols/32 bytes, the sub-block scale and minimum (0..63);
+ *   d,dmin: rows x cols/256 float32 (4-byte aligned).
+ * All row-major.  Matrices with rows = 0 may have null pointers.
+ * ------------------------------------------------------------------------- */
+#define QMV_Q4K_BLOCK 256
+#define QMV_Q4K_MAX_COLS 65536
+
+typedef struct {
+    uint8_t *q;
+    uint8_t *sc;
+    uint8_t *mn;
+    float *d;
+    float *dmin;
+    int32_t rows;
+    int32_t cols;
+} qmv_q4ktensor;
+
+/* The Q8_0 rule of qmv_quantize_q8 applied to 256-element blocks (the
+ * activation format of the K-quant product): out->q = k bytes, out->d =
+ * k/256 floats.  k % 256 == 0; otherwise as qmv_quantize_q8. */
+qmv_status qmv_quantize_q8_b256(qmv_qact *out, const float *x, int64_t k, void *stream);
+
+/* y[r] for r in [r0, r1): per super-block, S1 = sum_b sc_b * (sum_i w_i q_i)
+ * and S2 = sum_b mn_b * (sum_i q_i), exact in int32 (|S1| <= 8*63*32*127*15,
+ * the page's bound), and y[r] = sum over super-blocks of (S1 * d - S2 * dmin)
+ * * dx in float32, with (q, dx) the 256-block Q8_0 quantization of the
+ * float32 activation x (W->cols floats, 16-byte aligned) done inside the
+ * kernel.  If xq is not NULL it receives that quantized activation
+ * (q: cols bytes, 16-byte aligned; d: cols/256 floats) and xq->n = cols.
+ * Other entries of y are not written.  Limits: cols % 256 == 0,
+ * cols <= QMV_Q4K_MAX_COLS, rows * cols / 2 <= INT32_MAX.  Errors:
+ * QMV_E_ARG (null or misaligned pointers), QMV_E_SHAPE (sizes, row range). */
+qmv_status qmv_matvec_q4k_fx(float *y, const qmv_q4ktensor *W, const float *x, qmv_qact *xq,
+                             int32_t r0, int32_t r1, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Pack-once weight layout for the matrix-core product.  The spec stores
  * weights row-major (section 4 table); its companion write-ups on
  * block-quantized products re-lay the weights once, ahead of time, into the

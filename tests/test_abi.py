@@ -50,7 +50,7 @@ def test_header_declares_the_product_calls():
               "qmv_matvec_q8_fx_rmsnorm", "qmv_matvec_q4_fx_rmsnorm",
               "qmv_matvec_q8_fx_silu_mul", "qmv_matvec_q4_fx_silu_mul",
               "qmv_pack_bytes", "qmv_pack_weights", "qmv_gemm_q8_packed", "qmv_gemm_q4_packed",
-              "qmv_quantize_q8_b128", "qmv_matvec_zp_fx",
+              "qmv_quantize_q8_b128", "qmv_matvec_zp_fx", "qmv_quantize_q8_b256", "qmv_matvec_q4k_fx",
               "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
         assert n in names
 
@@ -242,6 +242,40 @@ def test_matvec_zp_validation(lib, bits):
     assert g(ctypes.byref(empty), None, 0, None) == OK and empty.n == 0
 
 
+class KT(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("sc", ctypes.c_void_p), ("mn", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("dmin", ctypes.c_void_p), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+def _kt(rows=8, cols=512, q=A, sc=A + 0x4000, mn=A + 0x5000, d=B, dmin=B + 0x100):
+    return KT(q, sc, mn, d, dmin, rows, cols)
+
+
+def test_matvec_q4k_validation(lib):
+    f = lib.qmv_matvec_q4k_fx
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    X = A + 0x1000
+    assert f(None, ctypes.byref(_kt()), X, None, 0, 8, None) == E_ARG
+    assert f(Y, None, X, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(_kt()), None, None, 0, 8, None) == E_ARG
+    for field in ("q", "sc", "mn", "d", "dmin"):
+        assert f(Y, ctypes.byref(_kt(**{field: 0})), X, None, 0, 8, None) == E_ARG, field
+    for cols in (0, 128, 300, 65536 + 256):
+        assert f(Y, ctypes.byref(_kt(cols=cols)), X, None, 0, 8, None) == E_SHAPE, cols
+    assert f(Y, ctypes.byref(_kt()), X, None, 0, 9, None) == E_SHAPE
+    assert f(Y, ctypes.byref(_kt()), X, None, 3, 2, None) == E_SHAPE
+    assert f(Y, ctypes.byref(_kt(q=A + 8)), X, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(_kt()), X + 4, None, 0, 8, None) == E_ARG
+    assert f(Y, ctypes.byref(_kt(d=B + 2)), X, None, 0, 8, None) == E_ARG
+    g = lib.qmv_quantize_q8_b256
+    g.argtypes = [P, P, ctypes.c_int64, P]
+    assert g(ctypes.byref(QA(A, B, 0)), Y, 128, None) == E_SHAPE
+    assert g(None, Y, 256, None) == E_ARG
+    empty = QA(0, 0, 7)
+    assert g(ctypes.byref(empty), None, 0, None) == OK and empty.n == 0
+
+
 def test_zero_rows_accept_null_pointers(lib):
     """A matrix without rows may have null data pointers (and a null output):
     the calls get past argument checking, to the device check (QMV_E_DEVICE
@@ -258,6 +292,9 @@ def test_zero_rows_accept_null_pointers(lib):
     f = lib.qmv_matvec_zp_fx
     f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
     assert f(None, ctypes.byref(ZT(0, 0, 0, 0, 256, 8)), A + 0x1000, None, 0, 0, None) in fine
+    f = lib.qmv_matvec_q4k_fx
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(None, ctypes.byref(KT(0, 0, 0, 0, 0, 0, 512)), A + 0x1000, None, 0, 0, None) in fine
     # with rows, null pointers are still refused
     assert lib.qmv_matvec_q8(Y, ctypes.byref(QT(0, 0, 8, 64, Q8)), ctypes.byref(_x()), 0, 0, None) == E_ARG
     assert lib.qmv_matvec_q8(None, ctypes.byref(_w()), ctypes.byref(_x()), 0, 0, None) == E_ARG
@@ -311,4 +348,7 @@ def test_no_device_is_an_error_not_a_crash(lib):
     g = lib.qmv_quantize_q8_b128
     g.argtypes = [P, P, ctypes.c_int64, P]
     assert g(ctypes.byref(QA(A, B, 0)), Y, 128, None) == st
+    f = lib.qmv_matvec_q4k_fx
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(Y, ctypes.byref(_kt()), A + 0x1000, None, 0, 8, None) == st
     assert lib.qmv_last_kernel().decode() == ""
