@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-batched", action="store_true", help="skip the M >= 16 matrix-core measurement")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the per-call timings of the other configurations (keeps kernel traces to the step)")
+    ap.add_argument("--q4k-only", action="store_true",
+                    help="only the K-quant super-block measurement (for profiling)")
     ap.add_argument("--zp-only", action="store_true",
                     help="only the 128-block zero-point format measurement (for profiling)")
     ap.add_argument("--batched-only", action="store_true",
@@ -115,12 +117,13 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.zp_only:
+    if args.zp_only or args.q4k_only:
         import torch
         from block_quantized_decode_amd import qmv
         torch.cuda.set_device(0)
         qmv.qmv_device_check()
-        print(json.dumps(zp_bench(torch.cuda.Stream())), flush=True)
+        fn = zp_bench if args.zp_only else q4k_bench
+        print(json.dumps(fn(torch.cuda.Stream())), flush=True)
         return
     if args.batched_only:
         import torch
@@ -242,10 +245,12 @@ def main():
     others = None
     fusion = None
     zp = None
+    q4k = None
     if not args.no_others:
         others = other_workloads_bench(stream)
         fusion = fusion_bench(stream)
         zp = zp_bench(stream)
+        q4k = q4k_bench(stream)
 
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
@@ -301,6 +306,7 @@ def main():
         "other_workloads": others,
         "fusion": fusion,
         "zp_b128": zp,
+        "q4k_superblock": q4k,
         "batched": batched,
     }
     print(json.dumps(line), flush=True)
@@ -529,6 +535,54 @@ def zp_bench(stream):
                 del calls
                 torch.cuda.empty_cache()
             out[f"{wname}_int{bits}_b128"] = per
+    return out
+
+
+def q4k_bench(stream):
+    """The K-quant super-block format (qmv_matvec_q4k_fx, the activation
+    quantized in the launch) on the shapes of the SKaiNET page's model
+    (TinyLlama-1.1B, every matrix of a layer) and on the Llama-7B FFN
+    matrices.  Nibbles, sub-block scales and minima (0..63) and super-block
+    scales are seeded random draws on the GPU; each matrix is rotated over
+    copies totalling more than 600 MB, so every launch streams from HBM.
+    Weight bytes = nibbles + scales + minima + d + dmin (0.59375 B per
+    element)."""
+    import torch
+
+    from block_quantized_decode_amd import qmv
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    shapes = {
+        "tinyllama_layer": [("W_q", 2048, 2048), ("W_k", 256, 2048), ("W_v", 256, 2048), ("W_o", 2048, 2048),
+                            ("W_gate", 5632, 2048), ("W_up", 5632, 2048), ("W_down", 2048, 5632)],
+        "llama7b_ffn": [("W_up", 11008, 4096), ("W_down", 4096, 11008)],
+    }
+    out = {}
+    for wname, mats in shapes.items():
+        per = {}
+        for name, rows, cols in mats:
+            wbytes = rows * (cols // 2 + 2 * (cols // 32) + 8 * (cols // 256))
+            copies = max(2, (600 << 20) // wbytes + 1)
+            x = torch.randn(cols, device=dev, generator=gen)
+            calls = []
+            for _ in range(copies):
+                q = torch.randint(0, 256, (rows, cols // 2), dtype=torch.uint8, device=dev, generator=gen)
+                sc = torch.randint(0, 64, (rows, cols // 32), dtype=torch.uint8, device=dev, generator=gen)
+                mn = torch.randint(0, 64, (rows, cols // 32), dtype=torch.uint8, device=dev, generator=gen)
+                d = torch.rand(rows, cols // 256, device=dev, generator=gen) * 1e-3
+                dmin = torch.rand(rows, cols // 256, device=dev, generator=gen) * 1e-3
+                y = torch.zeros(rows, device=dev)
+                calls.append(qmv.prepare_matvec_q4k_fx(q, sc, mn, d, dmin, x, y, stream=stream.cuda_stream))
+            us = _graph_us(calls, stream) / len(calls)
+            gbs = wbytes / (us * 1e-6) / 1e9
+            per[name] = {"shape": f"{rows}x{cols}", "us": round(us, 3), "weight_gb_s": round(gbs, 1),
+                         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "kernel": qmv.last_kernel(),
+                         "copies": copies}
+            del calls
+            torch.cuda.empty_cache()
+        out[wname] = per
     return out
 
 
