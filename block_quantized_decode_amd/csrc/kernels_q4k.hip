@@ -38,7 +38,6 @@
 namespace qmv {
 namespace {
 
-using rs::kWpb;
 using rs::kOOB;
 using rs::v4i;
 
@@ -68,14 +67,14 @@ __device__ __forceinline__ void quant_block256(float4 v, int (&q)[4], float &d, 
     sub = s + rs::dppi<rs::kM8>(s);
 }
 
-template <int L, int J, int D, int P>
-__global__ void __launch_bounds__(64 * kWpb)
+template <int L, int J, int D, int P, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wsc,
       const uint8_t *__restrict__ wmn, const float *__restrict__ wd, const float *__restrict__ wdm, int32_t rows,
       int32_t K, const float *__restrict__ x, int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0,
       int32_t r1, int32_t rows_wg) {
     static_assert(L >= LB && (L & (L - 1)) == 0 && L <= 64, "group size");
-    static_assert(P == 1 || (L == 64 && kWpb % P == 0), "teams of P wavefronts share rows of 64-lane groups");
+    static_assert(P == 1 || (L == 64 && WPB % P == 0), "teams of P wavefronts share rows of 64-lane groups");
     extern __shared__ __align__(16) unsigned char smem[];
     const int nk = K / SB, nsub = K / SUB;
     int8_t *xs = reinterpret_cast<int8_t *>(smem);                   // [K]
@@ -88,7 +87,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     const int chunks = nsub;  // 16 bytes of nibbles per sub-block
     const int row_bytes = K / 2;
     const int gl = lane & (L - 1);
-    const rs::RowMap<L, P> map(chunks, J, r0, r1, rows_wg);
+    const rs::RowMap<L, P, WPB> map(chunks, J, r0, r1, rows_wg);
 
     const __amdgpu_buffer_rsrc_t rq = rs::rsrc(wq, (int64_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t rsc = rs::rsrc(wsc, (int64_t)rows * nsub);
@@ -182,17 +181,17 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     // ---- phase A: the activation, quantized into LDS, one wavefront per
     // 256-element block; a wavefront first issues the loads of up to
     // kQBatch blocks, then quantizes them
-    for (int base = wid; base < nk; base += kWpb * kQBatch) {
+    for (int base = wid; base < nk; base += WPB * kQBatch) {
         float4 v[kQBatch];
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
-            const int b = base + kWpb * u;
+            const int b = base + WPB * u;
             v[u] = b < nk ? *reinterpret_cast<const float4 *>(x + (int64_t)b * SB + 4 * lane)
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
-            const int b = base + kWpb * u;
+            const int b = base + WPB * u;
             if (b >= nk) break;  // wave-uniform
             int q[4], subsum;
             float d;
@@ -223,7 +222,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     }
     if constexpr (P > 1) {
         __syncthreads();
-        for (int li = threadIdx.x; li < map.rows_here; li += 64 * kWpb) {
+        for (int li = threadIdx.x; li < map.rows_here; li += 64 * WPB) {
             float s = part[li * P];
 #pragma unroll
             for (int q = 1; q < P; ++q) s += part[li * P + q];
@@ -232,34 +231,34 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     }
 }
 
-template <int L, int J, int P>
+template <int L, int J, int P, int WPB>
 hipError_t launch_cfg(const Q4kArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
     constexpr int D = J <= 2 ? 4 : J <= 4 ? 3 : 2;
-    auto kern = k_q4k<L, J, D, P>;
+    auto kern = k_q4k<L, J, D, P, WPB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWpb), lds, s, a.y, a.wq, a.sc, a.mn, a.d, a.dmin, a.rows, a.K,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.sc, a.mn, a.d, a.dmin, a.rows, a.K,
                        a.x, a.xq_out, a.xd_out, a.r0, a.r1, rows_wg);
     static char kname[48];
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "q4k_l%d_j%d_d%d_p%d", L, J, D, P);
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "q4k_l%d_j%d_d%d_p%d_w%d", L, J, D, P, WPB);
     *name = kname;
     return hipGetLastError();
 }
 
+// 64-lane groups in workgroups of 16 wavefronts (rows of two or more chunks
+// per lane, or shared by teams)
 template <int P>
 hipError_t launch_j(const Q4kArgs &a, int J, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
     switch (J) {
-        case 1: return launch_cfg<64, 1, P>(a, grid, rows_wg, lds, s, name);
-        case 2: return launch_cfg<64, 2, P>(a, grid, rows_wg, lds, s, name);
-        case 3: return launch_cfg<64, 3, P>(a, grid, rows_wg, lds, s, name);
-        case 4: return launch_cfg<64, 4, P>(a, grid, rows_wg, lds, s, name);
-        case 5: return launch_cfg<64, 5, P>(a, grid, rows_wg, lds, s, name);
-        case 6: return launch_cfg<64, 6, P>(a, grid, rows_wg, lds, s, name);
-        case 7: return launch_cfg<64, 7, P>(a, grid, rows_wg, lds, s, name);
-        default: return launch_cfg<64, 8, P>(a, grid, rows_wg, lds, s, name);
+        case 1: return launch_cfg<64, 1, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 2: return launch_cfg<64, 2, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 3: return launch_cfg<64, 3, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 4: return launch_cfg<64, 4, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 5: return launch_cfg<64, 5, P, 16>(a, grid, rows_wg, lds, s, name);
+        default: return launch_cfg<64, 6, P, 16>(a, grid, rows_wg, lds, s, name);
     }
 }
 
@@ -291,18 +290,19 @@ hipError_t launch_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **
     const int chunks = a.K / SUB;
     const int nrow = a.r1 - a.r0;
     const size_t lds_x = lds_x_bytes(a.K);
-    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, LB);
-    const int waves = sh.wgpc * num_cu * kWpb;
+    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, LB, 6);  // 7 or 8 chunks per lane spill
+    const int waves = sh.wgpc * num_cu * sh.wpb;
     if (sh.P == 1) {
-        const int groups_per_wg = kWpb * (64 / sh.L);
+        const int groups_per_wg = sh.wpb * (64 / sh.L);
         int grid = (nrow + groups_per_wg - 1) / groups_per_wg;
-        if (grid > waves / kWpb) grid = waves / kWpb;
+        if (grid > waves / sh.wpb) grid = waves / sh.wpb;
         if (grid < 1) grid = 1;
-        if (sh.L == 16) return launch_cfg<16, 1, 1>(a, grid, 0, lds_x, s, name);
-        if (sh.L == 32) return launch_cfg<32, 1, 1>(a, grid, 0, lds_x, s, name);
+        if (sh.L == 16) return launch_cfg<16, 1, 1, 8>(a, grid, 0, lds_x, s, name);
+        if (sh.L == 32) return launch_cfg<32, 1, 1, 8>(a, grid, 0, lds_x, s, name);
+        if (sh.wpb == 8) return launch_cfg<64, 1, 1, 8>(a, grid, 0, lds_x, s, name);
         return launch_j<1>(a, sh.J, grid, 0, lds_x, s, name);
     }
-    int grid = waves / kWpb;
+    int grid = waves / sh.wpb;
     int rows_wg = (nrow + grid - 1) / grid;
     if (rows_wg < 1) rows_wg = 1;
     if (rows_wg * sh.P > 2048) rows_wg = 2048 / sh.P;

@@ -50,7 +50,6 @@
 namespace qmv {
 namespace {
 
-using rs::kWpb;
 using rs::kOOB;
 using rs::v4i;
 
@@ -90,14 +89,14 @@ __device__ __forceinline__ void quant_half(float4 v, int (&q)[4], float &d, int 
 // position of element e of a block in the 4-bit activation order
 __device__ __forceinline__ int perm4(int e) { return (e & ~7) + ((e & 1) << 2) + ((e & 7) >> 1); }
 
-template <int BITS, int L, int J, int D, int P>
-__global__ void __launch_bounds__(64 * kWpb)
+template <int BITS, int L, int J, int D, int P, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restrict__ wd,
      const uint8_t *__restrict__ wzp, int32_t rows, int32_t K, const float *__restrict__ x,
      int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0, int32_t r1, int32_t rows_wg) {
     constexpr int LB = BITS == 8 ? 8 : 4;  // lanes (16-byte chunks) per block
     static_assert(L >= LB && (L & (L - 1)) == 0 && L <= 64, "group size");
-    static_assert(P == 1 || (L == 64 && kWpb % P == 0), "teams of P wavefronts share rows of 64-lane groups");
+    static_assert(P == 1 || (L == 64 && WPB % P == 0), "teams of P wavefronts share rows of 64-lane groups");
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = K / BLK;
     int8_t *xs = reinterpret_cast<int8_t *>(smem);                          // [K]
@@ -110,7 +109,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     const int row_bytes = BITS == 8 ? K : K / 2;
     const int chunks = row_bytes >> 4;
     const int gl = lane & (L - 1);
-    const rs::RowMap<L, P> map(chunks, J, r0, r1, rows_wg);
+    const rs::RowMap<L, P, WPB> map(chunks, J, r0, r1, rows_wg);
 
     const __amdgpu_buffer_rsrc_t rq = rs::rsrc(wq, (int64_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t rd = rs::rsrc(wd, (int64_t)rows * nb * 4);
@@ -215,17 +214,17 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     // ---- phase A: the activation, quantized into LDS.  Each half-wavefront
     // takes one block (4 elements per lane); a wavefront first issues the
     // loads of up to kQBatch block pairs, then quantizes them.
-    for (int base = 2 * wid; base < nb; base += 2 * kWpb * kQBatch) {
+    for (int base = 2 * wid; base < nb; base += 2 * WPB * kQBatch) {
         float4 v[kQBatch];
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
-            const int b = base + 2 * kWpb * u + (lane >> 5);
+            const int b = base + 2 * WPB * u + (lane >> 5);
             v[u] = b < nb ? *reinterpret_cast<const float4 *>(x + (int64_t)b * BLK + 4 * (lane & 31))
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
-            const int b0 = base + 2 * kWpb * u;
+            const int b0 = base + 2 * WPB * u;
             if (b0 >= nb) break;  // wave-uniform
             const int b = b0 + (lane >> 5);
             int q[4], qs;
@@ -267,7 +266,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     }
     if constexpr (P > 1) {
         __syncthreads();
-        for (int li = threadIdx.x; li < map.rows_here; li += 64 * kWpb) {
+        for (int li = threadIdx.x; li < map.rows_here; li += 64 * WPB) {
             float s = part[li * P];
 #pragma unroll
             for (int q = 1; q < P; ++q) s += part[li * P + q];
@@ -276,34 +275,36 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     }
 }
 
-template <int BITS, int L, int J, int P>
+template <int BITS, int L, int J, int P, int WPB>
 hipError_t launch_cfg(const ZpArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
     constexpr int D = J <= 2 ? QMV_ZP_D12 : J <= 4 ? QMV_ZP_D34 : 2;
-    auto kern = k_zp<BITS, L, J, D, P>;
+    auto kern = k_zp<BITS, L, J, D, P, WPB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWpb), lds, s, a.y, a.wq, a.wd, a.wzp, a.rows, a.K, a.x,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.wzp, a.rows, a.K, a.x,
                        a.xq_out, a.xd_out, a.r0, a.r1, rows_wg);
     static char kname[48];
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "zp%d_l%d_j%d_d%d_p%d", BITS, L, J, D, P);
+    if (kname[0] == 0) snprintf(kname, sizeof kname, "zp%d_l%d_j%d_d%d_p%d_w%d", BITS, L, J, D, P, WPB);
     *name = kname;
     return hipGetLastError();
 }
 
+// 64-lane groups in workgroups of 16 wavefronts (rows of two or more chunks
+// per lane, or shared by teams)
 template <int BITS, int P>
 hipError_t launch_j(const ZpArgs &a, int J, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
     switch (J) {
-        case 1: return launch_cfg<BITS, 64, 1, P>(a, grid, rows_wg, lds, s, name);
-        case 2: return launch_cfg<BITS, 64, 2, P>(a, grid, rows_wg, lds, s, name);
-        case 3: return launch_cfg<BITS, 64, 3, P>(a, grid, rows_wg, lds, s, name);
-        case 4: return launch_cfg<BITS, 64, 4, P>(a, grid, rows_wg, lds, s, name);
-        case 5: return launch_cfg<BITS, 64, 5, P>(a, grid, rows_wg, lds, s, name);
-        case 6: return launch_cfg<BITS, 64, 6, P>(a, grid, rows_wg, lds, s, name);
-        case 7: return launch_cfg<BITS, 64, 7, P>(a, grid, rows_wg, lds, s, name);
-        default: return launch_cfg<BITS, 64, 8, P>(a, grid, rows_wg, lds, s, name);
+        case 1: return launch_cfg<BITS, 64, 1, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 2: return launch_cfg<BITS, 64, 2, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 3: return launch_cfg<BITS, 64, 3, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 4: return launch_cfg<BITS, 64, 4, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 5: return launch_cfg<BITS, 64, 5, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 6: return launch_cfg<BITS, 64, 6, P, 16>(a, grid, rows_wg, lds, s, name);
+        case 7: return launch_cfg<BITS, 64, 7, P, 16>(a, grid, rows_wg, lds, s, name);
+        default: return launch_cfg<BITS, 64, 8, P, 16>(a, grid, rows_wg, lds, s, name);
     }
 }
 
@@ -313,19 +314,20 @@ hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **
     const size_t lds_x = ((size_t)a.K + 8 * (size_t)(a.K / BLK) + 15) & ~(size_t)15;
     const int nrow = a.r1 - a.r0;
     const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, BITS == 8 ? 8 : 4);
-    const int waves = sh.wgpc * num_cu * kWpb;
+    const int waves = sh.wgpc * num_cu * sh.wpb;
     if (sh.P == 1) {
-        const int groups_per_wg = kWpb * (64 / sh.L);
+        const int groups_per_wg = sh.wpb * (64 / sh.L);
         int grid = (nrow + groups_per_wg - 1) / groups_per_wg;
-        if (grid > waves / kWpb) grid = waves / kWpb;
+        if (grid > waves / sh.wpb) grid = waves / sh.wpb;
         if (grid < 1) grid = 1;
-        if (sh.L == 16) return launch_cfg<BITS, 16, 1, 1>(a, grid, 0, lds_x, s, name);
-        if (sh.L == 32) return launch_cfg<BITS, 32, 1, 1>(a, grid, 0, lds_x, s, name);
+        if (sh.L == 16) return launch_cfg<BITS, 16, 1, 1, 8>(a, grid, 0, lds_x, s, name);
+        if (sh.L == 32) return launch_cfg<BITS, 32, 1, 1, 8>(a, grid, 0, lds_x, s, name);
+        if (sh.wpb == 8) return launch_cfg<BITS, 64, 1, 1, 8>(a, grid, 0, lds_x, s, name);
         return launch_j<BITS, 1>(a, sh.J, grid, 0, lds_x, s, name);
     }
     // P > 1: consecutive rows per workgroup, enough workgroups to give each
     // wavefront work, partial sums in LDS (at most 8 KiB of them)
-    int grid = waves / kWpb;
+    int grid = waves / sh.wpb;
     int rows_wg = (nrow + grid - 1) / grid;
     if (rows_wg < 1) rows_wg = 1;
     if (rows_wg * sh.P > 2048) rows_wg = 2048 / sh.P;

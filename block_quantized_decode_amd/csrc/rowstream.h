@@ -9,8 +9,8 @@
 // c, c + L, ... in windows of L * J chunks.
 //   P = 1: group g of the grid takes rows r0 + g, r0 + g + G, ... (G groups
 //   in the grid), each row in W windows, in order.
-//   P > 1: workgroup b takes rows_wg consecutive rows; its kWpb / P teams of
-//   P wavefronts take every (kWpb / P)-th of them, and wavefront q of a team
+//   P > 1: workgroup b takes rows_wg consecutive rows; its WPB / P teams of
+//   P wavefronts take every (WPB / P)-th of them, and wavefront q of a team
 //   takes windows q, q + P, ... of the team's rows.  The P partial sums of a
 //   row meet in LDS and are added in wavefront order at the end.
 // Every wavefront runs the same number of items; items past a group's rows
@@ -25,7 +25,6 @@ namespace rs {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kWpb = 8;                 // wavefronts per workgroup
 constexpr int kOOB = 0x7FFFFFF0;        // an offset beyond every descriptor range used here
 constexpr int kBufFlags = 0x00020000;   // buffer descriptor word 3: raw 32-bit data
 
@@ -99,10 +98,10 @@ struct Item {
     bool live, first, last;
 };
 
-template <int L, int P>
+template <int L, int P, int WPB>
 struct RowMap {
     static constexpr int GPW = 64 / L;         // row groups per wavefront
-    static constexpr int TPW = kWpb / P;       // teams per workgroup (P > 1)
+    static constexpr int TPW = WPB / P;        // teams per workgroup (P > 1)
     int W, r0, g, G, rows_g, rb0, rows_here, rows_team, wpw, tm, pw, items;
 
     __device__ __forceinline__ RowMap(int chunks, int J, int r0_, int r1, int rows_wg) {
@@ -117,8 +116,8 @@ struct RowMap {
         rows_team = P > 1 ? (rows_here - tm + TPW - 1) / TPW : 0;
         const int rows_team_max = P > 1 ? (rows_wg + TPW - 1) / TPW : 0;  // workgroup-uniform
         wpw = (W + P - 1) / P;
-        G = gridDim.x * kWpb * GPW;
-        const int g0 = (blockIdx.x * kWpb + wid) * GPW;
+        G = gridDim.x * WPB * GPW;
+        const int g0 = (blockIdx.x * WPB + wid) * GPW;
         g = g0 + lane / L;
         rows_g = g < nrow ? (nrow - g + G - 1) / G : 0;
         const int rows_w = g0 < nrow ? (nrow - g0 + G - 1) / G : 0;  // the wavefront's first group has the most
@@ -149,34 +148,43 @@ struct RowMap {
 };
 
 // Launch shape for rows of `chunks` chunks: lanes per row L, windows of J
-// chunks per lane, teams of P wavefronts, workgroups per compute unit.
+// chunks per lane, teams of P wavefronts, wavefronts per workgroup WPB and
+// workgroups per compute unit.
 struct Shape {
-    int L, J, P, wgpc;
+    int L, J, P, wpb, wgpc;
 };
 
-// J chunks per lane per window (at most 8) for rows split over P
+// J chunks per lane per window (at most jmax) for rows split over P
 // wavefronts: the windows of a row as even as possible.
-inline int pick_j(int chunks, int P) {
+inline int pick_j(int chunks, int P, int jmax = 8) {
     const int per = (chunks + P - 1) / P;
-    const int win = (per + 64 * 8 - 1) / (64 * 8);
+    const int win = (per + 64 * jmax - 1) / (64 * jmax);
     return (per + 64 * win - 1) / (64 * win);
 }
 
-// min_l: the smallest group allowed (the lanes of one block must fit).
-inline Shape pick_shape(int chunks, int nrow, int num_cu, int min_l) {
+// min_l: the smallest group allowed (the lanes of one block must fit);
+// jmax: the most chunks per lane the kernel holds without spilling.
+inline Shape pick_shape(int chunks, int nrow, int num_cu, int min_l, int jmax = 8) {
     Shape s;
     s.L = 64;
     if (chunks <= 16 && min_l <= 16) s.L = 16;
     else if (chunks <= 32 && min_l <= 32) s.L = 32;
-    s.wgpc = s.L < 64 || pick_j(chunks, 1) == 1 ? 4 : 2;
-    const int waves = s.wgpc * num_cu * kWpb;
-    // rows shared by a team of P wavefronts when there are fewer than two
-    // rows per wavefront and each row has at least two windows' worth
+    // Rows of one chunk per lane: 4 workgroups of 8 wavefronts per compute
+    // unit (32 wavefronts, few registers each).  Longer rows: one workgroup
+    // of 16 wavefronts per compute unit (more registers per wavefront; the
+    // activation is quantized once per compute unit instead of twice).
+    const bool short_rows = s.L < 64 || pick_j(chunks, 1) == 1;
+    s.wpb = short_rows ? 8 : 16;
+    s.wgpc = short_rows ? 4 : 1;
+    const int waves = s.wgpc * num_cu * s.wpb;
+    // rows shared by a team of P wavefronts (at most 8) when there are fewer
+    // than two rows per wavefront and each row has at least two windows' worth
+    // (which also means long rows)
     s.P = 1;
     if (s.L == 64 && chunks >= 128) {
-        while (s.P < kWpb && (int64_t)nrow * s.P < 2 * (int64_t)waves && chunks / (2 * s.P) >= 64) s.P *= 2;
+        while (s.P < 8 && (int64_t)nrow * s.P < 2 * (int64_t)waves && chunks / (2 * s.P) >= 64) s.P *= 2;
     }
-    s.J = s.L == 64 ? pick_j(chunks, s.P) : 1;
+    s.J = s.L == 64 ? pick_j(chunks, s.P, jmax) : 1;
     return s;
 }
 
