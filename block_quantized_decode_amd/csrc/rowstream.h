@@ -25,6 +25,7 @@ namespace rs {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+
 constexpr int kOOB = 0x7FFFFFF0;        // an offset beyond every descriptor range used here
 constexpr int kBufFlags = 0x00020000;   // buffer descriptor word 3: raw 32-bit data
 
@@ -126,8 +127,10 @@ struct RowMap {
 
     __device__ __forceinline__ Item item(int t) const {
         Item it;
+        // (W and wpw are wave-uniform; one window per row is the common case
+        // of short rows, and skips an integer division per item)
         if constexpr (P == 1) {
-            const int rl = t / W;
+            const int rl = W == 1 ? t : t / W;
             it.win = t - rl * W;
             it.live = rl < rows_g;
             it.r = r0 + g + rl * G;
@@ -135,7 +138,7 @@ struct RowMap {
             it.first = it.win == 0;
             it.last = it.win == W - 1;
         } else {
-            const int i = t / wpw, k = t - i * wpw;
+            const int i = wpw == 1 ? t : t / wpw, k = t - i * wpw;
             it.win = pw + P * k;
             it.li = tm + TPW * i;
             it.live = i < rows_team && it.win < W;
