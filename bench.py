@@ -60,6 +60,8 @@ def parse():
                     help="skip the per-call timings of the other configurations (keeps kernel traces to the step)")
     ap.add_argument("--q4k-only", action="store_true",
                     help="only the K-quant super-block measurement (for profiling)")
+    ap.add_argument("--q4k-shapes", default="",
+                    help="with --q4k-only: comma-separated shape groups (tinyllama_layer, llama7b_ffn); default all")
     ap.add_argument("--zp-only", action="store_true",
                     help="only the 128-block zero-point format measurement (for profiling)")
     ap.add_argument("--batched-only", action="store_true",
@@ -122,8 +124,9 @@ def main():
         from block_quantized_decode_amd import qmv
         torch.cuda.set_device(0)
         qmv.qmv_device_check()
-        fn = zp_bench if args.zp_only else q4k_bench
-        print(json.dumps(fn(torch.cuda.Stream())), flush=True)
+        stream = torch.cuda.Stream()
+        res = zp_bench(stream) if args.zp_only else q4k_bench(stream, args.q4k_shapes.split(",") if args.q4k_shapes else None)
+        print(json.dumps(res), flush=True)
         return
     if args.batched_only:
         import torch
@@ -538,7 +541,7 @@ def zp_bench(stream):
     return out
 
 
-def q4k_bench(stream):
+def q4k_bench(stream, groups=None):
     """The K-quant super-block format (qmv_matvec_q4k_fx, the activation
     quantized in the launch) on the shapes of the SKaiNET page's model
     (TinyLlama-1.1B, every matrix of a layer) and on the Llama-7B FFN
@@ -559,6 +562,8 @@ def q4k_bench(stream):
                             ("W_gate", 5632, 2048), ("W_up", 5632, 2048), ("W_down", 2048, 5632)],
         "llama7b_ffn": [("W_up", 11008, 4096), ("W_down", 4096, 11008)],
     }
+    if groups:
+        shapes = {k: v for k, v in shapes.items() if k in groups}
     out = {}
     for wname, mats in shapes.items():
         per = {}
