@@ -174,21 +174,27 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
         }
     };
 
-    Buf ring[D];
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
-
     // ---- phase A: the activation, quantized into LDS, one wavefront per
-    // 256-element block; a wavefront first issues the loads of up to
-    // kQBatch blocks, then quantizes them
-    for (int base = wid; base < nk; base += WPB * kQBatch) {
-        float4 v[kQBatch];
+    // 256-element block; a wavefront issues the loads of up to kQBatch
+    // blocks, then quantizes them.  The first batch is requested before the
+    // first weights: loads return in order, so the activation does not wait
+    // behind the weight stream.
+    float4 v[kQBatch];
+    auto load_x = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
             const int b = base + WPB * u;
             v[u] = b < nk ? *reinterpret_cast<const float4 *>(x + (int64_t)b * SB + 4 * lane)
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
+    };
+    load_x(wid);
+    Buf ring[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
+
+    for (int base = wid; base < nk; base += WPB * kQBatch) {
+        if (base != wid) load_x(base);  // later batches (wave-uniform)
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
             const int b = base + WPB * u;

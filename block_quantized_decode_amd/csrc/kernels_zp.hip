@@ -205,23 +205,29 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
         }
     };
 
-    // ring of D register buffers, D - 1 items in flight ahead of the one
-    // being computed (unrolled by D so that each buffer has fixed registers)
-    Buf ring[D];
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
-
     // ---- phase A: the activation, quantized into LDS.  Each half-wavefront
-    // takes one block (4 elements per lane); a wavefront first issues the
-    // loads of up to kQBatch block pairs, then quantizes them.
-    for (int base = 2 * wid; base < nb; base += 2 * WPB * kQBatch) {
-        float4 v[kQBatch];
+    // takes one block (4 elements per lane); a wavefront issues the loads of
+    // up to kQBatch block pairs, then quantizes them.  The first batch is
+    // requested before the first weights: loads return in order, so the
+    // activation does not wait behind the weight stream.
+    float4 v[kQBatch];
+    auto load_x = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
             const int b = base + 2 * WPB * u + (lane >> 5);
             v[u] = b < nb ? *reinterpret_cast<const float4 *>(x + (int64_t)b * BLK + 4 * (lane & 31))
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
+    };
+    load_x(2 * wid);
+    // ring of D register buffers, D - 1 items in flight ahead of the one
+    // being computed (unrolled by D so that each buffer has fixed registers)
+    Buf ring[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
+
+    for (int base = 2 * wid; base < nb; base += 2 * WPB * kQBatch) {
+        if (base != 2 * wid) load_x(base);  // later batches (wave-uniform)
 #pragma unroll
         for (int u = 0; u < kQBatch; ++u) {
             const int b0 = base + 2 * WPB * u;
