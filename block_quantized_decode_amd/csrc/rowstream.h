@@ -172,13 +172,16 @@ inline Shape pick_shape(int chunks, int nrow, int num_cu, int min_l, int jmax = 
     s.L = 64;
     if (chunks <= 16 && min_l <= 16) s.L = 16;
     else if (chunks <= 32 && min_l <= 32) s.L = 32;
-    // Rows of one chunk per lane: 4 workgroups of 8 wavefronts per compute
-    // unit (32 wavefronts, few registers each).  Longer rows: one workgroup
-    // of 16 wavefronts per compute unit (more registers per wavefront; the
-    // activation is quantized once per compute unit instead of twice).
+    // Rows of one chunk per lane: workgroups of 8 wavefronts (few registers
+    // each), 2 per compute unit while that leaves at most 16 rows per
+    // wavefront, 4 beyond (more rows in flight; each workgroup quantizes the
+    // whole activation, so fewer workgroups spend less on it when the rows
+    // are few).  Longer rows: one workgroup of 16 wavefronts per compute unit
+    // (more registers per wavefront; the activation is quantized once per
+    // compute unit).
     const bool short_rows = s.L < 64 || pick_j(chunks, 1) == 1;
     s.wpb = short_rows ? 8 : 16;
-    s.wgpc = short_rows ? 4 : 1;
+    s.wgpc = short_rows ? ((int64_t)nrow <= 16 * 2 * (int64_t)num_cu * 8 ? 2 : 4) : 1;
     const int waves = s.wgpc * num_cu * s.wpb;
     // rows shared by a team of P wavefronts (at most 8) when there are fewer
     // than two rows per wavefront and each row has at least two windows' worth
