@@ -296,7 +296,7 @@ hipError_t launch_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **
     const int chunks = a.K / SUB;
     const int nrow = a.r1 - a.r0;
     const size_t lds_x = lds_x_bytes(a.K);
-    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, LB, 6);  // 7 or 8 chunks per lane spill
+    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, LB, 6, 32);  // 7 or 8 chunks per lane spill
     const int waves = sh.wgpc * num_cu * sh.wpb;
     if (sh.P == 1) {
         const int groups_per_wg = sh.wpb * (64 / sh.L);

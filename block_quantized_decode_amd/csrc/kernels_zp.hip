@@ -319,7 +319,7 @@ hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **
     const int chunks = (BITS == 8 ? a.K : a.K / 2) / 16;
     const size_t lds_x = ((size_t)a.K + 8 * (size_t)(a.K / BLK) + 15) & ~(size_t)15;
     const int nrow = a.r1 - a.r0;
-    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, BITS == 8 ? 8 : 4);
+    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, BITS == 8 ? 8 : 4, 8, BITS == 8 ? 64 : 32);
     const int waves = sh.wgpc * num_cu * sh.wpb;
     if (sh.P == 1) {
         const int groups_per_wg = sh.wpb * (64 / sh.L);

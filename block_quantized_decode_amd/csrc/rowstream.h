@@ -166,8 +166,10 @@ inline int pick_j(int chunks, int P, int jmax = 8) {
 }
 
 // min_l: the smallest group allowed (the lanes of one block must fit);
-// jmax: the most chunks per lane the kernel holds without spilling.
-inline Shape pick_shape(int chunks, int nrow, int num_cu, int min_l, int jmax = 8) {
+// jmax: the most chunks per lane the kernel holds without spilling;
+// team_min: the fewest chunks of a row a wavefront of a team may take (1024
+// elements: 64 chunks of 8-bit codes, 32 of 4-bit ones).
+inline Shape pick_shape(int chunks, int nrow, int num_cu, int min_l, int jmax, int team_min) {
     Shape s;
     s.L = 64;
     if (chunks <= 16 && min_l <= 16) s.L = 16;
@@ -184,11 +186,11 @@ inline Shape pick_shape(int chunks, int nrow, int num_cu, int min_l, int jmax = 
     s.wgpc = short_rows ? ((int64_t)nrow <= 16 * 2 * (int64_t)num_cu * 8 ? 2 : 4) : 1;
     const int waves = s.wgpc * num_cu * s.wpb;
     // rows shared by a team of P wavefronts (at most 8) when there are fewer
-    // than two rows per wavefront and each row has at least two windows' worth
-    // (which also means long rows)
+    // than two rows per wavefront and each wavefront keeps at least team_min
+    // chunks of the row (long rows only)
     s.P = 1;
     if (s.L == 64 && chunks >= 128) {
-        while (s.P < 8 && (int64_t)nrow * s.P < 2 * (int64_t)waves && chunks / (2 * s.P) >= 64) s.P *= 2;
+        while (s.P < 8 && (int64_t)nrow * s.P < 2 * (int64_t)waves && chunks / (2 * s.P) >= team_min) s.P *= 2;
     }
     s.J = s.L == 64 ? pick_j(chunks, s.P, jmax) : 1;
     return s;
