@@ -17,7 +17,9 @@
 // already non-negative bytes, so sumi = sum B q - zp * sum q.  sum q is
 // computed once per block when the activation is quantized.
 //
-// Work layout.  Workgroups of 8 wavefronts, 2 or 4 per compute unit.
+// Work layout.  Workgroups of 8 wavefronts, 2 or 4 per compute unit, for
+// rows of one chunk per lane; of 16 wavefronts, one per compute unit, for
+// longer rows (the choice is rowstream.h's).
 //   Phase A: the workgroup quantizes the whole activation into LDS: each
 //   half-wavefront one 128-element block, 4 elements per lane, maximum and
 //   sum reduced by DPP within rows of 16 lanes and lane reads across rows;
