@@ -103,6 +103,25 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
         int sc[J], mn[J];
         float d[JM], dm[JM];
     };
+    // With one chunk per lane and window (J = 1) the D items of a ring turn
+    // share one load instead: lane `sub` < D of a super-block's 8 lanes loads
+    // d and dmin of that super-block in item t0 + sub of the turn that starts
+    // at item t0, and applies them to that item's S1 and S2 itself.
+    constexpr bool IB = J == 1 && D <= LB;
+    struct Sc {
+        float d, dm;
+    };
+    auto load_sc = [&](int tb) __attribute__((always_inline)) {
+        Sc sc;
+        const int sub = gl % LB;
+        const rs::Item it = map.item(tb + (sub < D ? sub : 0));
+        const int c = it.win * L + (gl - sub);  // the first sub-block of this lane's super-block
+        const bool ok = sub < D && it.live && c < chunks;
+        const int k = c / LB;
+        sc.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (it.r * nk + k) : kOOB, 0, 0));
+        sc.dm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdm, ok ? 4 * (it.r * nk + k) : kOOB, 0, 0));
+        return sc;
+    };
     auto load = [&](Buf &bf, int t) __attribute__((always_inline)) {
         const rs::Item it = map.item(t);
         const int r = it.r;
@@ -117,7 +136,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
         }
         const int sub = gl % LB;
 #pragma unroll
-        for (int m = 0; m < JM; ++m) {
+        for (int m = 0; m < (IB ? 0 : JM); ++m) {
             const int jj = sub + LB * m;
             const int c = (it.win * J + jj) * L + (gl - sub);
             const bool ok = it.live && jj < J && c < chunks;
@@ -129,7 +148,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     };
 
     float acc = 0.0f;
-    auto compute = [&](const Buf &bf, int t) __attribute__((always_inline)) {
+    auto compute = [&](const Buf &bf, int t, const Sc &sc, int dpos) __attribute__((always_inline)) {
         const rs::Item it = map.item(t);
         if (it.first) acc = 0.0f;
 #pragma unroll
@@ -155,10 +174,10 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
             s2 += rs::dppi<rs::kX2>(s2);
             s1 += rs::dppi<rs::kM8>(s1);
             s2 += rs::dppi<rs::kM8>(s2);
-            if (ok && sub == j % LB) {
+            if (ok && sub == (IB ? dpos : j % LB)) {
 #pragma clang fp contract(off)
-                const float tt = (float)s1 * bf.d[j / LB];
-                const float uu = (float)s2 * bf.dm[j / LB];
+                const float tt = (float)s1 * (IB ? sc.d : bf.d[j / LB]);
+                const float uu = (float)s2 * (IB ? sc.dm : bf.dm[j / LB]);
                 float v = tt - uu;
                 v = v * sd[cc / LB];
                 acc = acc + v;
@@ -192,6 +211,8 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     Buf ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
+    Sc cur = {}, nxt = {};
+    if constexpr (IB) nxt = load_sc(0);  // (measured: after the first weights is faster here)
 
     for (int base = wid; base < nk; base += WPB * kQBatch) {
         if (base != wid) load_x(base);  // later batches (wave-uniform)
@@ -217,12 +238,16 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
     // ---- phase B: the rows
     const int items = map.items;
     for (int t0 = 0; t0 < items; t0 += D) {
+        if constexpr (IB) {
+            cur = nxt;
+            nxt = load_sc(t0 + D);
+        }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int t = t0 + d;
             if (t < items) {  // wave-uniform
                 load(ring[(d + D - 1) % D], t + D - 1);
-                compute(ring[d], t);
+                compute(ring[d], t, cur, d);
             }
         }
     }

@@ -129,6 +129,27 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
         float dw[JM];
         int zp[JM];
     };
+    // With one chunk per lane and window (J = 1) the D items of a ring turn
+    // share one load instead: lane `sub` < D of a block's LB lanes loads the
+    // scale and zero point of that block in item t0 + sub of the turn that
+    // starts at item t0, and scales that item's block sum itself.
+    constexpr bool IB = J == 1 && D <= LB;
+    struct Sc {
+        float dw;
+        int zp;
+    };
+    auto load_sc = [&](int tb) __attribute__((always_inline)) {
+        Sc sc;
+        const int sub = gl % LB;
+        const rs::Item it = map.item(tb + (sub < D ? sub : 0));
+        const int c = it.win * L + (gl - sub);  // the first chunk of this lane's block
+        const bool ok = sub < D && it.live && c < chunks;
+        const int b = c / LB;
+        sc.dw = __builtin_bit_cast(float,
+                                   __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (it.r * nb + b) : kOOB, 0, 0));
+        sc.zp = wzp != nullptr ? (int)__builtin_amdgcn_raw_buffer_load_b8(rz, ok ? it.r * nb + b : kOOB, 0, 0) : zdef;
+        return sc;
+    };
     auto load = [&](Buf &bf, int t) __attribute__((always_inline)) {
         const rs::Item it = map.item(t);
         const int r = it.r;
@@ -141,7 +162,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
         }
         const int sub = gl % LB;
 #pragma unroll
-        for (int m = 0; m < JM; ++m) {
+        for (int m = 0; m < (IB ? 0 : JM); ++m) {
             const int jj = sub + LB * m;  // the iteration whose block this lane scales
             const int c = (it.win * J + jj) * L + (gl - sub);
             const bool ok = it.live && jj < J && c < chunks;
@@ -156,7 +177,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     };
 
     float acc = 0.0f;
-    auto compute = [&](const Buf &bf, int t) __attribute__((always_inline)) {
+    auto compute = [&](const Buf &bf, int t, const Sc &sc, int dpos) __attribute__((always_inline)) {
         const rs::Item it = map.item(t);
         if (it.first) acc = 0.0f;
 #pragma unroll
@@ -188,10 +209,10 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             p += rs::dppi<rs::kX1>(p);
             p += rs::dppi<rs::kX2>(p);
             if constexpr (LB == 8) p += rs::dppi<rs::kM8>(p);
-            if (ok && sub == j % LB) {
+            if (ok && sub == (IB ? dpos : j % LB)) {
 #pragma clang fp contract(off)
-                const int sumi = p - (bf.zp[j / LB] - off) * sq[b];
-                float tt = (float)sumi * bf.dw[j / LB];
+                const int sumi = p - ((IB ? sc.zp : bf.zp[j / LB]) - off) * sq[b];
+                float tt = (float)sumi * (IB ? sc.dw : bf.dw[j / LB]);
                 tt = tt * sd[b];
                 acc = acc + tt;
             }
@@ -224,6 +245,8 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     load_x(2 * wid);
     // ring of D register buffers, D - 1 items in flight ahead of the one
     // being computed (unrolled by D so that each buffer has fixed registers)
+    Sc cur = {}, nxt = {};
+    if constexpr (IB) nxt = load_sc(0);  // (measured: ahead of the weights is faster here)
     Buf ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) load(ring[d], d);  // the weights do not wait for the activation
@@ -263,12 +286,16 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     // ---- phase B: the rows
     const int items = map.items;
     for (int t0 = 0; t0 < items; t0 += D) {
+        if constexpr (IB) {
+            cur = nxt;
+            nxt = load_sc(t0 + D);
+        }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int t = t0 + d;
             if (t < items) {  // wave-uniform
                 load(ring[(d + D - 1) % D], t + D - 1);
-                compute(ring[d], t);
+                compute(ring[d], t, cur, d);
             }
         }
     }
