@@ -103,20 +103,21 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
         int sc[J], mn[J];
         float d[JM], dm[JM];
     };
-    // With one chunk per lane and window (J = 1) the D items of a ring turn
-    // share one load instead: lane `sub` < D of a super-block's 8 lanes loads
-    // d and dmin of that super-block in item t0 + sub of the turn that starts
-    // at item t0, and applies them to that item's S1 and S2 itself.
-    constexpr bool IB = J == 1 && D <= LB;
+    // When a super-block's 8 lanes outnumber the J * D (item, iteration)
+    // pairs of a ring turn, the turn shares one load instead: lane `sub` <
+    // J * D of the super-block's lanes loads d and dmin of iteration sub % J
+    // of item t0 + sub / J (the turn starting at item t0), and applies them
+    // to that S1 and S2 itself.
+    constexpr bool IB = J * D <= LB;
     struct Sc {
         float d, dm;
     };
     auto load_sc = [&](int tb) __attribute__((always_inline)) {
         Sc sc;
-        const int sub = gl % LB;
-        const rs::Item it = map.item(tb + (sub < D ? sub : 0));
-        const int c = it.win * L + (gl - sub);  // the first sub-block of this lane's super-block
-        const bool ok = sub < D && it.live && c < chunks;
+        const int sub = gl % LB, di = sub / J, jj = sub % J;
+        const rs::Item it = map.item(tb + (di < D ? di : 0));
+        const int c = (it.win * J + jj) * L + (gl - sub);  // the first sub-block of that super-block
+        const bool ok = di < D && it.live && c < chunks;
         const int k = c / LB;
         sc.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (it.r * nk + k) : kOOB, 0, 0));
         sc.dm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdm, ok ? 4 * (it.r * nk + k) : kOOB, 0, 0));
@@ -174,7 +175,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
             s2 += rs::dppi<rs::kX2>(s2);
             s1 += rs::dppi<rs::kM8>(s1);
             s2 += rs::dppi<rs::kM8>(s2);
-            if (ok && sub == (IB ? dpos : j % LB)) {
+            if (ok && sub == (IB ? dpos * J + j : j % LB)) {
 #pragma clang fp contract(off)
                 const float tt = (float)s1 * (IB ? sc.d : bf.d[j / LB]);
                 const float uu = (float)s2 * (IB ? sc.dm : bf.dm[j / LB]);

@@ -129,21 +129,22 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
         float dw[JM];
         int zp[JM];
     };
-    // With one chunk per lane and window (J = 1) the D items of a ring turn
-    // share one load instead: lane `sub` < D of a block's LB lanes loads the
-    // scale and zero point of that block in item t0 + sub of the turn that
-    // starts at item t0, and scales that item's block sum itself.
-    constexpr bool IB = J == 1 && D <= LB;
+    // When a block's LB lanes outnumber the J * D (item, iteration) pairs of
+    // a ring turn, the turn shares one load instead: lane `sub` < J * D of the
+    // block's lanes loads the scale and zero point of iteration sub % J of
+    // item t0 + sub / J (the turn starting at item t0), and scales that
+    // block sum itself.
+    constexpr bool IB = J * D <= LB;
     struct Sc {
         float dw;
         int zp;
     };
     auto load_sc = [&](int tb) __attribute__((always_inline)) {
         Sc sc;
-        const int sub = gl % LB;
-        const rs::Item it = map.item(tb + (sub < D ? sub : 0));
-        const int c = it.win * L + (gl - sub);  // the first chunk of this lane's block
-        const bool ok = sub < D && it.live && c < chunks;
+        const int sub = gl % LB, di = sub / J, jj = sub % J;
+        const rs::Item it = map.item(tb + (di < D ? di : 0));
+        const int c = (it.win * J + jj) * L + (gl - sub);  // the first chunk of that block
+        const bool ok = di < D && it.live && c < chunks;
         const int b = c / LB;
         sc.dw = __builtin_bit_cast(float,
                                    __builtin_amdgcn_raw_buffer_load_b32(rd, ok ? 4 * (it.r * nb + b) : kOOB, 0, 0));
@@ -209,7 +210,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             p += rs::dppi<rs::kX1>(p);
             p += rs::dppi<rs::kX2>(p);
             if constexpr (LB == 8) p += rs::dppi<rs::kM8>(p);
-            if (ok && sub == (IB ? dpos : j % LB)) {
+            if (ok && sub == (IB ? dpos * J + j : j % LB)) {
 #pragma clang fp contract(off)
                 const int sumi = p - ((IB ? sc.zp : bf.zp[j / LB]) - off) * sq[b];
                 float tt = (float)sumi * (IB ? sc.dw : bf.dw[j / LB]);
