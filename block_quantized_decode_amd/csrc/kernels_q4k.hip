@@ -265,7 +265,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
 
 template <int L, int J, int P, int WPB>
 hipError_t launch_cfg(const Q4kArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
-    constexpr int D = J <= 2 ? 4 : J <= 4 ? 3 : 2;
+    constexpr int D = J <= 2 ? 4 : 2;
     auto kern = k_q4k<L, J, D, P, WPB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

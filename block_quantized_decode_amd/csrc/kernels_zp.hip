@@ -59,7 +59,7 @@ using rs::v4i;
 #define QMV_ZP_D12 4
 #endif
 #ifndef QMV_ZP_D34  // ... and for 3-4 chunks per lane
-#define QMV_ZP_D34 3
+#define QMV_ZP_D34 2
 #endif
 
 constexpr int BLK = 128;    // elements per block
