@@ -313,7 +313,9 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 
 template <int BITS, int L, int J, int P, int WPB>
 hipError_t launch_cfg(const ZpArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
-    constexpr int D = J <= 2 ? QMV_ZP_D12 : J <= 4 ? QMV_ZP_D34 : 2;
+    // 2 stages wherever 4 would take the ring turn past one scale load
+    // (J * D > LB): measured faster on every such shape
+    constexpr int D = (J == 1 || (J == 2 && BITS == 8)) ? QMV_ZP_D12 : J <= 4 ? QMV_ZP_D34 : 2;
     auto kern = k_zp<BITS, L, J, D, P, WPB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
