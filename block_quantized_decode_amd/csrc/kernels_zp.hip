@@ -311,11 +311,15 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     }
 }
 
+// Register ring depth: 2 stages wherever 4 would take the ring turn past one
+// scale load (J * D > LB), measured faster on every such shape.
+constexpr int ring_depth(int bits, int J) {
+    return (J == 1 || (J == 2 && bits == 8)) ? QMV_ZP_D12 : J <= 4 ? QMV_ZP_D34 : 2;
+}
+
 template <int BITS, int L, int J, int P, int WPB>
 hipError_t launch_cfg(const ZpArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
-    // 2 stages wherever 4 would take the ring turn past one scale load
-    // (J * D > LB): measured faster on every such shape
-    constexpr int D = (J == 1 || (J == 2 && BITS == 8)) ? QMV_ZP_D12 : J <= 4 ? QMV_ZP_D34 : 2;
+    constexpr int D = ring_depth(BITS, J);
     auto kern = k_zp<BITS, L, J, D, P, WPB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -351,7 +355,14 @@ hipError_t launch_bits(const ZpArgs &a, int num_cu, hipStream_t s, const char **
     const int chunks = (BITS == 8 ? a.K : a.K / 2) / 16;
     const size_t lds_x = ((size_t)a.K + 8 * (size_t)(a.K / BLK) + 15) & ~(size_t)15;
     const int nrow = a.r1 - a.r0;
-    const rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, BITS == 8 ? 8 : 4, 8, BITS == 8 ? 64 : 32);
+    rs::Shape sh = rs::pick_shape(chunks, nrow, num_cu, BITS == 8 ? 8 : 4, 8, BITS == 8 ? 64 : 32);
+    // rows already shared by teams: more wavefronts per row until a ring
+    // turn takes one scale load (J * D <= LB); measured faster on the
+    // Llama-7B W_down shape (8-bit P = 2 -> 4: 13.3 -> 11.8 us)
+    while (sh.P > 1 && sh.P < 8 && sh.J * ring_depth(BITS, sh.J) > (BITS == 8 ? 8 : 4)) {
+        sh.P *= 2;
+        sh.J = rs::pick_j(chunks, sh.P);
+    }
     const int waves = sh.wgpc * num_cu * sh.wpb;
     if (sh.P == 1) {
         const int groups_per_wg = sh.wpb * (64 / sh.L);
