@@ -658,7 +658,7 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
 
 template <int QT, int NBL, int D, int WPB>
 hipError_t launch_mq_t(const RowsArgs &a, hipStream_t s, const char **name) {
-    static char kname[64];
+    static const std::string kname = variant_name("mq_q%d_n%d_d%d_w%d", QT, NBL, D, WPB);
     constexpr int D0 = QMV_FX_D0 < D - 1 ? QMV_FX_D0 : D - 1;
     auto kern = k_mq<QT, NBL, D, D0, WPB>;
     const int nrows = a.r1 - a.r0;
@@ -666,15 +666,12 @@ hipError_t launch_mq_t(const RowsArgs &a, hipStream_t s, const char **name) {
     const int rw = min(kMqRwCap, ((nrows + groups - 1) / groups + 3) / 4 * 4);
     const int grid = (nrows + rw - 1) / rw;
     const size_t lds = (size_t)4 * WPB * 4 * rw * 4;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    // the largest size any call of this kernel asks for (rw at its cap)
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), (size_t)4 * WPB * 4 * kMqRwCap * 4);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.M, a.xq, a.xd,
                        a.r0, a.r1, rw);
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "mq_q%d_n%d_d%d_w%d", QT, NBL, D, WPB);
-    *name = kname;
+    *name = kname.c_str();
     return hipGetLastError();
 }
 
@@ -690,29 +687,23 @@ hipError_t launch_mq(const RowsArgs &a, hipStream_t s, const char **name) {
 
 template <int QT, int M, int AX, int T, int NBL, int D, int WPB, bool KS = true>
 hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
-    static char kname[64];
+    static const std::string kname =
+        AX != kActQ8 ? variant_name("fx%s_q%d_t%d_n%d_d%d_w%d%s", AX == kActRms ? "n" : (AX == kActSilu ? "s" : ""),
+                                    QT, T, NBL, D, WPB, KS ? "" : "_rows")
+                     : variant_name("px_q%d_m%d_t%d_n%d_d%d_w%d%s", QT, M, T, NBL, D, WPB, KS ? "" : "_rows");
     constexpr int D0W = AX == kActRms ? QMV_FX_D0_RMS : (AX == kActSilu ? QMV_FX_D0_SILU : QMV_FX_D0);
     constexpr int D0 = D0W < D - 1 ? D0W : D - 1;
-    constexpr bool FX = AX != kActQ8;
     auto kern = k_fx<QT, M, AX, T, NBL, D, D0, WPB, KS>;
     const int nrows = a.r1 - a.r0;
     const int grid = (nrows + rw - 1) / rw;
     const size_t lds = KS ? (size_t)M * WPB * rw * 4 : 0;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (KS) {  // the largest size any call of this kernel asks for (rw at its cap)
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), (size_t)M * WPB * rw_cap(M) * 4);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq, a.xd,
                        AX == kActSilu ? a.xu : a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1, rw);
-    if (kname[0] == 0) {
-        if (FX)
-            snprintf(kname, sizeof kname, "fx%s_q%d_t%d_n%d_d%d_w%d%s",
-                     AX == kActRms ? "n" : (AX == kActSilu ? "s" : ""), QT, T, NBL, D, WPB, KS ? "" : "_rows");
-        else
-            snprintf(kname, sizeof kname, "px_q%d_m%d_t%d_n%d_d%d_w%d%s", QT, M, T, NBL, D, WPB, KS ? "" : "_rows");
-    }
-    *name = kname;
+    *name = kname.c_str();
     return hipGetLastError();
 }
 

@@ -323,18 +323,14 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
     constexpr int lds_stage = WPB * Rg::BYTES, lds_part = WPB * RT * MT * 1024;
     constexpr int lds = lds_stage > lds_part ? lds_stage : lds_part;
     static_assert(lds <= 160 * 1024, "LDS budget");
-    static char kname[64];
+    static const std::string kname = variant_name("mm%s_q%d_mt%d_rt%d_w%d_d%d", PK ? "p" : "", QT, MT, RT, WPB, D);
     auto kern = k_mm<QT, MT, RT, WPB, D, PK>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-    }
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
     const int grid = (a.r1 - a.r0 + 16 * RT - 1) / (16 * RT);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.Y, PK ? static_cast<const int8_t *>(a.pq) : a.wq,
                        PK ? a.pd : a.wd, a.rows, a.K, a.xq, a.xd, a.M, a.r0, a.r1);
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "mm%s_q%d_mt%d_rt%d_w%d_d%d", PK ? "p" : "", QT, MT, RT, WPB, D);
-    *name = kname;
+    *name = kname.c_str();
     return hipGetLastError();
 }
 

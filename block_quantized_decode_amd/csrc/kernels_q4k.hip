@@ -267,16 +267,12 @@ template <int L, int J, int P, int WPB>
 hipError_t launch_cfg(const Q4kArgs &a, int grid, int rows_wg, size_t lds, hipStream_t s, const char **name) {
     constexpr int D = J <= 2 ? 4 : 2;
     auto kern = k_q4k<L, J, D, P, WPB>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static const std::string kname = variant_name("q4k_l%d_j%d_d%d_p%d_w%d", L, J, D, P, WPB);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.sc, a.mn, a.d, a.dmin, a.rows, a.K,
                        a.x, a.xq_out, a.xd_out, a.r0, a.r1, rows_wg);
-    static char kname[48];
-    if (kname[0] == 0) snprintf(kname, sizeof kname, "q4k_l%d_j%d_d%d_p%d_w%d", L, J, D, P, WPB);
-    *name = kname;
+    *name = kname.c_str();
     return hipGetLastError();
 }
 

@@ -282,21 +282,16 @@ k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__rest
 
 template <int QT, int M, bool FX, int J, int R, int WPB>
 hipError_t launch_rows_t(const RowsArgs &a, hipStream_t s, const char **name) {
-    static char kname[96];
+    static const std::string kname = variant_name("rows_q%d_m%d%s_j%d_r%d_w%d", QT, M, FX ? "_fx" : "", J, R, WPB);
     auto kern = k_rows<QT, M, FX, J, R, WPB>;
     const size_t lds = lds_bytes(M, a.K, FX);
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
     const int nunits = (a.r1 - a.r0 + R - 1) / R;
     const int grid = (nunits + WPB - 1) / WPB;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq,
                        a.xd, a.xq_out, a.xd_out, a.r0, a.r1);
-    if (kname[0] == 0)
-        snprintf(kname, sizeof kname, "rows_q%d_m%d%s_j%d_r%d_w%d", QT, M, FX ? "_fx" : "", J, R, WPB);
-    *name = kname;
+    *name = kname.c_str();
     return hipGetLastError();
 }
 

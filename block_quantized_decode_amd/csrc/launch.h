@@ -3,9 +3,32 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <string>
 
 namespace qmv {
+
+// Printf-style kernel variant name.  Launchers keep the result in a
+// function-local static const (initialised once per template instantiation,
+// thread-safe), so the pointer handed to qmv_last_kernel stays valid and no
+// thread ever writes a name another thread reads.
+inline std::string variant_name(const char *fmt, ...) {
+    char buf[96];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    return std::string(buf);
+}
+
+// Raises the dynamic-LDS limit of kernel `kern` on the current device to
+// `bytes` if the limit granted so far is smaller (nothing to do up to the
+// 64 KiB default).  hipFuncSetAttribute runs at most once per kernel,
+// device and larger size; thread-safe (qmv_api.cpp).
+hipError_t allow_lds(const void *kern, size_t bytes);
 
 // Arguments of the weight-streaming product for M = 1 .. 8 activation rows.
 struct RowsArgs {
@@ -104,5 +127,13 @@ hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hi
 // Q4_0 quantization of nblk blocks of 32 floats (weights).
 hipError_t launch_quant_q4(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,
                            const char **name);
+
+// Measurement kernels (kernels_ceiling.hip): a plain streaming read of
+// `bytes` (multiple of 16) with `depth` (4 or 8) 16-byte loads in flight per
+// thread, and chains of int8 matrix-core instructions of one shape.
+hipError_t launch_ceiling_stream(uint32_t *sink, const void *buf, int64_t bytes, int32_t wgs, int32_t depth,
+                                 hipStream_t s, const char **name);
+hipError_t launch_ceiling_mfma(uint32_t *sink, int32_t shape, int32_t iters, int32_t wgs, int32_t a, int32_t b,
+                               hipStream_t s, const char **name);
 
 }  // namespace qmv

@@ -19,6 +19,9 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "launch.h"
 
@@ -27,17 +30,21 @@ namespace {
 constexpr int kMaxDevices = 64;
 // 0 = unchecked, 1 = gfx950, 2 = other architecture
 std::atomic<int> g_arch[kMaxDevices];
-int g_num_cu[kMaxDevices];
+std::atomic<int> g_num_cu[kMaxDevices];
 
 thread_local const char *t_last_kernel = "";
 
 bool diag_enabled() {
-    static int v = -1;
-    if (v < 0) {
+    static const bool v = [] {
         const char *e = getenv("QMV_DIAG");
-        v = (e != nullptr && e[0] != '\0' && e[0] != '0') ? 1 : 0;
-    }
-    return v == 1;
+        return e != nullptr && e[0] != '\0' && e[0] != '0';
+    }();
+    return v;
+}
+
+int num_cu(int dev) {
+    const int n = (dev >= 0 && dev < kMaxDevices) ? g_num_cu[dev].load(std::memory_order_relaxed) : 0;
+    return n > 0 ? n : 256;
 }
 
 qmv_status device_check(int *dev_out) {
@@ -54,7 +61,7 @@ qmv_status device_check(int *dev_out) {
             return QMV_E_DEVICE;
         }
         st = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-        g_num_cu[dev] = p.multiProcessorCount;
+        g_num_cu[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
         g_arch[dev].store(st, std::memory_order_release);
         if (diag_enabled())
             fprintf(stderr, "[qmv] device %d: %s, %d CUs -> %s\n", dev, p.gcnArchName, p.multiProcessorCount,
@@ -129,7 +136,7 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     a.xd_out = xq_out ? xq_out->d : nullptr;
     a.r0 = r0;
     a.r1 = r1;
-    a.num_cu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+    a.num_cu = num_cu(dev);
     const char *name = "";
     hipError_t e = qmv::launch_fx(a, static_cast<hipStream_t>(stream), &name);
     if (e == hipErrorNotSupported && xn == nullptr && xu == nullptr)
@@ -253,7 +260,7 @@ qmv_status matvec_zp_fx(float *y, const qmv_zptensor *W, const float *x, qmv_qac
     a.r0 = r0;
     a.r1 = r1;
     const char *name = "";
-    const int ncu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+    const int ncu = num_cu(dev);
     hipError_t e = qmv::launch_zp(a, ncu, static_cast<hipStream_t>(stream), &name);
     return finish(e, name, (long)(r1 - r0));
 }
@@ -293,7 +300,7 @@ qmv_status matvec_q4k_fx(float *y, const qmv_q4ktensor *W, const float *x, qmv_q
     a.r0 = r0;
     a.r1 = r1;
     const char *name = "";
-    const int ncu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+    const int ncu = num_cu(dev);
     hipError_t e = qmv::launch_q4k(a, ncu, static_cast<hipStream_t>(stream), &name);
     return finish(e, name, (long)(r1 - r0));
 }
@@ -320,7 +327,7 @@ qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, c
         a.r0 = r0;
         a.r1 = r1;
         const char *name = "";
-        const int ncu = (dev >= 0 && dev < kMaxDevices && g_num_cu[dev] > 0) ? g_num_cu[dev] : 256;
+        const int ncu = num_cu(dev);
         hipError_t e = qmv::launch_mm(a, ncu, static_cast<hipStream_t>(stream), &name);
         if ((st = finish(e, name, (r1 - r0 + 15) / 16)) != QMV_OK) return st;
     }
@@ -328,6 +335,25 @@ qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, c
 }
 
 }  // namespace
+
+namespace qmv {
+
+hipError_t allow_lds(const void *kern, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::map<std::pair<const void *, int>, size_t> granted;  // (kernel, device) -> bytes
+    std::lock_guard<std::mutex> lock(mu);
+    size_t &g = granted[std::make_pair(kern, dev)];
+    if (g >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) g = bytes;
+    return e;
+}
+
+}  // namespace qmv
 
 extern "C" {
 
@@ -498,6 +524,32 @@ qmv_status qmv_gemm_q8_packed(float *Y, const qmv_packed *P, const qmv_qtensor *
 qmv_status qmv_gemm_q4_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X, int32_t r0, int32_t r1,
                               void *stream) {
     return gemm_packed(QMV_Q4_0, Y, P, X, r0, r1, stream);
+}
+
+qmv_status qmv_ceiling_stream_read(uint32_t *sink, const void *buf, int64_t bytes, int32_t workgroups,
+                                   int32_t depth, void *stream) {
+    if (sink == nullptr || buf == nullptr || !aligned(buf, 16) || !aligned(sink, 4)) return QMV_E_ARG;
+    if (depth != 4 && depth != 8) return QMV_E_ARG;
+    if (bytes < 16 || (bytes % 16) != 0 || workgroups < 1 || workgroups > 65536) return QMV_E_SHAPE;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    const char *name = "";
+    hipError_t e = qmv::launch_ceiling_stream(sink, buf, bytes, workgroups, depth, static_cast<hipStream_t>(stream),
+                                              &name);
+    return finish(e, name, workgroups);
+}
+
+qmv_status qmv_ceiling_mfma_i8(uint32_t *sink, int32_t shape, int32_t iters, int32_t workgroups, int32_t a,
+                               int32_t b, void *stream) {
+    if (sink == nullptr || !aligned(sink, 4)) return QMV_E_ARG;
+    if (shape < 0 || shape > 2) return QMV_E_ARG;
+    if (iters < 0 || workgroups < 1 || workgroups > 65536) return QMV_E_SHAPE;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    const char *name = "";
+    hipError_t e = qmv::launch_ceiling_mfma(sink, shape, iters, workgroups, a, b, static_cast<hipStream_t>(stream),
+                                            &name);
+    return finish(e, name, workgroups);
 }
 
 const char *qmv_status_str(qmv_status s) {

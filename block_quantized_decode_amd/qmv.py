@@ -90,6 +90,8 @@ _SIGS = {
     "qmv_matvec_q4k_fx": [_P, ctypes.POINTER(Q4kTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32,
                           _P],
     "qmv_device_check": [],
+    "qmv_ceiling_stream_read": [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_ceiling_mfma_i8": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P],
 }
 
 
@@ -577,3 +579,26 @@ def prepare_matvec_q4k_fx(q, sc, mn, d, dmin, x, y, r0=None, r1=None, stream=Non
     r1 = W.rows if r1 is None else r1
     args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), None, r0, r1]
     return Prepared("qmv_matvec_q4k_fx", args, [W, q, sc, mn, d, dmin, x, y], stream)
+
+
+# ---- measurement helpers (not on the product path)
+
+def qmv_ceiling_stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, depth: int = 4,
+                            stream=None) -> None:
+    """Stream-read every byte of the device tensor buf (uint32 sink of
+    `workgroups` entries receives per-workgroup XORs of its 32-bit words)."""
+    _dev(buf)
+    _dev(sink, (torch.int32, torch.uint32))
+    _check(lib().qmv_ceiling_stream_read(sink.data_ptr(), buf.data_ptr(), buf.numel() * buf.element_size(),
+                                         workgroups, depth, _stream() if stream is None else stream),
+           "qmv_ceiling_stream_read")
+
+
+def qmv_ceiling_mfma_i8(sink: torch.Tensor, shape: int, iters: int, workgroups: int, a: int = 1, b: int = 1,
+                        stream=None) -> None:
+    """Chains of int8 matrix-core instructions (shape 0: 16x16x32, 1:
+    16x16x64, 2: 32x32x32); sink (4 * workgroups int32) receives per-wavefront
+    sums of the results."""
+    _dev(sink, (torch.int32, torch.uint32))
+    _check(lib().qmv_ceiling_mfma_i8(sink.data_ptr(), shape, iters, workgroups, a, b,
+                                     _stream() if stream is None else stream), "qmv_ceiling_mfma_i8")

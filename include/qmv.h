@@ -374,6 +374,41 @@ qmv_status qmv_gemm_q8_packed(float *Y, const qmv_packed *P, const qmv_qtensor *
 qmv_status qmv_gemm_q4_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X,
                               int32_t r0, int32_t r1, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not on the product path).  The bench divides each
+ * kernel's rate by what these reach on the same chip: the rate at which a
+ * plain kernel streams device memory (the "ONNX Runtime" page, "How we got
+ * there" item 1, sets its kernel against a STREAM floor; the
+ * "SKaiNET-native-kernels" page measures effective weight bandwidth as
+ * bytes over time) and the rate of the int8 matrix-core instructions with
+ * their operands in registers.
+ *
+ * qmv_ceiling_stream_read: reads `bytes` (a multiple of 16, at least 16) of
+ *   buf (device memory, 16-byte aligned) with `workgroups` (1 .. 65536)
+ *   workgroups of 1024 threads, each thread keeping `depth` (4 or 8) 16-byte
+ *   non-temporal loads in flight per round, the grid striding over the
+ *   buffer.  sink[w] (workgroups uint32 of device memory) receives the XOR
+ *   of the 32-bit words workgroup w read, so the XOR over all of sink is the
+ *   XOR of every 32-bit word of buf.
+ * qmv_ceiling_mfma_i8: `workgroups` (1 .. 65536) workgroups of 4
+ *   wavefronts; each wavefront runs 4 independent chains of `iters` (>= 0)
+ *   instructions of one shape (0: v_mfma_i32_16x16x32_i8, 1:
+ *   v_mfma_i32_16x16x64_i8, 2: v_mfma_i32_32x32x32_i8) on operands whose
+ *   bytes are all a (the A operand) and all b (B), as signed bytes.  Every
+ *   result element ends at iters * kdepth * a * b (kdepth = 32, 64, 32), and
+ *   sink[4 w + v] (4 * workgroups uint32 of device memory) receives the sum
+ *   modulo 2^32 of the 4 chains' elements of wavefront v of workgroup w:
+ *   4 * E * iters * kdepth * a * b with E = 256 (16 x 16 shapes) or 1024
+ *   (32 x 32).  Each launch performs workgroups * 16 * iters * 2 * E *
+ *   kdepth integer operations.
+ * Errors: QMV_E_ARG (null or misaligned pointers, depth or shape out of
+ * range), QMV_E_SHAPE (sizes out of range), then the device checks.
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_ceiling_stream_read(uint32_t *sink, const void *buf, int64_t bytes, int32_t workgroups,
+                                   int32_t depth, void *stream);
+qmv_status qmv_ceiling_mfma_i8(uint32_t *sink, int32_t shape, int32_t iters, int32_t workgroups, int32_t a,
+                               int32_t b, void *stream);
+
 /* Text of a status code (static storage). */
 const char *qmv_status_str(qmv_status s);
 

@@ -352,3 +352,29 @@ def test_no_device_is_an_error_not_a_crash(lib):
     f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, P]
     assert f(Y, ctypes.byref(_kt()), A + 0x1000, None, 0, 8, None) == st
     assert lib.qmv_last_kernel().decode() == ""
+
+
+def test_ceiling_validation(lib):
+    """The measurement entry points check their arguments like the rest."""
+    P = ctypes.c_void_p
+    f = lib.qmv_ceiling_stream_read
+    f.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
+    assert f(None, A, 1024, 4, 4, None) == E_ARG
+    assert f(Y, None, 1024, 4, 4, None) == E_ARG
+    assert f(Y, A + 8, 1024, 4, 4, None) == E_ARG        # buffer not 16-byte aligned
+    assert f(Y, A, 1024, 4, 3, None) == E_ARG            # depth 4 or 8
+    assert f(Y, A, 1000, 4, 4, None) == E_SHAPE          # not a multiple of 16
+    assert f(Y, A, 0, 4, 4, None) == E_SHAPE
+    assert f(Y, A, 1024, 0, 4, None) == E_SHAPE
+    assert f(Y, A, 1024, 65537, 4, None) == E_SHAPE
+    g = lib.qmv_ceiling_mfma_i8
+    g.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+    assert g(None, 0, 10, 4, 1, 1, None) == E_ARG
+    assert g(Y + 2, 0, 10, 4, 1, 1, None) == E_ARG
+    assert g(Y, 3, 10, 4, 1, 1, None) == E_ARG           # shape 0..2
+    assert g(Y, 0, -1, 4, 1, 1, None) == E_SHAPE
+    assert g(Y, 0, 10, 0, 1, 1, None) == E_SHAPE
+    st = lib.qmv_device_check()
+    if st != OK:
+        assert f(Y, A, 1024, 4, 4, None) == st
+        assert g(Y, 1, 10, 4, 1, 1, None) == st

@@ -19,7 +19,7 @@ import torch
 
 import pins
 from block_quantized_decode_amd import qmv, synth
-from gpu_util import announce, check_close, dev, host
+from gpu_util import announce, check_close, check_gemm_all, dev, host
 from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -181,7 +181,7 @@ def test_packed_exact_unit_scales(qtype, m):
 def test_packed_full_size(qtype, rows, k, m):
     """The bench's batched shapes (Llama-7B W_up and W_down at 16 and 64
     activation rows) and a case with more workgroups than compute units:
-    the same bits as the row-major product, and sampled rows within
+    the same bits as the row-major product, and every output within
     tolerance of the oracle."""
     announce(f"packed gemm full size q{qtype} {rows}x{k} m={m}")
     rng = np.random.default_rng(4600 + rows + k + m + qtype)
@@ -190,8 +190,5 @@ def test_packed_full_size(qtype, rows, k, m):
     Yp = host(_gemm_packed(qtype)(_pack(qtype, wq, wd), dev(xq), dev(xd)))
     Y = host(_gemm(qtype)(dev(wq), dev(wd), dev(xq), dev(xd)))
     assert np.array_equal(Yp.view(np.uint32), Y.view(np.uint32))
-    for r0 in (0, rows // 2 - 3, rows - 7):
-        r1 = r0 + 7
-        Yref = orc.gemm(qtype, wq, wd, xq, xd, r0, r1)
-        for i in range(m):
-            check_close(qtype, Yp[i], Yref[i], wq, wd, xq[i], xd[i], r0, r1, what=f"rows [{r0},{r1}) m row {i}")
+    worst = check_gemm_all(qtype, Yp, wq, wd, xq, xd, what=f"packed q{qtype} {rows}x{k} m={m}")
+    print(f"  all {m} x {rows} outputs, max |err| / tol = {worst:.4f}")

@@ -17,7 +17,7 @@ import torch
 
 import pins
 from block_quantized_decode_amd import qmv, synth
-from gpu_util import announce, dev, host
+from gpu_util import announce, check_zp_all, dev, host
 from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -127,21 +127,42 @@ def test_quantize_b128(k):
     assert np.array_equal(host(d).view(np.uint32), dr.view(np.uint32))
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("rows,k", [(4864, 896), (896, 4864), (151936, 896), (11008, 4096), (4096, 11008)])
-def test_zp_full_size(bits, rows, k):
-    """The bench's shapes (Qwen2.5-0.5B W_gate / W_up, W_down and lm_head;
-    Llama-7B W_up and W_down) at full size: codes bit-exact, sampled row
-    ranges within tolerance of the oracle."""
+# Full-size shapes and the launch each one takes on a 256-compute-unit
+# MI355X (names: lanes per row l, chunks per lane j, ring depth d, team of p
+# wavefronts, w wavefronts per workgroup), so that a change of dispatch shows:
+#   - the bench's shapes: Qwen2.5-0.5B W_gate / W_up, W_down and lm_head,
+#     Llama-7B W_up and W_down;
+#   - rows in [2048, 4096) at K = 11008, where teams take more wavefronts
+#     until a ring turn takes one scale load (p = 4);
+#   - one wavefront per row with two windows per row, the accumulator
+#     carried across items (8-bit K = 16384 and 4-bit K = 32768 at 8192 rows).
+FULL = [
+    (4, 4864, 896, "zp4_l32_j1_d4_p1_w8"), (8, 4864, 896, "zp8_l64_j1_d4_p1_w8"),
+    (4, 896, 4864, "zp4_l64_j1_d4_p4_w16"), (8, 896, 4864, "zp8_l64_j2_d4_p4_w16"),
+    (4, 151936, 896, "zp4_l32_j1_d4_p1_w8"), (8, 151936, 896, "zp8_l64_j1_d4_p1_w8"),
+    (4, 11008, 4096, "zp4_l64_j2_d2_p1_w16"), (8, 11008, 4096, "zp8_l64_j4_d2_p1_w16"),
+    (4, 4096, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 4096, 11008, "zp8_l64_j3_d2_p4_w16"),
+    (4, 2048, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 2048, 11008, "zp8_l64_j3_d2_p4_w16"),
+    (4, 3001, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 3001, 11008, "zp8_l64_j3_d2_p4_w16"),
+    (8, 8192, 16384, "zp8_l64_j8_d2_p1_w16"), (4, 8192, 32768, "zp4_l64_j8_d2_p1_w16"),
+]
+
+
+@pytest.mark.parametrize("bits,rows,k,kernel", FULL, ids=[f"zp{b}-{r}x{k}" for b, r, k, _ in FULL])
+def test_zp_full_size(bits, rows, k, kernel):
+    """Full size: codes bit-exact, every row within tolerance of the oracle,
+    and the launch shape named above."""
     announce(f"zp{bits} full size {rows}x{k}")
     rng = np.random.default_rng(5400 + rows + k + bits)
     wq, wd, wzp = synth.raw_zp(rng, bits, rows, k, with_zp=(rows != 151936))
     x = _x(rng, k)
     xq, xd = orc.quantize_q8_b128(x)
     y, qo, do = _run(bits, wq, wd, wzp, x)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert qmv.last_kernel() == kernel, qmv.last_kernel()
     assert np.array_equal(qo, xq) and np.array_equal(do.view(np.uint32), xd.view(np.uint32))
-    for r0 in (0, rows // 2 - 5, rows - 11):
-        _check(bits, y, wq, wd, wzp, xq, xd, r0, r0 + 11, f"full {rows}x{k} [{r0},{r0 + 11})")
+    worst = check_zp_all(bits, y, wq, wd, wzp, xq, xd, what=f"full {rows}x{k}")
+    print(f"  {qmv.last_kernel()}: all {rows} rows, max |err| / tol = {worst:.4f}")
 
 
 def test_zp_and_packed_graph_replay():
