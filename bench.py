@@ -87,8 +87,9 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 10}), flush=True)
 
 
-# The sources the timed kernel (the split-K fused matvec) is compiled from.
-TIMED_KERNEL_SOURCES = ("device_common.h", "kernels_fx.hip")
+# The sources the timed kernel (the split-K fused matvec) is compiled from:
+# the kernel file and every header it includes.
+TIMED_KERNEL_SOURCES = ("device_common.h", "launch.h", "kernels_fx.hip")
 
 
 def kernel_source_sha() -> str:
@@ -133,7 +134,9 @@ def main():
         from block_quantized_decode_amd import qmv
         torch.cuda.set_device(0)
         qmv.qmv_device_check()
-        print(json.dumps(batched_bench(torch.device("cuda:0"))), flush=True)
+        stream = torch.cuda.Stream()
+        ceil = ceilings_bench(stream, per_launch_bytes=28_240_896, step_bytes=16 * 28_240_896)
+        print(json.dumps(batched_bench(torch.device("cuda:0"), ceil=ceil, sclk_mhz=gpu_clock_mhz())), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -183,7 +186,14 @@ def main():
             for c in calls:
                 c()
     torch.cuda.synchronize()
-    kernel = qmv.last_kernel()
+    # the kernel variant each matrix shape runs (one per distinct shape)
+    kernels = {}
+    for (mt, *_r), c in zip(mats, calls):
+        with torch.cuda.stream(stream):
+            c()
+        kernels.setdefault(qmv.last_kernel(), mt.name.split(".")[0])
+    torch.cuda.synchronize()
+    kernel = " + ".join(f"{k} ({v})" for k, v in kernels.items())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for c in calls:
@@ -234,6 +244,7 @@ def main():
     value = weight_bytes / (ms_per_step * 1e-3) / 1e9
     sha = kernel_source_sha()
     traffic = load_traffic(kernel, sha)
+    ceil = ceilings_bench(stream, per_launch_bytes=int(avg_algo_bytes), step_bytes=int(sum(algo_bytes)))
 
     # ---- the same stack at M = 4 (small-batch decode): 4 activation rows per
     # matrix, quantized once with qmv_quantize_q8, one qmv_gemm per matrix
@@ -258,7 +269,7 @@ def main():
     # ---- the M >= 16 path (second half of the metric), timed the same way
     batched = None
     if not args.no_batched:
-        batched = batched_bench(dev)
+        batched = batched_bench(dev, ceil=ceil, sclk_mhz=sclk)
 
     # ---- CPU oracle baseline on a bounded sample (and a parity spot-check)
     cpu = None
@@ -290,7 +301,7 @@ def main():
             "event_timed_launch_us": {k: round(float(np.mean(v)), 3) for k, v in per_matrix_us.items()},
             "setup_s": round(setup_s, 1),
         },
-        "env": {"launch_floor_us": floor_us, "gpu_sclk_mhz": sclk},
+        "env": {"launch_floor_us": floor_us, "gpu_sclk_mhz": sclk, "ceilings": ceil},
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
@@ -298,6 +309,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "frac_of_measured_stream_ceiling": round(achieved_gbs / ceil["stream_read"]["per_launch"]["gb_s"], 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": round(avg_algo_bytes),
             "avg_launch_us": round(avg_launch_us, 3),
@@ -315,6 +327,62 @@ def main():
     print(json.dumps(line), flush=True)
     if cpu is not None and not cpu.get("parity_ok", True):
         sys.exit(1)
+
+
+def ceilings_bench(stream, per_launch_bytes, step_bytes):
+    """What plain kernels reach on this chip, measured like the step:
+      * stream_read.per_launch: 16 buffers of per_launch_bytes read in turn
+        by one launch each (a graph of 16 launches, replayed), the best of
+        a few grid shapes and load depths -- the ceiling of a single
+        launch of that size, ramp and drain included;
+      * stream_read.one_launch: step_bytes read by one launch (the plateau
+        without per-launch ramp and drain);
+      * mfma_i8: int8 matrix-core instructions with operands in registers,
+        4 independent chains per wavefront, the best grid, per instruction
+        shape (TOP/s; the vendor's dense int8 peak is 5000)."""
+    import torch
+
+    from block_quantized_decode_amd import qmv
+
+    dev = torch.device("cuda:0")
+    n16 = (per_launch_bytes + 15) // 16 * 16
+    bufs = [torch.ones(n16 // 4, dtype=torch.int32, device=dev) for _ in range(16)]
+    big = torch.ones((step_bytes + 15) // 16 * 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    sid = stream.cuda_stream
+    per = None
+    for wgs in (256, 512, 1024):
+        for depth in (4, 8):
+            calls = [qmv.Prepared("qmv_ceiling_stream_read", [sink.data_ptr(), b.data_ptr(), n16, wgs, depth], [b])
+                     for b in bufs]
+            us = _graph_us(calls, stream, reps=20) / len(calls)
+            if per is None or us < per["us"]:
+                per = {"us": round(us, 3), "gb_s": round(n16 / (us * 1e-6) / 1e9, 1), "workgroups": wgs,
+                       "depth": depth, "bytes": n16}
+    one = None
+    nb = big.numel() * 4
+    for wgs in (1024, 2048, 4096):
+        calls = [qmv.Prepared("qmv_ceiling_stream_read", [sink.data_ptr(), big.data_ptr(), nb, wgs, 8], [big])]
+        us = _graph_us(calls * 4, stream, reps=5) / 4
+        if one is None or us < one["us"]:
+            one = {"us": round(us, 2), "gb_s": round(nb / (us * 1e-6) / 1e9, 1), "workgroups": wgs, "bytes": nb}
+    del bufs, big
+    mfma = {}
+    for shape, (nm, e, kd) in enumerate((("16x16x32", 256, 32), ("16x16x64", 256, 64), ("32x32x32", 1024, 32))):
+        best = None
+        for wgs in (512, 1024, 2048):
+            iters = 2000 if e == 256 else 500
+            calls = [qmv.Prepared("qmv_ceiling_mfma_i8", [sink.data_ptr(), shape, iters, wgs, 1, 1], [])]
+            us = _graph_us(calls * 4, stream, reps=3) / 4
+            tops = wgs * 16 * iters * 2 * e * kd / (us * 1e-6) / 1e12
+            if best is None or tops > best["top_s"]:
+                best = {"top_s": round(tops, 1), "us": round(us, 2), "workgroups": wgs}
+        mfma[nm] = best
+    torch.cuda.empty_cache()
+    return {"stream_read": {"per_launch": per, "one_launch": one,
+                            "pct_hbm_peak_per_launch": round(100.0 * per["gb_s"] / HBM_PEAK_GBS, 2),
+                            "pct_hbm_peak_one_launch": round(100.0 * one["gb_s"] / HBM_PEAK_GBS, 2)},
+            "mfma_i8": mfma, "mfma_i8_best_top_s": max(v["top_s"] for v in mfma.values())}
 
 
 def launch_floor(stream, n=16, reps=50):
@@ -720,7 +788,7 @@ def small_batch_bench(wl, qtype, mats, stream, steps, warmup):
             "gop_s": round(ops / (ms * 1e-3) / 1e9, 1), "launches_per_step": len(calls), "kernel": kernel}
 
 
-def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
+def batched_bench(dev, name="batched_ffn_q4q8", replays=5, ceil=None, sclk_mhz=None):
     """The M >= 16 product (qmv_gemm_q4 / _q8, the int8 matrix-core kernel) on
     the batched workload: both matrices, both weight formats, M = 16 and 64.
     Weights are quantized on the GPU from the seeded float32 draw, then
@@ -728,7 +796,21 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
     the 256 MB last-level cache (every launch streams its weights from HBM);
     activations are quantized with qmv_quantize_q8.  Each case is a graph of
     2 x copies launches replayed `replays` times between HIP events on the
-    launch stream.  GOP/s counts 2 M N K operations per launch."""
+    launch stream.  GOP/s counts 2 M N K operations per launch.
+
+    Each case is also timed warm: the same weight copy every launch (28 or
+    51 MB, resident in the 256 MB last-level cache after the first), which
+    takes HBM out of the way and shows the matrix-core and VALU side.  The
+    rooflines next to each figure:
+      * cold: min(int8 peak, 2 M ops per weight byte x HBM bandwidth), with
+        the vendor figures (hbm_cap_*) and with the measured ceilings
+        (measured_cold_cap_*: the best int8 matrix-core loop and the
+        per-launch streaming read of env.ceilings);
+      * warm: min(measured int8 loop, the fp32 epilogue) -- the kernel
+        spends 3 non-packed VALU operations (convert, scale product, fused
+        multiply-add) per output and block against the block's 64 int8
+        operations, and the VALU does 64 lanes x 256 compute units per
+        clock, so the epilogue caps the rate at 64 / 3 x 64 x 256 x clock."""
     import torch
 
     from block_quantized_decode_amd import qmv, synth
@@ -777,11 +859,29 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
                 # ceiling from HBM alone: 2 m operations per weight against its
                 # bytes (0.625 B for Q4_0, 1.125 B for Q8_0), at the vendor 8 TB/s
                 hbm_cap = min(MFMA_I8_PEAK_TOPS * 1e3, 2.0 * m * (mt.rows * mt.cols) / wbytes * HBM_PEAK_GBS)
-                cases.append({"qtype": f"q{qtype}_0", "matrix": mt.name, "shape": f"{mt.rows}x{mt.cols}", "m": m,
-                              "us_per_launch": round(us, 2), "gop_s": round(gops, 1),
-                              "pct_int8_peak": round(100.0 * gops / (MFMA_I8_PEAK_TOPS * 1e3), 2),
-                              "hbm_cap_pct_int8_peak": round(100.0 * hbm_cap / (MFMA_I8_PEAK_TOPS * 1e3), 1),
-                              "weight_gb_s": round(wbytes / (us * 1e-6) / 1e9, 1), "kernel": kernel})
+                case = {"qtype": f"q{qtype}_0", "matrix": mt.name, "shape": f"{mt.rows}x{mt.cols}", "m": m,
+                        "us_per_launch": round(us, 2), "gop_s": round(gops, 1),
+                        "pct_int8_peak": round(100.0 * gops / (MFMA_I8_PEAK_TOPS * 1e3), 2),
+                        "hbm_cap_pct_int8_peak": round(100.0 * hbm_cap / (MFMA_I8_PEAK_TOPS * 1e3), 1),
+                        "weight_gb_s": round(wbytes / (us * 1e-6) / 1e9, 1), "kernel": kernel}
+                # warm: one weight copy, resident in the last-level cache
+                wus = _graph_us([calls[0]] * (2 * len(calls)), stream, reps=replays) / (2 * len(calls))
+                wgops = 2.0 * m * mt.rows * mt.cols / (wus * 1e-6) / 1e9
+                case.update({"warm_us_per_launch": round(wus, 2), "warm_gop_s": round(wgops, 1),
+                             "warm_pct_int8_peak": round(100.0 * wgops / (MFMA_I8_PEAK_TOPS * 1e3), 2)})
+                clock = (sclk_mhz or 2400) * 1e6
+                epi_cap = 64.0 / 3.0 * 64 * 256 * clock / 1e9   # GOP/s
+                case["epilogue_cap_gop_s"] = round(epi_cap, 1)
+                if ceil is not None:
+                    mfma = ceil["mfma_i8_best_top_s"] * 1e3
+                    bw = ceil["stream_read"]["per_launch"]["gb_s"]
+                    cold_cap = min(mfma, 2.0 * m * (mt.rows * mt.cols) / wbytes * bw)
+                    warm_cap = min(mfma, epi_cap)
+                    case.update({"measured_cold_cap_gop_s": round(cold_cap, 1),
+                                 "pct_of_measured_cold_cap": round(100.0 * gops / cold_cap, 1),
+                                 "measured_warm_cap_gop_s": round(warm_cap, 1),
+                                 "warm_pct_of_measured_warm_cap": round(100.0 * wgops / warm_cap, 1)})
+                cases.append(case)
                 del graph, calls
                 pcalls = [qmv.prepare_gemm_packed(P, xq, xd, y, stream=stream.cuda_stream) for P in packed]
                 pus = _graph_us(pcalls + pcalls, stream, reps=replays) / (2 * len(pcalls))
@@ -804,10 +904,13 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5):
         "best_packed_gop_s": best_p["packed_gop_s"],
         "best_packed_case": f"{best_p['qtype']} {best_p['matrix']} {best_p['shape']} M={best_p['m']}",
         "packed_note": "packed_*: the same product on weights re-laid once by qmv_pack_weights (qmv_gemm_*_packed)",
-        "bound_note": "HBM-bound for M <= 64: 2M ops per weight element against 0.625 B (Q4_0) or 1.125 B (Q8_0) "
-                      "stays below the chip's 625 op/B ridge (hbm_cap_pct_int8_peak per case); the fp32 per-block "
-                      "epilogue (3 VALU per output per block against 64 int8 ops) caps any case at ~17% of the "
-                      "int8 peak",
+        "bound_note": "cold: HBM-bound for M <= 64: 2M ops per weight element against 0.625 B (Q4_0) or 1.125 B "
+                      "(Q8_0) stays below the chip's 625 op/B ridge (hbm_cap_pct_int8_peak per case; "
+                      "measured_cold_cap_gop_s with the measured stream and matrix-core ceilings); warm: the fp32 "
+                      "per-block epilogue (3 VALU per output per block against 64 int8 ops, epilogue_cap_gop_s) "
+                      "caps every case at ~17% of the int8 peak",
+        "best_warm_gop_s": max(c["warm_gop_s"] for c in cases),
+        "best_warm_pct_int8_peak": max(c["warm_pct_int8_peak"] for c in cases),
         "cases": cases,
     }
 

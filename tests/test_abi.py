@@ -9,7 +9,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmv.h")
-LIB = os.path.join(ROOT, "block_quantized_decode_amd", "libqmv.so")
+# QMV_ABI_LIB: another build of the same library (the sanitizer tier runs
+# these tests against a host-sanitized build)
+LIB = os.environ.get("QMV_ABI_LIB") or os.path.join(ROOT, "block_quantized_decode_amd", "libqmv.so")
 
 OK, E_SHAPE, E_FORMAT, E_ARG, E_ARCH, E_DEVICE = range(6)
 Q4, Q8 = 4, 8
