@@ -22,8 +22,9 @@ Q4_0 and Q8_0, M = 16 and 64), is measured the same way and reported under
 "batched".  The other configurations (256 x 512 Q8_0, a TinyLlama-1.1B
 layer with and without concatenated projections, the Qwen2.5-0.5B FFN and
 lm_head) are timed per call and per layer under "other_workloads", and the
-decode-step neighbours fused into the product's launch (rmsnorm ahead of
-the quantization, the FFN gate silu(g) * u) under "fusion".  "env" holds the per-launch floor of the smallest libqmv kernel
+decode-step neighbours (rmsnorm ahead of the quantization, the FFN gate
+silu(g) * u) unfused, fused into the product's launch and as the stacked
+gate|up form, under "fusion".  "env" holds the per-launch floor of the smallest libqmv kernel
 replayed the same way and the shader clock rocm-smi reports; the CPU
 baseline also gives the oracle's single-thread rate, the host CPU model
 and the oracle's compiler flags.
@@ -351,7 +352,7 @@ def ceilings_bench(stream, per_launch_bytes, step_bytes):
     sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
     sid = stream.cuda_stream
     per = None
-    for wgs in (256, 512, 1024):
+    for wgs in (128, 256, 512):
         for depth in (4, 8):
             calls = [qmv.Prepared("qmv_ceiling_stream_read", [sink.data_ptr(), b.data_ptr(), n16, wgs, depth], [b])
                      for b in bufs]
@@ -361,7 +362,7 @@ def ceilings_bench(stream, per_launch_bytes, step_bytes):
                        "depth": depth, "bytes": n16}
     one = None
     nb = big.numel() * 4
-    for wgs in (1024, 2048, 4096):
+    for wgs in (512, 1024, 2048, 4096):
         calls = [qmv.Prepared("qmv_ceiling_stream_read", [sink.data_ptr(), big.data_ptr(), nb, wgs, 8], [big])]
         us = _graph_us(calls * 4, stream, reps=5) / 4
         if one is None or us < one["us"]:
@@ -660,17 +661,22 @@ def q4k_bench(stream, groups=None):
 
 
 def fusion_bench(stream):
-    """The decode-step neighbours fused into the product's launch: rmsnorm
-    ahead of the quantization, and the FFN gate silu(g) * u.  Timed like
-    the step (graphs of prepared calls, weights rotated over copies beyond
-    the 256 MB cache):
-      * a TinyLlama-1.1B layer's matrix path in 4 launches -- rmsnorm + Q|K|V
-        (2560 x 2048), W_o, rmsnorm + gate|up (11264 x 2048), silu_mul + down
-        (g, u = the two halves of the gate|up output) -- against the same 4
-        launches with no rmsnorm or gate (the layer_concat figure of
-        other_workloads);
-      * one Llama-7B FFN launch of each form against the plain fused one:
-        W_up 11008 x 4096 with rmsnorm, W_down 4096 x 11008 with the gate."""
+    """The decode-step neighbours (rmsnorm ahead of a quantization, the FFN
+    gate silu(g) * u) with the product, timed like the step (graphs of
+    prepared calls, weights rotated over copies beyond the 256 MB cache),
+    in three forms:
+      * unfused: each neighbour a launch of its own (qmv_rmsnorm,
+        qmv_silu_mul) ahead of the plain fused product;
+      * fused: the neighbour inside the product's launch (_fx_rmsnorm,
+        _fx_silu_mul);
+      * swiglu: rmsnorm + stacked gate|up + gate in one launch
+        (_fx_swiglu), the down projection a plain fused product of the
+        gate's output;
+    against "plain": the same products with no neighbour at all (the
+    layer_concat figure of other_workloads).  For a TinyLlama-1.1B layer's
+    matrix path (Q|K|V 2560 x 2048, W_o, gate|up 11264 x 2048, down 2048 x
+    5632) and single Llama-7B FFN launches (W_up 11008 x 4096 with rmsnorm,
+    W_down 4096 x 11008 with the gate, stacked gate|up 22016 x 4096)."""
     import torch
 
     from block_quantized_decode_amd import qmv
@@ -688,58 +694,87 @@ def fusion_bench(stream):
     sid = stream.cuda_stream
     # TinyLlama layer
     copies = 20
-    x_attn = torch.randn(2048, device=dev)
-    x_o = torch.randn(2048, device=dev)
-    x_ffn = torch.randn(2048, device=dev)
-    n_attn = 1.0 + 0.1 * torch.randn(2048, device=dev)
-    n_ffn = 1.0 + 0.1 * torch.randn(2048, device=dev)
-    fused, plain = [], []
+    H, F = 2048, 5632
+    x_attn = torch.randn(H, device=dev)
+    x_o = torch.randn(H, device=dev)
+    x_ffn = torch.randn(H, device=dev)
+    n_attn = 1.0 + 0.1 * torch.randn(H, device=dev)
+    n_ffn = 1.0 + 0.1 * torch.randn(H, device=dev)
+    h_attn = torch.zeros(H, device=dev)
+    h_ffn = torch.zeros(H, device=dev)
+    a_ffn = torch.zeros(F, device=dev)
+    forms = {"plain": [], "unfused": [], "fused": [], "swiglu": []}
     keep = []
     for _ in range(copies):
-        qkv, wo, gu, dn = quantized(2560, 2048), quantized(2048, 2048), quantized(11264, 2048), quantized(2048, 5632)
+        qkv, wo, gu, dn = quantized(2560, H), quantized(H, H), quantized(2 * F, H), quantized(H, F)
         y_qkv = torch.zeros(2560, device=dev)
-        y_o = torch.zeros(2048, device=dev)
-        y_gu = torch.randn(11264, device=dev)
-        y_dn = torch.zeros(2048, device=dev)
-        fused += [qmv.prepare_matvec_fx_rmsnorm(4, *qkv, x_attn, n_attn, 1e-5, y_qkv, stream=sid),
-                  qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
-                  qmv.prepare_matvec_fx_rmsnorm(4, *gu, x_ffn, n_ffn, 1e-5, y_gu, stream=sid),
-                  qmv.prepare_matvec_fx_silu_mul(4, *dn, y_gu[:5632], y_gu[5632:], y_dn, stream=sid)]
-        plain += [qmv.prepare_matvec_fx(4, *qkv, x_attn, y_qkv, stream=sid),
-                  qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
-                  qmv.prepare_matvec_fx(4, *gu, x_ffn, y_gu, stream=sid),
-                  qmv.prepare_matvec_fx(4, *dn, y_gu[:5632], y_dn, stream=sid)]
+        y_o = torch.zeros(H, device=dev)
+        y_gu = torch.randn(2 * F, device=dev)
+        y_dn = torch.zeros(H, device=dev)
+        forms["plain"] += [qmv.prepare_matvec_fx(4, *qkv, x_attn, y_qkv, stream=sid),
+                           qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
+                           qmv.prepare_matvec_fx(4, *gu, x_ffn, y_gu, stream=sid),
+                           qmv.prepare_matvec_fx(4, *dn, y_gu[:F], y_dn, stream=sid)]
+        forms["unfused"] += [qmv.prepare_rmsnorm(x_attn, n_attn, 1e-5, h_attn, stream=sid),
+                             qmv.prepare_matvec_fx(4, *qkv, h_attn, y_qkv, stream=sid),
+                             qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
+                             qmv.prepare_rmsnorm(x_ffn, n_ffn, 1e-5, h_ffn, stream=sid),
+                             qmv.prepare_matvec_fx(4, *gu, h_ffn, y_gu, stream=sid),
+                             qmv.prepare_silu_mul(y_gu[:F], y_gu[F:], a_ffn, stream=sid),
+                             qmv.prepare_matvec_fx(4, *dn, a_ffn, y_dn, stream=sid)]
+        forms["fused"] += [qmv.prepare_matvec_fx_rmsnorm(4, *qkv, x_attn, n_attn, 1e-5, y_qkv, stream=sid),
+                           qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
+                           qmv.prepare_matvec_fx_rmsnorm(4, *gu, x_ffn, n_ffn, 1e-5, y_gu, stream=sid),
+                           qmv.prepare_matvec_fx_silu_mul(4, *dn, y_gu[:F], y_gu[F:], y_dn, stream=sid)]
+        forms["swiglu"] += [qmv.prepare_matvec_fx_rmsnorm(4, *qkv, x_attn, n_attn, 1e-5, y_qkv, stream=sid),
+                            qmv.prepare_matvec_fx(4, *wo, x_o, y_o, stream=sid),
+                            qmv.prepare_matvec_fx_swiglu(4, *gu, x_ffn, a_ffn, y_gu, w_norm=n_ffn, eps=1e-5,
+                                                         stream=sid),
+                            qmv.prepare_matvec_fx(4, *dn, a_ffn, y_dn, stream=sid)]
         keep.append((qkv, wo, gu, dn, y_qkv, y_o, y_gu, y_dn))
-    fused_us = _graph_us(fused, stream) / copies
-    plain_us = _graph_us(plain, stream) / copies
-    out["tinyllama_layer_q4"] = {"fused_us": round(fused_us, 3), "plain_us": round(plain_us, 3), "launches": 4,
-                                 "fused_steps": "rmsnorm+QKV, W_o, rmsnorm+gate|up, silu_mul+down", "copies": copies}
-    del keep, fused, plain
+    lay = {k: round(_graph_us(v, stream) / copies, 3) for k, v in forms.items()}
+    lay["launches"] = {"plain": 4, "unfused": 7, "fused": 4, "swiglu": 4}
+    lay["copies"] = copies
+    out["tinyllama_layer_q4_us"] = lay
+    del keep, forms
     torch.cuda.empty_cache()
     # Llama-7B FFN launches
     copies = 8
     res = {}
-    for name, rows, cols, form in (("W_up+rmsnorm", 11008, 4096, "rms"), ("W_down+silu_mul", 4096, 11008, "silu")):
+    for name, rows, cols, form in (("W_up+rmsnorm", 11008, 4096, "rms"), ("W_down+silu_mul", 4096, 11008, "silu"),
+                                   ("W_gate|W_up+rmsnorm+gate", 22016, 4096, "swiglu")):
         x = torch.randn(cols, device=dev)
-        x2 = torch.randn(cols, device=dev)
-        f_calls, p_calls, keep = [], [], []
+        x2 = 1.0 + 0.1 * torch.randn(cols, device=dev)
+        hbuf = torch.zeros(cols, device=dev)
+        abuf = torch.zeros(rows // 2, device=dev)
+        calls = {"plain": [], "unfused": [], "fused": []}
+        keep = []
         for _ in range(copies):
             q, d = quantized(rows, cols)
             y = torch.zeros(rows, device=dev)
+            calls["plain"].append(qmv.prepare_matvec_fx(4, q, d, x, y, stream=sid))
             if form == "rms":
-                f_calls.append(qmv.prepare_matvec_fx_rmsnorm(4, q, d, x, x2, 1e-5, y, stream=sid))
+                calls["unfused"] += [qmv.prepare_rmsnorm(x, x2, 1e-5, hbuf, stream=sid),
+                                     qmv.prepare_matvec_fx(4, q, d, hbuf, y, stream=sid)]
+                calls["fused"].append(qmv.prepare_matvec_fx_rmsnorm(4, q, d, x, x2, 1e-5, y, stream=sid))
+            elif form == "silu":
+                calls["unfused"] += [qmv.prepare_silu_mul(x, x2, hbuf, stream=sid),
+                                     qmv.prepare_matvec_fx(4, q, d, hbuf, y, stream=sid)]
+                calls["fused"].append(qmv.prepare_matvec_fx_silu_mul(4, q, d, x, x2, y, stream=sid))
             else:
-                f_calls.append(qmv.prepare_matvec_fx_silu_mul(4, q, d, x, x2, y, stream=sid))
-            p_calls.append(qmv.prepare_matvec_fx(4, q, d, x, y, stream=sid))
+                F7 = rows // 2
+                calls["unfused"] += [qmv.prepare_rmsnorm(x, x2, 1e-5, hbuf, stream=sid),
+                                     qmv.prepare_matvec_fx(4, q, d, hbuf, y, stream=sid),
+                                     qmv.prepare_silu_mul(y[:F7], y[F7:], abuf, stream=sid)]
+                calls["fused"].append(qmv.prepare_matvec_fx_swiglu(4, q, d, x, abuf, y, w_norm=x2, eps=1e-5,
+                                                                   stream=sid))
             keep.append((q, d, y))
-        res[name] = {"fused_us": round(_graph_us(f_calls, stream) / copies, 3),
-                     "plain_us": round(_graph_us(p_calls, stream) / copies, 3)}
-        del keep, f_calls, p_calls
+        res[name] = {k: round(_graph_us(v, stream) / copies, 3) for k, v in calls.items()}
+        del keep, calls
         torch.cuda.empty_cache()
-    out["llama7b_ffn_q4"] = res
+    out["llama7b_ffn_q4_us"] = res
     out["launch_floor_us"] = launch_floor(stream)
     return out
-
 
 def small_batch_bench(wl, qtype, mats, stream, steps, warmup):
     """The workload's stack at M = 4 activation rows: weight bytes per step

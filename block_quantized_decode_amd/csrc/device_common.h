@@ -147,6 +147,78 @@ __device__ __forceinline__ int quant_q4_group8(float4 v, float &d) {
     return pack4(n0, n1, n2, n3);
 }
 
+// Activation forms of the products: Q8_0 rows as given, a float32 row
+// quantized in the kernel, a float32 row normalized (rmsnorm) and then
+// quantized, or the FFN gate silu(g) * u of two float32 rows, then quantized.
+enum { kActQ8 = 0, kActF32 = 1, kActRms = 2, kActSilu = 3 };
+
+// ---- the decode-step neighbours of the product (Legacy-ISA ML Inference
+// Runtime -- Design Spec, section 5 kernel list: ml_k_rmsnorm,
+// ml_k_silu_mul; section 6 forward pass), shared by the fused activation
+// forms and the standalone kernels so that both give the same bits.
+
+// The rmsnorm scale 1 / sqrt(ss / n + eps), each operation rounded on its
+// own (contraction off; the division and the square root are the correctly
+// rounded ones).
+__device__ __forceinline__ float rms_inv(float ss, int n, float eps) {
+#pragma clang fp contract(off)
+    const float mean = ss / (float)n;
+    return 1.0f / sqrtf(mean + eps);
+}
+
+// w * (inv * x), two roundings.
+__device__ __forceinline__ float rms_apply(float x, float w, float inv) {
+#pragma clang fp contract(off)
+    const float t = inv * x;
+    return w * t;
+}
+
+// exp(-g) to a few ulp (the spec bounds silu's exp at 1e-6 relative) in six
+// instructions: 2^t with t = -g log2(e).  The product is rounded (t_hi) and
+// its rounding error recovered exactly by an FMA, the low part of log2(e)
+// added to that residual r, and 2^t = 2^t_hi (v_exp_f32, 1 ulp) * (1 + r ln 2)
+// with |r| < 2^-17, so the neglected (r ln 2)^2 / 2 stays below 1e-11.
+// t >= 128 overflows to +inf as exp does.
+__device__ __forceinline__ float exp_neg(float g) {
+    const float x = -g;
+    const float t = x * 1.44269502f;                     // log2(e), rounded
+    float r = __builtin_fmaf(x, 1.44269502f, -t);        // x log2e_hi - t, exact
+    r = __builtin_fmaf(x, 1.92596303e-8f, r);            // + x (log2(e) - log2e_hi)
+    const float e = __builtin_amdgcn_exp2f(t);
+    return t < 128.0f ? __builtin_fmaf(e, r * 0.693147182f, e) : e;
+}
+
+// silu(g) * u as g * (1 / (1 + exp(-g))) * u: the exp above and the
+// hardware reciprocal (1 ulp), well within the spec's 1e-6; each other
+// operation rounded on its own.
+__device__ __forceinline__ float silu_mul1(float g, float u) {
+#pragma clang fp contract(off)
+    const float s = __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
+    const float v = g * s;
+    return v * u;
+}
+
+// Pairwise (recursive-halving) sum of the squares of 8 consecutive values.
+__device__ __forceinline__ float sumsq8(float4 a, float4 b) {
+#pragma clang fp contract(off)
+    const float s0 = a.x * a.x, s1 = a.y * a.y, s2 = a.z * a.z, s3 = a.w * a.w;
+    const float s4 = b.x * b.x, s5 = b.y * b.y, s6 = b.z * b.z, s7 = b.w * b.w;
+    return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
+}
+
+// The sum of a 32-element block's squares from its four 8-element pairwise
+// sums (consecutive elements), pairwise.
+__device__ __forceinline__ float block_sumsq(const float (&q)[4]) {
+#pragma clang fp contract(off)
+    return (q[0] + q[1]) + (q[2] + q[3]);
+}
+
+// a + b rounded once (never fused with a neighbouring product).
+__device__ __forceinline__ float pair_add(float a, float b) {
+#pragma clang fp contract(off)
+    return a + b;
+}
+
 // v_dot4_i32_i8: c + sum of the four signed byte products of a and b.
 __device__ __forceinline__ int dot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);

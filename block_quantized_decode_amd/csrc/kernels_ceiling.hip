@@ -10,38 +10,40 @@
 namespace qmv {
 namespace {
 
-// XOR of every 32-bit word of buf[0, n16 * 16): each lane keeps D 16-byte
-// non-temporal loads in flight per round; the grid strides over the buffer.
-// One word per workgroup goes to sink (the XOR of its share), so the loads
-// cannot be dropped and the result can be checked.
+// XOR of every 32-bit word of buf[0, n16 * 16).  The grid reads the buffer
+// in rounds of D x (threads) 16-byte pieces: in a round thread t loads
+// pieces base + d * threads + t for d < D (each load instruction of a
+// wavefront covers 1 KiB contiguously), all D issued before any is used, so
+// a buffer of up to D x threads pieces is requested at once.  One word per
+// workgroup goes to sink (the XOR of its share), so the loads cannot be
+// dropped and the result can be checked.
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ void __launch_bounds__(1024) k_stream_read(uint32_t *__restrict__ sink, const u4 *__restrict__ buf,
                                                       int64_t n16) {
     __shared__ uint32_t s_x[16];
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t T = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + (D - 1) * stride < n16; i += D * stride) {
+    for (int64_t base = 0; base < n16; base += D * T) {
         u4 v[D];
 #pragma unroll
-        for (int d = 0; d < D; ++d) v[d] = __builtin_nontemporal_load(buf + i + d * stride);
+        for (int d = 0; d < D; ++d) {
+            const int64_t i = base + d * T + t;
+            v[d] = i < n16 ? __builtin_nontemporal_load(buf + i) : (u4){0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int d = 0; d < D; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
-    }
-    for (; i < n16; i += stride) {
-        const u4 v = __builtin_nontemporal_load(buf + i);
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
     if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t t = 0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t ^= s_x[w];
-        sink[blockIdx.x] = t;
+        uint32_t x = 0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) x ^= s_x[w];
+        sink[blockIdx.x] = x;
     }
 }
 

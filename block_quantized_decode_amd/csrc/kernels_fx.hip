@@ -118,67 +118,20 @@ __device__ __forceinline__ float group_sum(float a) {
 // 160 KiB of a compute unit.
 constexpr int rw_cap(int M) { return M <= 3 ? 1024 : 512; }
 
-// Activation forms of k_fx: Q8_0 rows as given, a float32 row quantized in
-// the kernel, a float32 row normalized (rmsnorm) and then quantized, or the
-// FFN gate silu(g) * u of two float32 rows, then quantized.
-enum { kActQ8 = 0, kActF32 = 1, kActRms = 2, kActSilu = 3 };
 
-// The rmsnorm scale 1 / sqrt(ss / n + eps), each operation rounded on its
-// own (contraction off; the division and the square root are the correctly
-// rounded ones).
-__device__ __forceinline__ float rms_inv(float ss, int n, float eps) {
-#pragma clang fp contract(off)
-    const float mean = ss / (float)n;
-    return 1.0f / sqrtf(mean + eps);
-}
-
-// w * (inv * x), two roundings.
-__device__ __forceinline__ float rms_apply(float x, float w, float inv) {
-#pragma clang fp contract(off)
-    const float t = inv * x;
-    return w * t;
-}
-
-// exp(-g) to a few ulp (the spec bounds silu's exp at 1e-6 relative) in six
-// instructions: 2^t with t = -g log2(e).  The product is rounded (t_hi) and
-// its rounding error recovered exactly by an FMA, the low part of log2(e)
-// added to that residual r, and 2^t = 2^t_hi (v_exp_f32, 1 ulp) * (1 + r ln 2)
-// with |r| < 2^-17, so the neglected (r ln 2)^2 / 2 stays below 1e-11.
-// t >= 128 overflows to +inf as exp does.
-__device__ __forceinline__ float exp_neg(float g) {
-    const float x = -g;
-    const float t = x * 1.44269502f;                     // log2(e), rounded
-    float r = __builtin_fmaf(x, 1.44269502f, -t);        // x log2e_hi - t, exact
-    r = __builtin_fmaf(x, 1.92596303e-8f, r);            // + x (log2(e) - log2e_hi)
-    const float e = __builtin_amdgcn_exp2f(t);
-    return t < 128.0f ? __builtin_fmaf(e, r * 0.693147182f, e) : e;
-}
-
-// silu(g) * u as g * (1 / (1 + exp(-g))) * u: the exp above and the
-// hardware reciprocal (1 ulp), well within the spec's 1e-6; each other
-// operation rounded on its own.
-__device__ __forceinline__ float silu_mul1(float g, float u) {
-#pragma clang fp contract(off)
-    const float s = __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
-    const float v = g * s;
-    return v * u;
-}
-
-// Pairwise (recursive-halving) sum of the squares of 8 consecutive values.
-__device__ __forceinline__ float sumsq8(float4 a, float4 b) {
-#pragma clang fp contract(off)
-    const float s0 = a.x * a.x, s1 = a.y * a.y, s2 = a.z * a.z, s3 = a.w * a.w;
-    const float s4 = b.x * b.x, s5 = b.y * b.y, s6 = b.z * b.z, s7 = b.w * b.w;
-    return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
-}
-
-template <int QT, int M, int AX, int T, int NBL, int D, int D0, int WPB, bool KS>
+template <int QT, int M, int AX, int T, int NBL, int D, int D0, int WPB, bool KS, bool GU = false>
 __global__ void __launch_bounds__(64 * WPB)
 k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
      const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xd,
      const float *__restrict__ xn, float eps, int8_t *__restrict__ xq_out, float *__restrict__ xd_out, int32_t r0,
-     int32_t r1, int32_t rw) {
+     int32_t r1, int32_t rw, float *__restrict__ ya) {
+    // GU: rows = 2 F, the first F rows the FFN gate and the last F the up
+    // projection; this workgroup takes pairs [g0, g1) -- gate rows g0 .. g1 - 1
+    // and up rows F + g0 .. F + g1 - 1, as passes 0 .. nph - 1 and nph .. 2 nph - 1
+    // -- and ends with ya[j] = silu(y[j]) * y[F + j] (the spec's silu_mul on
+    // the two halves of the product) besides y itself
     constexpr bool FX = AX != kActQ8;          // float32 activation, quantized here
+    static_assert(!GU || (KS && M == 1), "paired gate and up rows: split-K, one activation row");
     constexpr int PASS = 64 / T;               // rows per pass
     constexpr int QB = (QT == 8) ? 32 : 16;    // quant bytes per block
     static_assert(T * NBL <= 64 && (T * NBL) % 16 == 0, "a slice is at most 64 blocks, loaded 16 blocks at a time");
@@ -200,10 +153,13 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     const int S = KS ? (nb + WPB - 1) / WPB : nb;
     const int kb0 = KS ? min(wid * S, nb) : 0;
     const int ns = min(S, nb - kb0);           // blocks in this wavefront's slice
-    const int g0 = r0 + blockIdx.x * rw;       // this workgroup's rows g0 .. g1 - 1
+    const int g0 = r0 + blockIdx.x * rw;       // this workgroup's rows (GU: pairs) g0 .. g1 - 1
     const int g1 = min(r1, g0 + rw);
-    const int nrp = (g1 - g0 + PASS - 1) / PASS;  // passes of the workgroup
+    const int F = rows >> 1;                   // GU: gate rows
+    const int nph = (g1 - g0 + PASS - 1) / PASS;  // GU: passes per half
+    const int nrp = GU ? 2 * nph : nph;        // passes of the workgroup
     const int npass = KS ? nrp : (nrp + WPB - 1) / WPB;  // passes of this wavefront
+    const int rws = GU ? 2 * rw : rw;          // slice sums kept per wavefront
     const int pstride = KS ? 1 : WPB;          // pass j of this wavefront = workgroup pass j * pstride + pfirst
     const int pfirst = KS ? 0 : wid;
 
@@ -256,8 +212,14 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
 
     // 2. the first D - 1 passes of weights
     const int rows_here = g1 - g0;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq + (size_t)g0 * nb * QB, rows_here * nb * QB);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(wd + (size_t)g0 * nb, rows_here * nb * 4);
+    // GU: the descriptors span gate row g0 .. up row F + g1 - 1; passes of
+    // the up half skip the F - PASS * nph rows between the two ranges (rows of
+    // the gate half's last pass past g1 read other rows, whose sums are
+    // never stored)
+    const int span = GU ? F + rows_here : rows_here;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(wq + (size_t)g0 * nb * QB, span * nb * QB);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(wd + (size_t)g0 * nb, span * nb * 4);
+    const int skipq = GU ? (F - PASS * nph) * nb * QB : 0, skipd = GU ? (F - PASS * nph) * nb * 4 : 0;
     const int prow = lane / T;                 // row of a pass
     int oq[NBL], od[NBL];                      // pass-0 offsets of this lane's blocks
 #pragma unroll
@@ -269,10 +231,11 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     }
     const int pq = pstride * PASS * nb * QB, pd = pstride * PASS * nb * 4;  // bytes per pass of this wavefront
     auto load = [&](Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
+        const bool up = GU && j >= nph;
 #pragma unroll
         for (int k = 0; k < NBL; ++k) {
             // offsets of passes at or beyond npass fall outside the range
-            const int a = oq[k] + j * pq, b = od[k] + j * pd;
+            const int a = oq[k] + j * pq + (up ? skipq : 0), b = od[k] + j * pd + (up ? skipd : 0);
             p.w[k][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a, 0, kNT));
             if constexpr (QT == 8)
                 p.w[k][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a + 16, 0, kNT));
@@ -460,7 +423,7 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                 const float t = group_sum<T>(a[m]);
                 if constexpr (KS) {
                     const int r = j * PASS + prow;
-                    if (lane % T == T - 1 && j < npass && r < rw) s_red[(m * WPB + wid) * rw + r] = t;
+                    if (lane % T == T - 1 && j < npass && r < rws) s_red[(m * WPB + wid) * rws + r] = t;
                 } else {  // whole rows: store directly
                     const int r = (j * pstride + pfirst) * PASS + prow;
                     if (lane % T == T - 1 && j < npass && r < rows_here) y[(size_t)m * rows + g0 + r] = t;
@@ -472,12 +435,26 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     if constexpr (!KS) return;
     // 5. add the wavefronts' slice sums of each row in wavefront order
     __syncthreads();
+    if constexpr (GU) {
+        for (int v = threadIdx.x; v < rows_here; v += 64 * WPB) {
+            float sg = 0.0f, su = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPB; ++w) {
+                sg += s_red[w * rws + v];
+                su += s_red[w * rws + PASS * nph + v];
+            }
+            y[g0 + v] = sg;
+            y[F + g0 + v] = su;
+            ya[g0 + v] = silu_mul1(sg, su);
+        }
+        return;
+    }
     for (int r = threadIdx.x; r < rows_here; r += 64 * WPB) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float s = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WPB; ++w) s += s_red[(m * WPB + w) * rw + r];
+            for (int w = 0; w < WPB; ++w) s += s_red[(m * WPB + w) * rws + r];
             y[(size_t)m * rows + g0 + r] = s;
         }
     }
@@ -685,24 +662,24 @@ hipError_t launch_mq(const RowsArgs &a, hipStream_t s, const char **name) {
     return launch_mq_t<QT, 4, D, W>(a, s, name);
 }
 
-template <int QT, int M, int AX, int T, int NBL, int D, int WPB, bool KS = true>
+template <int QT, int M, int AX, int T, int NBL, int D, int WPB, bool KS = true, bool GU = false>
 hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name) {
     static const std::string kname =
-        AX != kActQ8 ? variant_name("fx%s_q%d_t%d_n%d_d%d_w%d%s", AX == kActRms ? "n" : (AX == kActSilu ? "s" : ""),
-                                    QT, T, NBL, D, WPB, KS ? "" : "_rows")
+        AX != kActQ8 ? variant_name("fx%s_q%d_t%d_n%d_d%d_w%d%s%s", AX == kActRms ? "n" : (AX == kActSilu ? "s" : ""),
+                                    QT, T, NBL, D, WPB, KS ? "" : "_rows", GU ? "_gu" : "")
                      : variant_name("px_q%d_m%d_t%d_n%d_d%d_w%d%s", QT, M, T, NBL, D, WPB, KS ? "" : "_rows");
     constexpr int D0W = AX == kActRms ? QMV_FX_D0_RMS : (AX == kActSilu ? QMV_FX_D0_SILU : QMV_FX_D0);
     constexpr int D0 = D0W < D - 1 ? D0W : D - 1;
-    auto kern = k_fx<QT, M, AX, T, NBL, D, D0, WPB, KS>;
+    auto kern = k_fx<QT, M, AX, T, NBL, D, D0, WPB, KS, GU>;
     const int nrows = a.r1 - a.r0;
     const int grid = (nrows + rw - 1) / rw;
-    const size_t lds = KS ? (size_t)M * WPB * rw * 4 : 0;
+    const size_t lds = KS ? (size_t)M * WPB * (GU ? 2 : 1) * rw * 4 : 0;
     if (KS) {  // the largest size any call of this kernel asks for (rw at its cap)
         hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), (size_t)M * WPB * rw_cap(M) * 4);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq, a.xd,
-                       AX == kActSilu ? a.xu : a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1, rw);
+                       AX == kActSilu ? a.xu : a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1, rw, a.ya);
     *name = kname.c_str();
     return hipGetLastError();
 }
@@ -729,6 +706,17 @@ hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
         const int want = ((nrows + groups - 1) / groups + pass - 1) / pass * pass;
         return ks ? min(rw_cap(M), want) : want;
     };
+    if (a.ya != nullptr) {  // paired gate and up rows: split K only, pairs per workgroup at most rw_cap / 2
+        if constexpr (FX && M == 1) {
+            const int want = ((nrows + groups - 1) / groups + 3) / 4 * 4;
+            const int rwp = min(rw_cap(M) / 2, want);
+            if (nb >= 64 && S <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W, true, true>(a, rwp, s, name);
+            if (nb >= 64 && S <= 32) return launch_t<QT, M, AX, 16, 2, ring_depth<QT, M, 2>(), W, true, true>(a, rwp, s, name);
+            if (nb >= 64 && S <= 48) return launch_t<QT, M, AX, 16, 3, ring_depth<QT, M, 3>(), W, true, true>(a, rwp, s, name);
+            if (nb >= 64 && S <= 64) return launch_t<QT, M, AX, 16, 4, ring_depth<QT, M, 4>(), W, true, true>(a, rwp, s, name);
+        }
+        return hipErrorNotSupported;
+    }
     if (nb <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(4 * W, false), s, name);
     if (nb <= 32) return launch_t<QT, M, AX, 32, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(2 * W, false), s, name);
     // split K: the fused matvec, and pre-quantized Q8_0 weights with 2 .. 4
@@ -774,6 +762,7 @@ hipError_t launch_fx(const RowsArgs &a, hipStream_t s, const char **name) {
     const int nb = a.K / QK;
     if ((a.x != nullptr && a.M != 1) || a.M < 1 || a.M > 4 || (nb > 32 && nb < 64) || nb > 64 * QMV_FX_WPB)
         return hipErrorNotSupported;
+    if (a.ya != nullptr && (a.x == nullptr || a.xu != nullptr)) return hipErrorNotSupported;
     return a.qtype == 4 ? launch_q<4>(a, s, name) : launch_q<8>(a, s, name);
 }
 

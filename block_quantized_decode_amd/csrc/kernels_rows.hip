@@ -139,16 +139,19 @@ constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2);
 //                    whole 1 KiB chunks
 // (the pre-quantized arrays are rounded up to whole 64-block chunks, the
 // granularity of their direct loads).
-__host__ __device__ constexpr size_t lds_bytes(int M, int K, bool fx) {
-    return (size_t)((M * (K / 32) + 63) / 64 * 64) * 40 + (fx ? ((size_t)M * K * 4 + 1023) / 1024 * 1024 : 0);
+__host__ __device__ constexpr size_t lds_bytes(int M, int K, bool fx, bool rms = false) {
+    return (size_t)((M * (K / 32) + 63) / 64 * 64) * 40 + (fx ? ((size_t)M * K * 4 + 1023) / 1024 * 1024 : 0) +
+           (rms ? (size_t)next_pow2(K / 32) * 4 : 0);
 }
 
-template <int QT, int M, bool FX, int J, int R, int WPB>
+template <int QT, int M, int AX, int J, int R, int WPB>
 __global__ void __launch_bounds__(64 * WPB)
 k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restrict__ wd,
        int32_t rows, int32_t K, const float *__restrict__ x, const int8_t *__restrict__ xq,
-       const float *__restrict__ xd, int8_t *__restrict__ xq_out, float *__restrict__ xd_out,
-       int32_t r0, int32_t r1) {
+       const float *__restrict__ xd, const float *__restrict__ xn, float eps, int8_t *__restrict__ xq_out,
+       float *__restrict__ xd_out, int32_t r0, int32_t r1) {
+    constexpr bool FX = AX != kActQ8;
+    static_assert(AX <= kActF32 || M == 1, "the neighbour forms take one float32 activation row");
     constexpr int NV = next_pow2(R * M);
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = K >> 5;
@@ -159,6 +162,8 @@ k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__rest
     float *xdx = reinterpret_cast<float *>(xhi + nblk64);
     int *xsx = reinterpret_cast<int *>(xdx + nblk64);
     float *raw = reinterpret_cast<float *>(xsx + nblk64);
+    // rmsnorm: the block sums of squares, padded to a power of two, after raw
+    float *bs = raw + (M * K + 255) / 256 * 256;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -195,6 +200,33 @@ k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__rest
     // 3. once the activation has landed, quantize / sum it in LDS
     __syncthreads();
     if constexpr (FX) {
+        float inv = 0.0f;
+        if constexpr (AX == kActRms) {
+            // rmsnorm: each block's squares summed pairwise (8-element sums,
+            // then pairs of those), then the block sums pairwise over their
+            // count padded to a power of two (an in-LDS tree adding
+            // neighbours at every level) -- the order of the fused split-K
+            // form and of the standalone kernel, hence the same bits
+            int P = 1;
+            while (P < nb) P *= 2;
+            for (int b = tid; b < P; b += 64 * WPB) {
+                float s = 0.0f;
+                if (b < nb) {
+                    const float4 *src = reinterpret_cast<const float4 *>(raw + 32 * b);
+                    float q[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) q[k] = sumsq8(src[2 * k], src[2 * k + 1]);
+                    s = block_sumsq(q);
+                }
+                bs[b] = s;
+            }
+            for (int h = 1; h < P; h *= 2) {
+                __syncthreads();
+                for (int i = tid; i < P / (2 * h); i += 64 * WPB) bs[2 * h * i] = pair_add(bs[2 * h * i], bs[2 * h * i + h]);
+            }
+            __syncthreads();
+            inv = rms_inv(bs[0], K, eps);
+        }
         // one lane per 32-element block: the two divisions once per block,
         // no cross-lane steps.  Lane b reads its block's eight 16-byte
         // chunks in the rotated order (k + b) mod 8, which keeps the 64
@@ -207,6 +239,20 @@ k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__rest
             float4 v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = src[(k + rot) & 7];
+            if constexpr (AX == kActRms || AX == kActSilu) {
+                // the norm weights (rmsnorm) or u (gate) of the same elements
+                const float4 *nsrc = reinterpret_cast<const float4 *>(xn + 32 * (size_t)blk);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 nv = nsrc[(k + rot) & 7];
+                    if constexpr (AX == kActRms)
+                        v[k] = make_float4(rms_apply(v[k].x, nv.x, inv), rms_apply(v[k].y, nv.y, inv),
+                                           rms_apply(v[k].z, nv.z, inv), rms_apply(v[k].w, nv.w, inv));
+                    else
+                        v[k] = make_float4(silu_mul1(v[k].x, nv.x), silu_mul1(v[k].y, nv.y), silu_mul1(v[k].z, nv.z),
+                                           silu_mul1(v[k].w, nv.w));
+                }
+            }
             float amax = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k)
@@ -280,17 +326,19 @@ k_rows(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__rest
     if (reduce_owner<NV>(lane) && m < M && row < r1) y[(size_t)m * rows + row] = tot;
 }
 
-template <int QT, int M, bool FX, int J, int R, int WPB>
+template <int QT, int M, int AX, int J, int R, int WPB>
 hipError_t launch_rows_t(const RowsArgs &a, hipStream_t s, const char **name) {
-    static const std::string kname = variant_name("rows_q%d_m%d%s_j%d_r%d_w%d", QT, M, FX ? "_fx" : "", J, R, WPB);
-    auto kern = k_rows<QT, M, FX, J, R, WPB>;
-    const size_t lds = lds_bytes(M, a.K, FX);
+    static const std::string kname =
+        variant_name("rows_q%d_m%d%s_j%d_r%d_w%d", QT, M,
+                     AX == kActQ8 ? "" : AX == kActF32 ? "_fx" : AX == kActRms ? "_fxn" : "_fxs", J, R, WPB);
+    auto kern = k_rows<QT, M, AX, J, R, WPB>;
+    const size_t lds = lds_bytes(M, a.K, AX != kActQ8, AX == kActRms);
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     const int nunits = (a.r1 - a.r0 + R - 1) / R;
     const int grid = (nunits + WPB - 1) / WPB;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.x, a.xq,
-                       a.xd, a.xq_out, a.xd_out, a.r0, a.r1);
+                       a.xd, AX == kActSilu ? a.xu : a.xn, a.eps, a.xq_out, a.xd_out, a.r0, a.r1);
     *name = kname.c_str();
     return hipGetLastError();
 }
@@ -311,50 +359,54 @@ constexpr int jmax() {
 // spreads over 8 - 16 wavefronts per CU and each workgroup's activation
 // quantization is shared by that many wavefronts.  Several activation rows
 // always use R = 4.
-template <int QT, int M, bool FX, int J>
+template <int QT, int M, int AX, int J>
 hipError_t launch_rows_r(const RowsArgs &a, hipStream_t s, const char **name) {
     constexpr int JJ = J < jmax<QT, M>() ? J : jmax<QT, M>();
     if constexpr (M > 1) {
-        return launch_rows_t<QT, M, FX, JJ, 4, 4>(a, s, name);
+        return launch_rows_t<QT, M, AX, JJ, 4, 4>(a, s, name);
     } else {
         const int nrows = a.r1 - a.r0;
         const int per_cu = 8 * a.num_cu;
-        if (nrows / 4 >= per_cu) return launch_rows_t<QT, M, FX, JJ, 4, 4>(a, s, name);
-        if (nrows / 2 >= per_cu) return launch_rows_t<QT, M, FX, JJ, 2, 8>(a, s, name);
-        return launch_rows_t<QT, M, FX, JJ, 1, 16>(a, s, name);
+        if (nrows / 4 >= per_cu) return launch_rows_t<QT, M, AX, JJ, 4, 4>(a, s, name);
+        if (nrows / 2 >= per_cu) return launch_rows_t<QT, M, AX, JJ, 2, 8>(a, s, name);
+        return launch_rows_t<QT, M, AX, JJ, 1, 16>(a, s, name);
     }
 }
 
-template <int QT, int M, bool FX>
+template <int QT, int M, int AX>
 hipError_t launch_rows_j(const RowsArgs &a, hipStream_t s, const char **name) {
     const int nj = (a.K / QK + 63) / 64;
-    if (nj <= 1) return launch_rows_r<QT, M, FX, 1>(a, s, name);
-    if (nj <= 2) return launch_rows_r<QT, M, FX, 2>(a, s, name);
-    if (nj <= 3) return launch_rows_r<QT, M, FX, 3>(a, s, name);
-    if (nj <= 4) return launch_rows_r<QT, M, FX, 4>(a, s, name);
-    if (nj <= 6) return launch_rows_r<QT, M, FX, 6>(a, s, name);
-    return launch_rows_r<QT, M, FX, 8>(a, s, name);
+    if (nj <= 1) return launch_rows_r<QT, M, AX, 1>(a, s, name);
+    if (nj <= 2) return launch_rows_r<QT, M, AX, 2>(a, s, name);
+    if (nj <= 3) return launch_rows_r<QT, M, AX, 3>(a, s, name);
+    if (nj <= 4) return launch_rows_r<QT, M, AX, 4>(a, s, name);
+    if (nj <= 6) return launch_rows_r<QT, M, AX, 6>(a, s, name);
+    return launch_rows_r<QT, M, AX, 8>(a, s, name);
 }
 
 template <int QT>
 hipError_t launch_rows_q(const RowsArgs &a, hipStream_t s, const char **name) {
-    if (a.x != nullptr) return launch_rows_j<QT, 1, true>(a, s, name);
+    if (a.x != nullptr) {
+        if (a.xu != nullptr) return launch_rows_j<QT, 1, kActSilu>(a, s, name);
+        if (a.xn != nullptr) return launch_rows_j<QT, 1, kActRms>(a, s, name);
+        return launch_rows_j<QT, 1, kActF32>(a, s, name);
+    }
     switch (a.M) {
-        case 1: return launch_rows_j<QT, 1, false>(a, s, name);
-        case 2: return launch_rows_j<QT, 2, false>(a, s, name);
-        case 3: return launch_rows_j<QT, 3, false>(a, s, name);
-        case 4: return launch_rows_j<QT, 4, false>(a, s, name);
-        case 5: return launch_rows_j<QT, 5, false>(a, s, name);
-        case 6: return launch_rows_j<QT, 6, false>(a, s, name);
-        case 7: return launch_rows_j<QT, 7, false>(a, s, name);
-        case 8: return launch_rows_j<QT, 8, false>(a, s, name);
+        case 1: return launch_rows_j<QT, 1, kActQ8>(a, s, name);
+        case 2: return launch_rows_j<QT, 2, kActQ8>(a, s, name);
+        case 3: return launch_rows_j<QT, 3, kActQ8>(a, s, name);
+        case 4: return launch_rows_j<QT, 4, kActQ8>(a, s, name);
+        case 5: return launch_rows_j<QT, 5, kActQ8>(a, s, name);
+        case 6: return launch_rows_j<QT, 6, kActQ8>(a, s, name);
+        case 7: return launch_rows_j<QT, 7, kActQ8>(a, s, name);
+        case 8: return launch_rows_j<QT, 8, kActQ8>(a, s, name);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-size_t rows_lds_bytes(int M, int K, bool fx) { return lds_bytes(M, K, fx); }
+size_t rows_lds_bytes(int M, int K, bool fx, bool rms) { return lds_bytes(M, K, fx, rms); }
 
 hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name) {
     return a.qtype == 4 ? launch_rows_q<4>(a, s, name) : launch_rows_q<8>(a, s, name);

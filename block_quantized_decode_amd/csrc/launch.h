@@ -46,8 +46,9 @@ struct RowsArgs {
     const float *xu;           // FFN gate: the activation is silu(x) * xu, or null
     int8_t *xq_out;            // optional copy of the fused quantization
     float *xd_out;
-    int32_t r0, r1;
+    int32_t r0, r1;            // (ya: pairs [r0, r1) of gate row r and up row rows / 2 + r)
     int num_cu;                // compute units of the device (sizes the grid)
+    float *ya;                 // paired gate and up rows: ya[r] = silu(y[r]) * y[rows / 2 + r], or null
 };
 
 hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name);
@@ -56,8 +57,9 @@ hipError_t launch_rows(const RowsArgs &a, hipStream_t s, const char **name);
 // hipErrorNotSupported (nothing launched) for shapes it does not cover.
 hipError_t launch_fx(const RowsArgs &a, hipStream_t s, const char **name);
 // LDS bytes the row-streaming kernel needs for M activation rows of K
-// (fused: the float32 activation is staged too).
-size_t rows_lds_bytes(int M, int K, bool fused);
+// (fused: the float32 activation is staged too; rms: plus the rmsnorm
+// block sums).
+size_t rows_lds_bytes(int M, int K, bool fused, bool rms = false);
 
 // Arguments of the matrix-core product for up to 64 activation rows per launch.
 struct GemmArgs {
@@ -127,6 +129,12 @@ hipError_t launch_quant_q8(int8_t *q, float *d, const float *x, int64_t nblk, hi
 // Q4_0 quantization of nblk blocks of 32 floats (weights).
 hipError_t launch_quant_q4(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s,
                            const char **name);
+
+// The neighbours as launches of their own (kernels_neighbour.hip): rmsnorm
+// of n floats (one workgroup; n % 32 == 0, n <= 131072) and silu(g) * u.
+hipError_t launch_rmsnorm(float *o, const float *x, const float *w, int32_t n, float eps, hipStream_t s,
+                          const char **name);
+hipError_t launch_silu_mul(float *o, const float *g, const float *u, int64_t n, hipStream_t s, const char **name);
 
 // Measurement kernels (kernels_ceiling.hip): a plain streaming read of
 // `bytes` (multiple of 16) with `depth` (4 or 8) 16-byte loads in flight per

@@ -102,12 +102,13 @@ qmv_status check_weight_align(const qmv_qtensor *W) {
 
 qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, const float *x,
                        const int8_t *xq, const float *xd, qmv_qact *xq_out, int32_t r0, int32_t r1,
-                       void *stream, const float *xn = nullptr, float eps = 0.0f, const float *xu = nullptr) {
+                       void *stream, const float *xn = nullptr, float eps = 0.0f, const float *xu = nullptr,
+                       float *ya = nullptr) {
     qmv_status st = check_weight(W, qtype);
     if (st != QMV_OK) return st;
     if (y == nullptr && W->rows != 0) return QMV_E_ARG;
     if ((st = check_range(W, r0, r1)) != QMV_OK) return st;
-    if (W->cols > 131072 || qmv::rows_lds_bytes(M, W->cols, x != nullptr) > (size_t)QMV_LDS_BYTES)
+    if (W->cols > 131072 || qmv::rows_lds_bytes(M, W->cols, x != nullptr, xn != nullptr) > (size_t)QMV_LDS_BYTES)
         return QMV_E_SHAPE;
     if ((st = check_weight_align(W)) != QMV_OK) return st;
     if (!aligned(y, 4)) return QMV_E_ARG;
@@ -137,10 +138,33 @@ qmv_status rows_common(int qtype, float *y, const qmv_qtensor *W, int32_t M, con
     a.r0 = r0;
     a.r1 = r1;
     a.num_cu = num_cu(dev);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const char *name = "";
-    hipError_t e = qmv::launch_fx(a, static_cast<hipStream_t>(stream), &name);
-    if (e == hipErrorNotSupported && xn == nullptr && xu == nullptr)
-        e = qmv::launch_rows(a, static_cast<hipStream_t>(stream), &name);
+    hipError_t e = hipErrorNotSupported;
+    if (ya != nullptr) {  // paired gate and up rows [r0, r1) and F + [r0, r1)
+        a.ya = ya;
+        e = qmv::launch_fx(a, s, &name);
+        if (e != hipErrorNotSupported) return finish(e, name, (r1 - r0 + 3) / 4);
+        // no split-K form for this K: the two halves as products of their
+        // own, then the gate from the stored outputs (same bits)
+        const int32_t F = W->rows / 2;
+        a.ya = nullptr;
+        e = qmv::launch_fx(a, s, &name);
+        if (e == hipErrorNotSupported) e = qmv::launch_rows(a, s, &name);
+        if (e != hipSuccess) return finish(e, name, 0);
+        a.xq_out = nullptr;
+        a.xd_out = nullptr;
+        a.r0 = F + r0;
+        a.r1 = F + r1;
+        e = qmv::launch_fx(a, s, &name);
+        if (e == hipErrorNotSupported) e = qmv::launch_rows(a, s, &name);
+        if (e != hipSuccess) return finish(e, name, 0);
+        const char *gname = "";
+        e = qmv::launch_silu_mul(ya + r0, y + r0, y + F + r0, r1 - r0, s, &gname);
+        return finish(e, name, (r1 - r0 + 15) / 16);
+    }
+    e = qmv::launch_fx(a, s, &name);
+    if (e == hipErrorNotSupported) e = qmv::launch_rows(a, s, &name);
     return finish(e, name, (r1 - r0 + 15) / 16);
 }
 
@@ -165,10 +189,6 @@ qmv_status matvec_fx_rmsnorm(int qtype, float *y, const qmv_qtensor *W, const fl
     if (x == nullptr || w_norm == nullptr) return QMV_E_ARG;
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return QMV_E_ARG;
     if (xq != nullptr && (xq->q == nullptr || xq->d == nullptr)) return QMV_E_ARG;
-    qmv_status st = check_weight(W, qtype);
-    if (st != QMV_OK) return st;
-    const int32_t nb = W->cols / QMV_QK;
-    if ((nb > 32 && nb < 64) || nb > 512) return QMV_E_SHAPE;  // the split-K kernel's range
     if (!aligned(w_norm, 16)) return QMV_E_ARG;
     return rows_common(qtype, y, W, 1, x, nullptr, nullptr, xq, r0, r1, stream, w_norm, eps);
 }
@@ -177,12 +197,23 @@ qmv_status matvec_fx_silu_mul(int qtype, float *y, const qmv_qtensor *W, const f
                               qmv_qact *xq, int32_t r0, int32_t r1, void *stream) {
     if (g == nullptr || u == nullptr) return QMV_E_ARG;
     if (xq != nullptr && (xq->q == nullptr || xq->d == nullptr)) return QMV_E_ARG;
-    qmv_status st = check_weight(W, qtype);
-    if (st != QMV_OK) return st;
-    const int32_t nb = W->cols / QMV_QK;
-    if ((nb > 32 && nb < 64) || nb > 512) return QMV_E_SHAPE;  // the split-K kernel's range
     if (!aligned(u, 16)) return QMV_E_ARG;
     return rows_common(qtype, y, W, 1, g, nullptr, nullptr, xq, r0, r1, stream, nullptr, 0.0f, u);
+}
+
+qmv_status matvec_fx_swiglu(int qtype, float *ya, float *y, const qmv_qtensor *W, const float *x,
+                            const float *w_norm, float eps, qmv_qact *xq, int32_t p0, int32_t p1, void *stream) {
+    if (x == nullptr) return QMV_E_ARG;
+    if (w_norm != nullptr && (!(eps >= 0.0f) || !std::isfinite(eps) || !aligned(w_norm, 16))) return QMV_E_ARG;
+    if (xq != nullptr && (xq->q == nullptr || xq->d == nullptr)) return QMV_E_ARG;
+    qmv_status st = check_weight(W, qtype);
+    if (st != QMV_OK) return st;
+    if ((W->rows % 2) != 0) return QMV_E_SHAPE;
+    if (p0 < 0 || p1 > W->rows / 2 || p0 > p1) return QMV_E_SHAPE;
+    if (W->rows != 0 && (ya == nullptr || y == nullptr)) return QMV_E_ARG;
+    if (!aligned(ya, 4)) return QMV_E_ARG;
+    if (W->rows == 0) return rows_common(qtype, y, W, 1, x, nullptr, nullptr, xq, 0, 0, stream, w_norm, eps);
+    return rows_common(qtype, y, W, 1, x, nullptr, nullptr, xq, p0, p1, stream, w_norm, eps, nullptr, ya);
 }
 
 qmv_status gemm_passes(int qtype, float *Y, const int8_t *wq, const float *wd, const void *pq, const float *pd,
@@ -432,6 +463,16 @@ qmv_status qmv_matvec_q4_fx_silu_mul(float *y, const qmv_qtensor *W, const float
     return matvec_fx_silu_mul(QMV_Q4_0, y, W, g, u, xq, r0, r1, stream);
 }
 
+qmv_status qmv_matvec_q8_fx_swiglu(float *a, float *y, const qmv_qtensor *W, const float *x, const float *w_norm,
+                                   float eps, qmv_qact *xq, int32_t p0, int32_t p1, void *stream) {
+    return matvec_fx_swiglu(QMV_Q8_0, a, y, W, x, w_norm, eps, xq, p0, p1, stream);
+}
+
+qmv_status qmv_matvec_q4_fx_swiglu(float *a, float *y, const qmv_qtensor *W, const float *x, const float *w_norm,
+                                   float eps, qmv_qact *xq, int32_t p0, int32_t p1, void *stream) {
+    return matvec_fx_swiglu(QMV_Q4_0, a, y, W, x, w_norm, eps, xq, p0, p1, stream);
+}
+
 qmv_status qmv_gemm_q8(float *Y, const qmv_qtensor *W, const qmv_qtensor *X, int32_t r0, int32_t r1,
                        void *stream) {
     return gemm(QMV_Q8_0, Y, W, X, r0, r1, stream);
@@ -524,6 +565,30 @@ qmv_status qmv_gemm_q8_packed(float *Y, const qmv_packed *P, const qmv_qtensor *
 qmv_status qmv_gemm_q4_packed(float *Y, const qmv_packed *P, const qmv_qtensor *X, int32_t r0, int32_t r1,
                               void *stream) {
     return gemm_packed(QMV_Q4_0, Y, P, X, r0, r1, stream);
+}
+
+qmv_status qmv_rmsnorm(float *o, const float *x, const float *w, int64_t n, float eps, void *stream) {
+    if (o == nullptr || x == nullptr || w == nullptr) return QMV_E_ARG;
+    if (n <= 0 || (n % QMV_QK) != 0 || n > 131072) return QMV_E_SHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return QMV_E_ARG;
+    if (!aligned(o, 16) || !aligned(x, 16) || !aligned(w, 16)) return QMV_E_ARG;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    const char *name = "";
+    hipError_t e = qmv::launch_rmsnorm(o, x, w, (int32_t)n, eps, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, 1);
+}
+
+qmv_status qmv_silu_mul(float *o, const float *g, const float *u, int64_t n, void *stream) {
+    if (n < 0 || n > INT32_MAX) return QMV_E_SHAPE;
+    if (n == 0) return QMV_OK;
+    if (o == nullptr || g == nullptr || u == nullptr) return QMV_E_ARG;
+    if (!aligned(o, 16) || !aligned(g, 16) || !aligned(u, 16)) return QMV_E_ARG;
+    qmv_status st = device_check(nullptr);
+    if (st != QMV_OK) return st;
+    const char *name = "";
+    hipError_t e = qmv::launch_silu_mul(o, g, u, n, static_cast<hipStream_t>(stream), &name);
+    return finish(e, name, (long)(n / 1024));
 }
 
 qmv_status qmv_ceiling_stream_read(uint32_t *sink, const void *buf, int64_t bytes, int32_t workgroups,

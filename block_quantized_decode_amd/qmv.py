@@ -77,6 +77,10 @@ _SIGS = {
                                   ctypes.c_int32, _P],
     "qmv_matvec_q4_fx_silu_mul": [_P, ctypes.POINTER(QTensor), _P, _P, ctypes.POINTER(QAct), ctypes.c_int32,
                                   ctypes.c_int32, _P],
+    "qmv_matvec_q8_fx_swiglu": [_P, _P, ctypes.POINTER(QTensor), _P, _P, ctypes.c_float, ctypes.POINTER(QAct),
+                                ctypes.c_int32, ctypes.c_int32, _P],
+    "qmv_matvec_q4_fx_swiglu": [_P, _P, ctypes.POINTER(QTensor), _P, _P, ctypes.c_float, ctypes.POINTER(QAct),
+                                ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_gemm_q8": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_gemm_q4": [_P, ctypes.POINTER(QTensor), ctypes.POINTER(QTensor), ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_pack_bytes": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
@@ -90,6 +94,8 @@ _SIGS = {
     "qmv_matvec_q4k_fx": [_P, ctypes.POINTER(Q4kTensor), _P, ctypes.POINTER(QAct), ctypes.c_int32, ctypes.c_int32,
                           _P],
     "qmv_device_check": [],
+    "qmv_rmsnorm": [_P, _P, _P, ctypes.c_int64, ctypes.c_float, _P],
+    "qmv_silu_mul": [_P, _P, _P, ctypes.c_int64, _P],
     "qmv_ceiling_stream_read": [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P],
     "qmv_ceiling_mfma_i8": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P],
 }
@@ -518,6 +524,43 @@ def prepare_matvec_fx_rmsnorm(qtype, wq, wd, x, w_norm, eps, y, r0=None, r1=None
     return Prepared(fname, args, [W, act, wq, wd, x, w_norm, y, xq_out], stream)
 
 
+def _swiglu_args(qtype, wq, wd, x, w_norm, eps, a, y, p0, p1, xq_out):
+    W = qtensor(wq, wd, qtype)
+    if W.rows % 2:
+        raise ValueError("the stacked gate|up matrix needs an even row count")
+    _dev(x, torch.float32)
+    if w_norm is not None:
+        _dev(w_norm, torch.float32)
+    p0 = 0 if p0 is None else p0
+    p1 = W.rows // 2 if p1 is None else p1
+    y = _out(y, W.rows, wd)
+    a = _out(a, W.rows // 2, wd)
+    act = None
+    if xq_out is not None:
+        q, d = xq_out
+        act = QAct(_dev(q, torch.int8).data_ptr(), _dev(d, torch.float32).data_ptr(), 0)
+    fname = "qmv_matvec_q4_fx_swiglu" if qtype == QMV_Q4_0 else "qmv_matvec_q8_fx_swiglu"
+    args = [a.data_ptr(), y.data_ptr(), ctypes.byref(W), x.data_ptr(),
+            w_norm.data_ptr() if w_norm is not None else None, ctypes.c_float(eps),
+            ctypes.byref(act) if act is not None else None, p0, p1]
+    return fname, args, [W, act, wq, wd, x, w_norm, a, y, xq_out], a, y
+
+
+def qmv_matvec_fx_swiglu(qtype, wq, wd, x, w_norm=None, eps=0.0, p0=None, p1=None, a=None, y=None, xq_out=None):
+    """Stacked gate|up product with the gate applied: returns (a, y), y = W h
+    (h = x, or rmsnorm(x) * w_norm) and a = silu(y[:F]) * y[F:] (include/qmv.h)."""
+    fname, args, _keep, a, y = _swiglu_args(qtype, wq, wd, x, w_norm, eps, a, y, p0, p1, xq_out)
+    _check(getattr(lib(), fname)(*args, _stream()), fname)
+    return a, y
+
+
+def prepare_matvec_fx_swiglu(qtype, wq, wd, x, a, y, w_norm=None, eps=0.0, p0=None, p1=None, xq_out=None,
+                             stream=None) -> Prepared:
+    """Prepared qmv_matvec_q4_fx_swiglu / qmv_matvec_q8_fx_swiglu."""
+    fname, args, keep, _a, _y = _swiglu_args(qtype, wq, wd, x, w_norm, eps, a, y, p0, p1, xq_out)
+    return Prepared(fname, args, keep, stream)
+
+
 def prepare_matvec_fx_silu_mul(qtype, wq, wd, g, u, y, r0=None, r1=None, xq_out=None, stream=None) -> Prepared:
     """Prepared qmv_matvec_q4_fx_silu_mul / qmv_matvec_q8_fx_silu_mul."""
     W = qtensor(wq, wd, qtype)
@@ -579,6 +622,34 @@ def prepare_matvec_q4k_fx(q, sc, mn, d, dmin, x, y, r0=None, r1=None, stream=Non
     r1 = W.rows if r1 is None else r1
     args = [y.data_ptr(), ctypes.byref(W), x.data_ptr(), None, r0, r1]
     return Prepared("qmv_matvec_q4k_fx", args, [W, q, sc, mn, d, dmin, x, y], stream)
+
+
+def qmv_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float, o: torch.Tensor | None = None):
+    """o = w * (x / rms(x)) as qmv_rmsnorm computes it (one launch)."""
+    _dev(x, torch.float32)
+    _dev(w, torch.float32)
+    o = torch.empty_like(x) if o is None else _dev(o, torch.float32)
+    _check(lib().qmv_rmsnorm(o.data_ptr(), x.data_ptr(), w.data_ptr(), x.numel(), float(eps), _stream()),
+           "qmv_rmsnorm")
+    return o
+
+
+def qmv_silu_mul(g: torch.Tensor, u: torch.Tensor, o: torch.Tensor | None = None):
+    """o = silu(g) * u as qmv_silu_mul computes it (one launch)."""
+    _dev(g, torch.float32)
+    _dev(u, torch.float32)
+    o = torch.empty_like(g) if o is None else _dev(o, torch.float32)
+    _check(lib().qmv_silu_mul(o.data_ptr(), g.data_ptr(), u.data_ptr(), g.numel(), _stream()), "qmv_silu_mul")
+    return o
+
+
+def prepare_rmsnorm(x, w, eps, o, stream=None) -> "Prepared":
+    return Prepared("qmv_rmsnorm", [o.data_ptr(), x.data_ptr(), w.data_ptr(), x.numel(), ctypes.c_float(eps)],
+                    [o, x, w], stream)
+
+
+def prepare_silu_mul(g, u, o, stream=None) -> "Prepared":
+    return Prepared("qmv_silu_mul", [o.data_ptr(), g.data_ptr(), u.data_ptr(), g.numel()], [o, g, u], stream)
 
 
 # ---- measurement helpers (not on the product path)

@@ -73,9 +73,11 @@ enum { QMV_Q4_0 = 4, QMV_Q8_0 = 8 };
 /* On-chip LDS budget of the single-row and few-row products: the quantized
  * activation rows are staged in LDS, 40 bytes per 32-element block per
  * activation row (rounded up to 64 blocks), plus, for the fused calls, the
- * float32 activation itself (4 bytes per element, rounded up to 1 KiB).
- * That bounds K: at most 131072 for the pre-quantized single-row product,
- * 31744 for the fused one, M * K <= 131072 for M <= 8 activation rows.
+ * float32 activation itself (4 bytes per element, rounded up to 1 KiB),
+ * and for the rmsnorm form 4 bytes per block (rounded up to a power of two)
+ * of block sums.  That bounds K: at most 131072 for the pre-quantized
+ * single-row product, 30720 for the fused one (30208 with rmsnorm), M * K
+ * <= 131072 for M <= 8 activation rows.
  * The matrix-core product (M > 8) stages nothing but its 32 KiB of partial
  * sums. */
 #define QMV_LDS_BYTES (160 * 1024)
@@ -148,7 +150,7 @@ qmv_status qmv_matvec_q4(float *y, const qmv_qtensor *W, const qmv_qact *x,
  * qmv_matvec_q8_fx / qmv_matvec_q4_fx -- the same product from a float32
  * activation x (W->cols floats, 16-byte aligned): the activation is
  * quantized to Q8_0 inside the kernel (the rule of qmv_quantize_q8, the
- * same bits) and never leaves the chip (limit: K <= 31744, the LDS budget
+ * same bits) and never leaves the chip (limit: K <= 30720, the LDS budget
  * with the float32 activation staged).  If xq is not NULL, xq->q (W->cols
  * bytes) and xq->d (W->cols / 32 floats) also receive the quantized
  * activation and xq->n is set to W->cols.
@@ -177,8 +179,7 @@ qmv_status qmv_matvec_q4_fx(float *y, const qmv_qtensor *W, const float *x,
  *   eps       : finite and >= 0 (QMV_E_ARG otherwise); with eps = 0 an
  *               all-zero x gives a non-finite inv (the caller's choice).
  *   xq        : NULL, or receives the quantized h (as in qmv_matvec_*_fx).
- *   K / 32 must be at most 32 or in [64, 512] (QMV_E_SHAPE otherwise: the
- *   normalization is built into the split-K kernel only).
+ *   K <= 30208 (the LDS budget; QMV_E_SHAPE beyond).
  *   Rows, y indexing and errors otherwise as qmv_matvec_q8_fx.
  * ------------------------------------------------------------------------- */
 qmv_status qmv_matvec_q8_fx_rmsnorm(float *y, const qmv_qtensor *W, const float *x,
@@ -203,7 +204,7 @@ qmv_status qmv_matvec_q4_fx_rmsnorm(float *y, const qmv_qtensor *W, const float 
  *   g, u : W->cols floats each, 16-byte aligned, device memory (they may be
  *          the two halves of one concatenated W1|W3 output).
  *   xq   : NULL, or receives the quantized a.
- *   K / 32 must be at most 32 or in [64, 512] (QMV_E_SHAPE otherwise).
+ *   K <= 30720, as qmv_matvec_q8_fx.
  *   Rows, y indexing and errors otherwise as qmv_matvec_q8_fx.
  * ------------------------------------------------------------------------- */
 qmv_status qmv_matvec_q8_fx_silu_mul(float *y, const qmv_qtensor *W, const float *g,
@@ -212,6 +213,54 @@ qmv_status qmv_matvec_q8_fx_silu_mul(float *y, const qmv_qtensor *W, const float
 qmv_status qmv_matvec_q4_fx_silu_mul(float *y, const qmv_qtensor *W, const float *g,
                                      const float *u, qmv_qact *xq, int32_t r0, int32_t r1,
                                      void *stream);
+
+/* ---------------------------------------------------------------------------
+ * qmv_matvec_q8_fx_swiglu / qmv_matvec_q4_fx_swiglu -- the FFN's first half
+ * of a decode step in one launch (spec section 6: h = rmsnorm(x); qa =
+ * quantize_q8(h); g = matvec(W1, qa); u = matvec(W3, qa); silu_mul(g, u)),
+ * with W1 and W3 stacked as one matrix: W->rows = 2 F, rows 0 .. F - 1 the
+ * gate W1 and rows F .. 2 F - 1 the up projection W3.  For pairs p0 <= j <
+ * p1 (0 <= p0 <= p1 <= F):
+ *   y[j] = (W h)[j],  y[F + j] = (W h)[F + j]   (as qmv_matvec_q8_fx, or
+ *                                                 _fx_rmsnorm when w_norm)
+ *   a[j] = (y[j] * (1 / (1 + exp(-y[j])))) * y[F + j]   (qmv_silu_mul's
+ *          evaluation, so a is bit-identical to qmv_silu_mul on this y).
+ * h = x when w_norm is NULL, else rmsnorm(x) * w_norm with eps as in
+ * qmv_matvec_q8_fx_rmsnorm.  y has W->rows floats and a has F floats, both
+ * indexed by absolute row (4-byte aligned); other entries are not written.
+ * For 64 <= K / 32 <= 512 both halves and the gate come from one launch
+ * (each workgroup takes a run of pairs, both of its rows' slices); for
+ * other K the two halves run as the plain fused products and the gate as
+ * a launch of its own (same bits).  W->rows odd or the pair range outside
+ * [0, F] is QMV_E_SHAPE; other arguments and errors as qmv_matvec_q8_fx.
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_matvec_q8_fx_swiglu(float *a, float *y, const qmv_qtensor *W, const float *x,
+                                   const float *w_norm, float eps, qmv_qact *xq,
+                                   int32_t p0, int32_t p1, void *stream);
+qmv_status qmv_matvec_q4_fx_swiglu(float *a, float *y, const qmv_qtensor *W, const float *x,
+                                   const float *w_norm, float eps, qmv_qact *xq,
+                                   int32_t p0, int32_t p1, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The two neighbours as launches of their own (spec section 5 kernel list:
+ * ml_k_rmsnorm(o, x, w, n, eps), ml_k_silu_mul(g, u, n)).  They evaluate
+ * the same device functions, in the same order, as the fused activation
+ * forms above, so e.g. qmv_rmsnorm then qmv_matvec_q4_fx gives the same bits
+ * as qmv_matvec_q4_fx_rmsnorm (one launch more).
+ *
+ * qmv_rmsnorm: o_j = w_j * (inv * x_j), inv = 1 / sqrt(ss / n + eps), ss
+ *   summed as qmv_matvec_q8_fx_rmsnorm states (pairwise within each
+ *   32-element block, then pairwise over the zero-padded block sums).
+ *   o, x, w: n floats each, device memory, 16-byte aligned; o may equal x.
+ *   0 < n <= 131072, n % 32 == 0 (QMV_E_SHAPE otherwise); eps finite and
+ *   >= 0 (QMV_E_ARG otherwise).  Runs as one workgroup.
+ * qmv_silu_mul: o_j = (g_j * (1 / (1 + exp(-g_j)))) * u_j with the exp and
+ *   reciprocal of qmv_matvec_q8_fx_silu_mul.  o, g, u: n floats each,
+ *   device memory, 16-byte aligned; o may equal g or u.  0 <= n <=
+ *   INT32_MAX; n == 0 enqueues nothing and accepts null pointers.
+ * ------------------------------------------------------------------------- */
+qmv_status qmv_rmsnorm(float *o, const float *x, const float *w, int64_t n, float eps, void *stream);
+qmv_status qmv_silu_mul(float *o, const float *g, const float *u, int64_t n, void *stream);
 
 /* ---------------------------------------------------------------------------
  * qmv_gemm_q8 / qmv_gemm_q4 -- the product for M activation rows at once:
@@ -385,9 +434,10 @@ qmv_status qmv_gemm_q4_packed(float *Y, const qmv_packed *P, const qmv_qtensor *
  *
  * qmv_ceiling_stream_read: reads `bytes` (a multiple of 16, at least 16) of
  *   buf (device memory, 16-byte aligned) with `workgroups` (1 .. 65536)
- *   workgroups of 1024 threads, each thread keeping `depth` (4 or 8) 16-byte
- *   non-temporal loads in flight per round, the grid striding over the
- *   buffer.  sink[w] (workgroups uint32 of device memory) receives the XOR
+ *   workgroups of 1024 threads in rounds: in each round every thread issues
+ *   `depth` (4 or 8) 16-byte non-temporal loads (consecutive threads read
+ *   consecutive 16-byte pieces; the round covers depth x threads pieces)
+ *   before using any.  sink[w] (workgroups uint32 of device memory) receives the XOR
  *   of the 32-bit words workgroup w read, so the XOR over all of sink is the
  *   XOR of every 32-bit word of buf.
  * qmv_ceiling_mfma_i8: `workgroups` (1 .. 65536) workgroups of 4

@@ -51,6 +51,7 @@ def test_header_declares_the_product_calls():
               "qmv_matvec_q8_fx", "qmv_matvec_q4_fx", "qmv_gemm_q8", "qmv_gemm_q4",
               "qmv_matvec_q8_fx_rmsnorm", "qmv_matvec_q4_fx_rmsnorm",
               "qmv_matvec_q8_fx_silu_mul", "qmv_matvec_q4_fx_silu_mul",
+              "qmv_matvec_q8_fx_swiglu", "qmv_matvec_q4_fx_swiglu", "qmv_rmsnorm", "qmv_silu_mul",
               "qmv_pack_bytes", "qmv_pack_weights", "qmv_gemm_q8_packed", "qmv_gemm_q4_packed",
               "qmv_quantize_q8_b128", "qmv_matvec_zp_fx", "qmv_quantize_q8_b256", "qmv_matvec_q4k_fx",
               "qmv_status_str", "qmv_last_kernel", "qmv_device_check"):
@@ -133,8 +134,10 @@ def test_matvec_fx_rmsnorm_validation(lib, fn, t):
     assert f(Y, ctypes.byref(W), X + 8, N, 1e-5, None, 0, 8, None) == E_ARG               # x misaligned
     assert f(Y, ctypes.byref(W), X, N, 1e-5, ctypes.byref(QA(0, B, 0)), 0, 8, None) == E_ARG
     assert f(Y, ctypes.byref(_w(t=Q4 if t == Q8 else Q8)), X, N, 1e-5, None, 0, 8, None) == E_FORMAT
-    for cols in (32 * 33, 32 * 63, 32 * 513):                                              # outside the kernel's K
-        assert f(Y, ctypes.byref(_w(t=t, cols=cols)), X, N, 1e-5, None, 0, 8, None) == E_SHAPE, cols
+    assert f(Y, ctypes.byref(_w(t=t, cols=32 * 945)), X, N, 1e-5, None, 0, 8, None) == E_SHAPE  # beyond LDS
+    st = lib.qmv_device_check()
+    for cols in (32 * 33, 32 * 63, 32 * 513, 32 * 944):   # every K up to the LDS budget passes the checks
+        assert f(Y, ctypes.byref(_w(t=t, cols=cols)), X, N, 1e-5, None, 3, 3, None) in (st, OK), cols
     assert f(Y, ctypes.byref(W), X, N, 1e-5, None, 3, 2, None) == E_SHAPE
 
 
@@ -151,9 +154,68 @@ def test_matvec_fx_silu_mul_validation(lib, fn, t):
     assert f(Y, ctypes.byref(W), G, U + 8, None, 0, 8, None) == E_ARG                     # u misaligned
     assert f(Y, ctypes.byref(W), G, U, ctypes.byref(QA(A, 0, 0)), 0, 8, None) == E_ARG    # xq with null d
     assert f(Y, ctypes.byref(_w(t=Q4 if t == Q8 else Q8)), G, U, None, 0, 8, None) == E_FORMAT
-    for cols in (32 * 33, 32 * 63, 32 * 513):
-        assert f(Y, ctypes.byref(_w(t=t, cols=cols)), G, U, None, 0, 8, None) == E_SHAPE, cols
+    assert f(Y, ctypes.byref(_w(t=t, cols=32 * 961)), G, U, None, 0, 8, None) == E_SHAPE   # beyond LDS
+    st = lib.qmv_device_check()
+    for cols in (32 * 33, 32 * 63, 32 * 513, 32 * 960):
+        assert f(Y, ctypes.byref(_w(t=t, cols=cols)), G, U, None, 3, 3, None) in (st, OK), cols
     assert f(Y, ctypes.byref(W), G, U, None, 0, 9, None) == E_SHAPE
+
+
+@pytest.mark.parametrize("fn,t", [("qmv_matvec_q8_fx_swiglu", Q8), ("qmv_matvec_q4_fx_swiglu", Q4)])
+def test_matvec_fx_swiglu_validation(lib, fn, t):
+    f = getattr(lib, fn)
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, P, P, P, ctypes.c_float, P, ctypes.c_int32, ctypes.c_int32, P]
+    W = _w(t=t)                       # 8 rows: F = 4 pairs
+    X, N, Ya = A + 0x1000, A + 0x2000, Y + 0x1000
+    assert f(Ya, Y, ctypes.byref(W), None, N, 1e-5, None, 0, 4, None) == E_ARG            # null x
+    assert f(None, Y, ctypes.byref(W), X, N, 1e-5, None, 0, 4, None) == E_ARG              # null a
+    assert f(Ya, None, ctypes.byref(W), X, N, 1e-5, None, 0, 4, None) == E_ARG             # null y
+    assert f(Ya + 2, Y, ctypes.byref(W), X, N, 1e-5, None, 0, 4, None) == E_ARG            # a misaligned
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert f(Ya, Y, ctypes.byref(W), X, N, eps, None, 0, 4, None) == E_ARG, eps
+    assert f(Ya, Y, ctypes.byref(W), X, N + 4, 1e-5, None, 0, 4, None) == E_ARG           # w_norm misaligned
+    assert f(Ya, Y, ctypes.byref(W), X + 8, None, 0.0, None, 0, 4, None) == E_ARG          # x misaligned
+    assert f(Ya, Y, ctypes.byref(W), X, N, 1e-5, ctypes.byref(QA(0, B, 0)), 0, 4, None) == E_ARG
+    assert f(Ya, Y, ctypes.byref(_w(t=Q4 if t == Q8 else Q8)), X, N, 1e-5, None, 0, 4, None) == E_FORMAT
+    assert f(Ya, Y, ctypes.byref(_w(rows=7, t=t)), X, N, 1e-5, None, 0, 3, None) == E_SHAPE   # odd rows
+    assert f(Ya, Y, ctypes.byref(W), X, N, 1e-5, None, 0, 5, None) == E_SHAPE              # p1 > F
+    assert f(Ya, Y, ctypes.byref(W), X, N, 1e-5, None, -1, 2, None) == E_SHAPE
+    assert f(Ya, Y, ctypes.byref(W), X, N, 1e-5, None, 3, 2, None) == E_SHAPE
+    assert f(Ya, Y, ctypes.byref(_w(t=t, cols=32 * 945)), X, N, 1e-5, None, 0, 4, None) == E_SHAPE
+    st = lib.qmv_device_check()
+    assert f(Ya, Y, ctypes.byref(_w(t=t, cols=32 * 960)), X, None, 0.0, None, 0, 0, None) in (st, OK)
+    assert f(None, None, ctypes.byref(QT(0, 0, 0, 64, t)), X, None, 0.0, None, 0, 0, None) in (st, OK)
+
+
+def test_neighbour_validation(lib):
+    P = ctypes.c_void_p
+    f = lib.qmv_rmsnorm
+    f.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_float, P]
+    O, X, N = Y, A + 0x1000, A + 0x2000
+    assert f(None, X, N, 64, 1e-5, None) == E_ARG
+    assert f(O, None, N, 64, 1e-5, None) == E_ARG
+    assert f(O, X, None, 64, 1e-5, None) == E_ARG
+    for n in (0, -32, 48, 131072 + 32):
+        assert f(O, X, N, n, 1e-5, None) == E_SHAPE, n
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert f(O, X, N, 64, eps, None) == E_ARG, eps
+    assert f(O + 4, X, N, 64, 1e-5, None) == E_ARG
+    assert f(O, X + 8, N, 64, 1e-5, None) == E_ARG
+    assert f(O, X, N + 4, 64, 1e-5, None) == E_ARG
+    g = lib.qmv_silu_mul
+    g.argtypes = [P, P, P, ctypes.c_int64, P]
+    assert g(None, None, None, 0, None) == OK                      # n = 0: nothing to do
+    assert g(O, X, N, -1, None) == E_SHAPE
+    assert g(O, X, N, 2 ** 31, None) == E_SHAPE
+    assert g(None, X, N, 5, None) == E_ARG
+    assert g(O, None, N, 5, None) == E_ARG
+    assert g(O, X, None, 5, None) == E_ARG
+    assert g(O + 4, X, N, 5, None) == E_ARG
+    st = lib.qmv_device_check()
+    if st != OK:
+        assert f(O, X, N, 96, 0.0, None) == st
+        assert g(O, X, N, 5, None) == st
 
 
 @pytest.mark.parametrize("fn,t", [("qmv_gemm_q8", Q8), ("qmv_gemm_q4", Q4)])
