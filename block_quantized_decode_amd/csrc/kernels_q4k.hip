@@ -35,6 +35,10 @@
 #include "launch.h"
 #include "rowstream.h"
 
+#ifndef QMV_GS  // split-K kernel (kernels_gs.hip) for rows of 128 and more sub-blocks
+#define QMV_GS 1
+#endif
+
 namespace qmv {
 namespace {
 
@@ -45,27 +49,6 @@ constexpr int SB = 256;     // elements per super-block
 constexpr int SUB = 32;     // elements per sub-block (one 16-byte chunk)
 constexpr int LB = SB / SUB;  // chunks (lanes) per super-block
 constexpr int kQBatch = 2;  // blocks whose loads a wavefront issues together
-
-// Quantize the 256-element block held by this wavefront (lane c holds
-// elements 4c .. 4c + 3): amax exact, d = amax / 127, id = 127 / amax, the
-// spec's rounding; sub = the sum of the quants of this lane's 32-element
-// sub-block (lanes 8j .. 8j + 7), in every lane of it.
-__device__ __forceinline__ void quant_block256(float4 v, int (&q)[4], float &d, int &sub) {
-    const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    int r0, r1, r2, r3;
-    rs::row_values(rs::row16_reduce(__float_as_int(m), [](int a, int b) { return max(a, b); }), r0, r1, r2, r3);
-    const float amax = __int_as_float(max(max(r0, r1), max(r2, r3)));  // non-negative floats order like ints
-    d = amax / 127.0f;
-    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
-    q[0] = rs::q8_round(v.x, id);
-    q[1] = rs::q8_round(v.y, id);
-    q[2] = rs::q8_round(v.z, id);
-    q[3] = rs::q8_round(v.w, id);
-    int s = q[0] + q[1] + q[2] + q[3];
-    s += rs::dppi<rs::kX1>(s);
-    s += rs::dppi<rs::kX2>(s);
-    sub = s + rs::dppi<rs::kM8>(s);
-}
 
 template <int L, int J, int D, int P, int WPB>
 __global__ void __launch_bounds__(64 * WPB)
@@ -223,7 +206,7 @@ k_q4k(float *__restrict__ y, const uint8_t *__restrict__ wq, const uint8_t *__re
             if (b >= nk) break;  // wave-uniform
             int q[4], subsum;
             float d;
-            quant_block256(v[u], q, d, subsum);
+            rs::quant_block256(v[u], q, d, subsum);
             const int pk = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | (q[3] << 24);
             *reinterpret_cast<int *>(xs + b * SB + 4 * lane) = pk;
             if ((lane & 7) == 0) sqs[b * LB + (lane >> 3)] = subsum;
@@ -302,7 +285,7 @@ k_quant_b256(int8_t *__restrict__ q, float *__restrict__ d, const float *__restr
         const float4 v = *reinterpret_cast<const float4 *>(x + b * SB + 4 * lane);
         int qv[4], subsum;
         float dd;
-        quant_block256(v, qv, dd, subsum);
+        rs::quant_block256(v, qv, dd, subsum);
         *reinterpret_cast<int *>(q + b * SB + 4 * lane) =
             (qv[0] & 0xFF) | ((qv[1] & 0xFF) << 8) | ((qv[2] & 0xFF) << 16) | (qv[3] << 24);
         if (lane == 0) d[b] = dd;
@@ -315,6 +298,10 @@ size_t q4k_lds_bytes(int32_t K) { return lds_x_bytes(K) + 8192; }
 
 hipError_t launch_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **name) {
     if (a.K % SB != 0 || q4k_lds_bytes(a.K) > 160 * 1024) return hipErrorNotSupported;
+#if QMV_GS
+    const hipError_t e = launch_gs_q4k(a, num_cu, s, name);  // the split-K form where it takes the shape
+    if (e != hipErrorNotSupported) return e;
+#endif
     const int chunks = a.K / SUB;
     const int nrow = a.r1 - a.r0;
     const size_t lds_x = lds_x_bytes(a.K);

@@ -55,6 +55,9 @@ namespace {
 using rs::kOOB;
 using rs::v4i;
 
+#ifndef QMV_GS  // split-K kernel (kernels_gs.hip) for rows of 128 and more units
+#define QMV_GS 1
+#endif
 #ifndef QMV_ZP_D12  // register ring depth for 1-2 chunks per lane
 #define QMV_ZP_D12 4
 #endif
@@ -64,29 +67,6 @@ using rs::v4i;
 
 constexpr int BLK = 128;    // elements per block
 constexpr int kQBatch = 2;  // block pairs whose loads a wavefront issues together
-
-// Quantize the 128-element block held by this half-wavefront (lane c of the
-// half holds elements 4c .. 4c + 3): amax exact (maximum over the half by
-// DPP within rows and lane reads across them; non-negative floats order like
-// their bit patterns), d = amax / 127, id = 127 / amax (correctly rounded
-// divisions), then the spec's rounding; qsum = the sum of the 128 quants.
-__device__ __forceinline__ void quant_half(float4 v, int (&q)[4], float &d, int &qsum) {
-    const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    const auto imax = [](int a, int b) { return max(a, b); };
-    const auto isum = [](int a, int b) { return a + b; };
-    int r0, r1, r2, r3;
-    rs::row_values(rs::row16_reduce(__float_as_int(m), imax), r0, r1, r2, r3);
-    const bool hi = (threadIdx.x & 32) != 0;
-    const float amax = __int_as_float(hi ? max(r2, r3) : max(r0, r1));
-    d = amax / 127.0f;
-    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
-    q[0] = rs::q8_round(v.x, id);
-    q[1] = rs::q8_round(v.y, id);
-    q[2] = rs::q8_round(v.z, id);
-    q[3] = rs::q8_round(v.w, id);
-    rs::row_values(rs::row16_reduce(q[0] + q[1] + q[2] + q[3], isum), r0, r1, r2, r3);
-    qsum = hi ? r2 + r3 : r0 + r1;
-}
 
 // position of element e of a block in the 4-bit activation order
 __device__ __forceinline__ int perm4(int e) { return (e & ~7) + ((e & 1) << 2) + ((e & 7) >> 1); }
@@ -261,7 +241,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             const int b = b0 + (lane >> 5);
             int q[4], qs;
             float d;
-            quant_half(v[u], q, d, qs);
+            rs::quant_half(v[u], q, d, qs);
             if (b < nb) {
                 const int e = 4 * (lane & 31);
                 const int pk = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | (q[3] << 24);
@@ -397,7 +377,7 @@ k_quant_b128(int8_t *__restrict__ q, float *__restrict__ d, const float *__restr
                                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         int qv[4], qs;
         float dd;
-        quant_half(v, qv, dd, qs);
+        rs::quant_half(v, qv, dd, qs);
         if (b < nblk) {
             *reinterpret_cast<int *>(q + b * BLK + 4 * (lane & 31)) =
                 (qv[0] & 0xFF) | ((qv[1] & 0xFF) << 8) | ((qv[2] & 0xFF) << 16) | (qv[3] << 24);
@@ -412,6 +392,10 @@ size_t zp_lds_bytes(int32_t K) { return (((size_t)K + 8 * (size_t)(K / BLK) + 15
 
 hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
     if (a.K % BLK != 0 || zp_lds_bytes(a.K) > 160 * 1024) return hipErrorNotSupported;
+#if QMV_GS
+    const hipError_t e = launch_gs_zp(a, num_cu, s, name);  // the split-K form where it takes the shape
+    if (e != hipErrorNotSupported) return e;
+#endif
     return a.bits == 8 ? launch_bits<8>(a, num_cu, s, name) : launch_bits<4>(a, num_cu, s, name);
 }
 

@@ -96,6 +96,10 @@ struct ZpArgs {
     int32_t r0, r1;
 };
 size_t zp_lds_bytes(int32_t K);
+// Split-K form of the zero-point and K-quant products for rows of at least
+// 16 units (32 elements each) per wavefront (kernels_gs.hip); returns
+// hipErrorNotSupported, launching nothing, for other shapes.
+hipError_t launch_gs_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name);
 hipError_t launch_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name);
 hipError_t launch_quant_b128(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name);
 
@@ -112,6 +116,7 @@ struct Q4kArgs {
     int32_t r0, r1;
 };
 size_t q4k_lds_bytes(int32_t K);
+hipError_t launch_gs_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **name);
 hipError_t launch_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **name);
 hipError_t launch_quant_b256(int8_t *q, float *d, const float *x, int64_t nblk, hipStream_t s, const char **name);
 

@@ -92,6 +92,50 @@ __device__ __forceinline__ float group_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Quantize the 128-element block held by this half-wavefront (lane c of the
+// half holds elements 4c .. 4c + 3): amax exact (maximum over the half by
+// DPP within rows and lane reads across them; non-negative floats order like
+// their bit patterns), d = amax / 127, id = 127 / amax (correctly rounded
+// divisions), then the spec's rounding; qsum = the sum of the 128 quants.
+__device__ __forceinline__ void quant_half(float4 v, int (&q)[4], float &d, int &qsum) {
+    const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    const auto imax = [](int a, int b) { return max(a, b); };
+    const auto isum = [](int a, int b) { return a + b; };
+    int r0, r1, r2, r3;
+    row_values(row16_reduce(__float_as_int(m), imax), r0, r1, r2, r3);
+    const bool hi = (threadIdx.x & 32) != 0;
+    const float amax = __int_as_float(hi ? max(r2, r3) : max(r0, r1));
+    d = amax / 127.0f;
+    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
+    q[0] = q8_round(v.x, id);
+    q[1] = q8_round(v.y, id);
+    q[2] = q8_round(v.z, id);
+    q[3] = q8_round(v.w, id);
+    row_values(row16_reduce(q[0] + q[1] + q[2] + q[3], isum), r0, r1, r2, r3);
+    qsum = hi ? r2 + r3 : r0 + r1;
+}
+
+// Quantize the 256-element block held by this wavefront (lane c holds
+// elements 4c .. 4c + 3): amax exact, d = amax / 127, id = 127 / amax, the
+// spec's rounding; sub = the sum of the quants of this lane's 32-element
+// sub-block (lanes 8j .. 8j + 7), in every lane of it.
+__device__ __forceinline__ void quant_block256(float4 v, int (&q)[4], float &d, int &sub) {
+    const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int r0, r1, r2, r3;
+    row_values(row16_reduce(__float_as_int(m), [](int a, int b) { return max(a, b); }), r0, r1, r2, r3);
+    const float amax = __int_as_float(max(max(r0, r1), max(r2, r3)));  // non-negative floats order like ints
+    d = amax / 127.0f;
+    const float id = amax != 0.0f ? 127.0f / amax : 0.0f;
+    q[0] = q8_round(v.x, id);
+    q[1] = q8_round(v.y, id);
+    q[2] = q8_round(v.z, id);
+    q[3] = q8_round(v.w, id);
+    int s = q[0] + q[1] + q[2] + q[3];
+    s += dppi<kX1>(s);
+    s += dppi<kX2>(s);
+    sub = s + dppi<kM8>(s);
+}
+
 // Work item t of a lane group: its row, window, and whether it starts or
 // ends the row's accumulation.
 struct Item {

@@ -62,7 +62,7 @@ def test_q4k_matches_oracle(rows, k):
     x = _x(rng, k)
     xq, xd = orc.quantize_q8_b256(x)
     y, qo, do = _run(w, x)
-    assert qmv.last_kernel().startswith("q4k_"), qmv.last_kernel()
+    assert qmv.last_kernel().startswith(("q4k_", "gs_q4k_")), qmv.last_kernel()
     assert np.array_equal(qo, xq), "activation codes"
     assert np.array_equal(do.view(np.uint32), xd.view(np.uint32)), "activation scales"
     _check(y, w, xq, xd, 0, rows, f"q4k {rows}x{k}")

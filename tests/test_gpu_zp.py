@@ -66,7 +66,7 @@ def test_zp_matches_oracle(bits, rows, k, with_zp):
     x = _x(rng, k)
     xq, xd = orc.quantize_q8_b128(x)
     y, qo, do = _run(bits, wq, wd, wzp, x)
-    assert qmv.last_kernel().startswith(f"zp{bits}_"), qmv.last_kernel()
+    assert qmv.last_kernel().startswith((f"zp{bits}_", "gs_zp4_" if bits == 4 else "zp8_")), qmv.last_kernel()
     assert np.array_equal(qo, xq), "activation codes"
     assert np.array_equal(do.view(np.uint32), xd.view(np.uint32)), "activation scales"
     _check(bits, y, wq, wd, wzp, xq, xd, 0, rows, f"zp{bits} {rows}x{k}")
@@ -135,13 +135,15 @@ def test_quantize_b128(k):
 #   - rows in [2048, 4096) at K = 11008, where teams take more wavefronts
 #     until a ring turn takes one scale load (p = 4);
 #   - one wavefront per row with two windows per row, the accumulator
-#     carried across items (8-bit K = 16384 and 4-bit K = 32768 at 8192 rows).
+#     carried across items (8-bit K = 16384 and 4-bit K = 32768 at 8192 rows);
+#   - the split-K kernel for 4-bit codes (gs_: n units per lane and pass,
+#     ring depth d, w wavefronts) on the Llama-7B shapes.
 FULL = [
     (4, 4864, 896, "zp4_l32_j1_d4_p1_w8"), (8, 4864, 896, "zp8_l64_j1_d4_p1_w8"),
     (4, 896, 4864, "zp4_l64_j1_d4_p4_w16"), (8, 896, 4864, "zp8_l64_j2_d4_p4_w16"),
     (4, 151936, 896, "zp4_l32_j1_d4_p1_w8"), (8, 151936, 896, "zp8_l64_j1_d4_p1_w8"),
-    (4, 11008, 4096, "zp4_l64_j2_d2_p1_w16"), (8, 11008, 4096, "zp8_l64_j4_d2_p1_w16"),
-    (4, 4096, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 4096, 11008, "zp8_l64_j3_d2_p4_w16"),
+    (4, 11008, 4096, "gs_zp4_n1_d4_w8"), (8, 11008, 4096, "zp8_l64_j4_d2_p1_w16"),
+    (4, 4096, 11008, "gs_zp4_n3_d4_w8"), (8, 4096, 11008, "zp8_l64_j3_d2_p4_w16"),
     (4, 2048, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 2048, 11008, "zp8_l64_j3_d2_p4_w16"),
     (4, 3001, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 3001, 11008, "zp8_l64_j3_d2_p4_w16"),
     (8, 8192, 16384, "zp8_l64_j8_d2_p1_w16"), (4, 8192, 32768, "zp4_l64_j8_d2_p1_w16"),
