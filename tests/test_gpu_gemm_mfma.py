@@ -14,10 +14,11 @@ are checked against the oracle within
 |y - y_ref| <= 1e-5 * sum_b |sumi * dw * dx| + 1e-6."""
 import numpy as np
 import pytest
+import torch
 
 import pins
 from block_quantized_decode_amd import qmv, synth
-from gpu_util import announce, check_close, dev, host
+from gpu_util import announce, check_close, check_gemm_all, dev, host
 from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -193,3 +194,30 @@ def test_gemm_mfma_row_tiles(qtype, rows, k, m):
     xq, xd = _act(rng, m, k)
     Y = host(_f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd)))
     _check_all(qtype, Y, wq, wd, xq, xd, 0, rows, f"q{qtype} {rows}x{k} m={m}")
+
+
+# One activation tile (9 .. 16 rows): stages per wavefront 4 (K = 4096), 8
+# (8192), 11 (11008), 16 (16384); 1 .. 4 weight tiles per workgroup; a ragged
+# last tile and a partial last stage (K = 4128).
+ONE_TILE_CASES = [(4096, 4096, 16, 1), (4090, 8192, 9, 1), (4096, 11008, 16, 1), (3001, 16384, 12, 1),
+                  (8000, 4096, 16, 2), (11008, 4096, 16, 3), (11000, 8192, 13, 3), (16000, 4128, 16, 4),
+                  (16001, 8192, 10, 4)]
+
+
+@pytest.mark.parametrize("qtype", [4, 8])
+@pytest.mark.parametrize("rows,k,m,rt", ONE_TILE_CASES, ids=[f"{r}x{k}-m{m}-rt{t}" for r, k, m, t in ONE_TILE_CASES])
+def test_gemm_one_activation_tile(qtype, rows, k, m, rt):
+    """Every output against the oracle, and the launch shape (weight tiles
+    per workgroup) on a 256-compute-unit MI355X."""
+    announce(f"gemm one tile q{qtype} {rows}x{k} m={m}")
+    rng = np.random.default_rng(9000 + rows + k + m + qtype)
+    wq, wd = _weights(rng, qtype, rows, k)
+    xq, xd = _act(rng, m, k)
+    Y = host(_f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd)))
+    kname = qmv.last_kernel()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert kname.startswith(f"mm_q{qtype}_mt1_rt{rt}_"), kname
+    worst = check_gemm_all(qtype, Y, wq, wd, xq, xd, what=f"q{qtype} {rows}x{k} m={m}")
+    print(f"  {kname}: max |err| / tol = {worst:.4f}")
+    Y2 = host(_f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd)))
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32)), "same inputs, same bits"

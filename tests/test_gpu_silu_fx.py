@@ -6,8 +6,10 @@ activation is checked against the oracle (oracle.silu_mul with the C
 library's expf, then quantize_q8) to that accuracy:
   * block scales within 2e-6 relative of the oracle's (all-zero blocks: 0);
   * every code within one of the oracle's, and a rounding of the oracle's
-    activation at the kernel's own scale within the same error; fewer than
-    one code in a thousand differs;
+    activation at the kernel's own scale within the same error; a code that
+    differs from the oracle's lies within that error of a rounding boundary
+    of the oracle's scaled value (so differences are confined to elements the
+    spec's exp tolerance leaves undecided);
 and y is checked within the product's tolerance against the oracle's product
 on the kernel's own codes and scales (the xq output), which isolates the
 product from the exp difference.  The activation may be the two halves of
@@ -39,8 +41,16 @@ def _check_activation(a_ref, qo, do):
     xq_ref, xd_ref = orc.quantize_q8(a_ref)
     assert np.all(np.abs(do.astype(np.float64) - xd_ref) <= REL * xd_ref), "block scales"
     assert np.all(np.abs(qo.astype(np.int32) - xq_ref.astype(np.int32)) <= 1), "codes beyond one step"
-    differ = np.count_nonzero(qo != xq_ref)
-    assert differ <= max(1, k // 1000), f"{differ} of {k} codes differ"
+    # a code may differ from the oracle's only where the oracle's scaled value
+    # t = a * 127 / amax lies within the exp error of a rounding boundary:
+    # a and amax each move by at most REL relative, so t by 2 REL |t| (plus
+    # the fp32 rounding of the product, below 1e-7 |t|)
+    amax = np.repeat(np.max(np.abs(a_ref.reshape(-1, 32)).astype(np.float64), axis=1), 32)
+    tr = np.where(amax > 0, np.abs(a_ref.astype(np.float64)) * 127.0 / np.where(amax > 0, amax, 1.0), 0.0)
+    dist = np.abs(tr - np.floor(tr) - 0.5)
+    diff = qo != xq_ref
+    assert np.all(dist[diff] <= (2 * REL + 1e-7) * (tr[diff] + 1.0)), \
+        f"{int(diff.sum())} of {k} codes differ, some away from a rounding boundary"
     # each code rounds the oracle's activation at the kernel's scale, to within the exp error
     dd = np.repeat(do.astype(np.float64), 32)
     ok = dd > 0
