@@ -110,7 +110,7 @@ struct Region {
 // the quants go from the load straight into the operand, never through LDS.
 // The sums are the same operations in the same order as for the row-major
 // layout, so the two give the same bits.
-template <int QT, int MT, int RT, int WPB, int D, bool PK>
+template <int QT, int MT, int RT, int WPB, int D, bool PK, bool TAIL>
 __global__ void __launch_bounds__(64 * WPB)
 k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restrict__ wd, int32_t rows, int32_t K,
      const int8_t *__restrict__ xq, const float *__restrict__ xd, int32_t M, int32_t r0, int32_t r1) {
@@ -131,7 +131,6 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     // stages of this wavefront: wid, wid + WPB, wid + 2 WPB, ... (the
     // wavefronts of the workgroup read adjacent spans of each row together)
     const int ns = (nb + KU - 1) / KU;
-    const int per = (ns + WPB - 1) / WPB;
     const int nst = wid < ns ? (ns - wid + WPB - 1) / WPB : 0;
     auto stage = [&](int j) { return wid + WPB * j; };
 
@@ -272,23 +271,58 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     };
 
     // ring of D register stages, unrolled by D so that each stage lives in
-    // fixed registers; every wavefront runs the same number of iterations
+    // fixed registers.  (This wavefront's reads of the previous stage are
+    // done before its writes of this one: LDS operations of a wavefront
+    // complete in order.)
     St ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) load(ring[d], d);
-    const int nit = (per + D - 1) / D;
-    for (int it = 0; it < nit; ++it) {
+    auto step = [&](int d, int j) __attribute__((always_inline)) {
+        stash(ring[d], j);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        compute(ring[d]);
+    };
+    if constexpr (TAIL) {
+        // many stages (the launcher's choice): turns whose loads all fall
+        // among this wavefront's stages run unguarded (exact wait counts),
+        // and the last one or two load and compute only stages that exist
+        // (measured: Q4_0 W_down 4096 x 11008 at M = 16, 11 stages,
+        // 14.3 -> 12.9 us)
+        int it = 0;
+        for (; (it + 2) * D - 2 < nst; ++it) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int j = it * D + d;
-            load(ring[(d + D - 1) % D], j + D - 1);
-            // this wavefront's reads of the previous stage are done before
-            // its writes of this one (LDS operations of a wavefront complete
-            // in order)
-            stash(ring[d], j);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            compute(ring[d]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int d = 0; d < D; ++d) {
+                const int j = it * D + d;
+                load(ring[(d + D - 1) % D], j + D - 1);
+                step(d, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        for (; it * D < nst; ++it) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int j = it * D + d;
+                if (j < nst) {  // (wave-uniform)
+                    if (j + D - 1 < nst) load(ring[(d + D - 1) % D], j + D - 1);
+                    step(d, j);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        // few stages: whole turns (stages past the last load nothing and
+        // compute zeros); a guarded tail would be half of the loop here and
+        // measured slower (Q8_0 W_up 11008 x 4096, 4 stages: 28 -> 31 us at
+        // M = 64), and so was one kernel holding both loops
+        const int nit = (nst + D - 1) / D;
+        for (int it = 0; it < nit; ++it) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int j = it * D + d;
+                load(ring[(d + D - 1) % D], j + D - 1);
+                step(d, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -313,8 +347,8 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     }
 }
 
-template <int QT, int MT, int RT, bool PK>
-hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
+template <int QT, int MT, int RT, bool PK, bool TAIL>
+hipError_t launch_cfg_t(const GemmArgs &a, hipStream_t s, const char **name) {
     // register stages in the ring (D - 1 in flight) by activation tiles
     // (measured: deeper rings for one tile lose more to registers than they
     // gain in flight; four tiles leave no room for a third stage)
@@ -323,8 +357,9 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
     constexpr int lds_stage = WPB * Rg::BYTES, lds_part = WPB * RT * MT * 1024;
     constexpr int lds = lds_stage > lds_part ? lds_stage : lds_part;
     static_assert(lds <= 160 * 1024, "LDS budget");
-    static const std::string kname = variant_name("mm%s_q%d_mt%d_rt%d_w%d_d%d", PK ? "p" : "", QT, MT, RT, WPB, D);
-    auto kern = k_mm<QT, MT, RT, WPB, D, PK>;
+    static const std::string kname =
+        variant_name("mm%s_q%d_mt%d_rt%d_w%d_d%d%s", PK ? "p" : "", QT, MT, RT, WPB, D, TAIL ? "_t" : "");
+    auto kern = k_mm<QT, MT, RT, WPB, D, PK, TAIL>;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     const int grid = (a.r1 - a.r0 + 16 * RT - 1) / (16 * RT);
@@ -332,6 +367,17 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
                        PK ? a.pd : a.wd, a.rows, a.K, a.xq, a.xd, a.M, a.r0, a.r1);
     *name = kname.c_str();
     return hipGetLastError();
+}
+
+// The stage loop with a guarded tail for wavefronts of at least 3 ring turns
+// of stages (every wavefront has per or per - 1 stages), whole turns below.
+template <int QT, int MT, int RT, bool PK>
+hipError_t launch_cfg(const GemmArgs &a, hipStream_t s, const char **name) {
+    constexpr int D = MT == 1 ? QMV_MM_D1 : MT == 2 ? QMV_MM_D2 : QMV_MM_D4;
+    constexpr int WPB = (PK && MT == 1) ? QMV_MM_W1 : 8;
+    const int ns = (a.K / 32 + KU - 1) / KU;
+    if (ns / WPB >= 3 * D) return launch_cfg_t<QT, MT, RT, PK, true>(a, s, name);
+    return launch_cfg_t<QT, MT, RT, PK, false>(a, s, name);
 }
 
 template <int QT, int MT, bool PK>
