@@ -193,7 +193,7 @@ k_gs(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 
     // 2. weight offsets of pass 0 and the first pass in flight
     const int prow = lane / T;
-    const int gl = lane % G;              // position in the scale block; this lane scales unit k = gl
+    const int gl = lane % G;              // position in the scale block (the lane of its pairs g = gl)
     const int64_t rb = (int64_t)g0;
     const __amdgpu_buffer_rsrc_t rq = rs::rsrc(wq + rb * row_bytes, (int64_t)rows_here * row_bytes);
     const __amdgpu_buffer_rsrc_t r0s = rs::rsrc(ws0 + rb * nbk, (int64_t)rows_here * nbk * 4);
