@@ -474,10 +474,11 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
 // its own activation row's block, straight into registers.  The Q4_0 offset
 // -8 * sum(qx) seeds the accumulator.  The fp32 scaling is spread over all
 // 64 lanes (4 block sums each), the 4 lanes of a tile share the weight
-// scales through quad permutes, and the 4 tiles of each 16-lane row are
-// added with row-shift DPP adds; the per-row partial sums of the 4 rows of
-// 16 lanes and of the wavefronts are added in LDS in a fixed order.
-constexpr int kMqRwCap = 256;  // rows per workgroup: slice sums [4][WPB][4][rw] in LDS
+// scales through quad permutes, the 4 tiles of each 16-lane row are added
+// with row-shift DPP adds and the 4 rows of 16 lanes with two lane
+// shuffles; the wavefronts' sums are added in LDS in wavefront order, one
+// (weight row, activation row) per thread.
+constexpr int kMqRwCap = 256;  // rows per workgroup: slice sums [4][WPB][rw] in LDS
 
 template <int QT, int NBL, int D, int D0, int WPB>
 __global__ void __launch_bounds__(64 * WPB)
@@ -485,7 +486,7 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
      int32_t M, const int8_t *__restrict__ xq, const float *__restrict__ xd, int32_t r0, int32_t r1, int32_t rw) {
     constexpr int QB = (QT == 8) ? 32 : 16;    // quant bytes per block
     static_assert(D0 >= 0 && D0 <= D - 1, "passes issued before the activation sums");
-    extern __shared__ float s_red[];           // [activation row][wavefront][quarter][rw] partial sums
+    extern __shared__ float s_red[];           // [activation row][wavefront][rw] partial sums
 
     const int nb = K >> 5;
     const int lane = threadIdx.x & 63;
@@ -565,7 +566,7 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     for (int d = D0; d < D - 1; ++d) load(ring[d], d);
 
     // 4. passes: loads of pass j + D - 1 in flight while pass j is computed
-    float *red = s_red + ((i * WPB + wid) * 4 + (lane >> 4)) * rw;
+    float *red = s_red + (i * WPB + wid) * rw;
     const int nit = (npass + D - 1) / D;
     for (int it = 0; it < nit; ++it) {
 #pragma unroll
@@ -611,25 +612,24 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                 // tiles 4 r .. 4 r + 3 of the 16-lane row r: lanes 12 .. 15 end with the sums
                 f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x114, 0xF, 0xF, false));
                 f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x118, 0xF, 0xF, false));
+                // then the four 16-lane rows: (r0 + r1) + (r2 + r3) in every row
+                f[v] += __shfl_xor(f[v], 16);
+                f[v] += __shfl_xor(f[v], 32);
             }
-            if ((lane & 15) >= 12 && j < npass)
+            if (lane >= 12 && lane < 16 && j < npass)
                 *reinterpret_cast<float4 *>(red + 4 * j) = make_float4(f[0], f[1], f[2], f[3]);
         }
     }
 
-    // 5. add the partial sums of each (activation row, weight row): the 4
-    //    rows of 16 lanes of each wavefront, wavefronts in order
+    // 5. add the wavefronts' sums of each (activation row, weight row) in
+    //    wavefront order, one pair per thread
     __syncthreads();
-    for (int r = threadIdx.x; r < rows_here; r += 64 * WPB) {
-        for (int m = 0; m < M; ++m) {
-            float s = 0.0f;
+    for (int e = threadIdx.x; e < rows_here * M; e += 64 * WPB) {  // one (weight row, activation row) per thread
+        const int r = e % rows_here, m = e / rows_here;
+        float s = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WPB; ++w) {
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) s += s_red[((m * WPB + w) * 4 + qq) * rw + r];
-            }
-            y[(size_t)m * rows + g0 + r] = s;
-        }
+        for (int w = 0; w < WPB; ++w) s += s_red[(m * WPB + w) * rw + r];
+        y[(size_t)m * rows + g0 + r] = s;
     }
 }
 
@@ -642,9 +642,9 @@ hipError_t launch_mq_t(const RowsArgs &a, hipStream_t s, const char **name) {
     const int groups = a.num_cu * QMV_FX_WG_PER_CU;
     const int rw = min(kMqRwCap, ((nrows + groups - 1) / groups + 3) / 4 * 4);
     const int grid = (nrows + rw - 1) / rw;
-    const size_t lds = (size_t)4 * WPB * 4 * rw * 4;
+    const size_t lds = (size_t)4 * WPB * rw * 4;
     // the largest size any call of this kernel asks for (rw at its cap)
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), (size_t)4 * WPB * 4 * kMqRwCap * 4);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), (size_t)4 * WPB * kMqRwCap * 4);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, s, a.y, a.wq, a.wd, a.rows, a.K, a.M, a.xq, a.xd,
                        a.r0, a.r1, rw);
