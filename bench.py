@@ -65,6 +65,8 @@ def parse():
                     help="with --q4k-only: comma-separated shape groups (tinyllama_layer, llama7b_ffn); default all")
     ap.add_argument("--zp-only", action="store_true",
                     help="only the 128-block zero-point format measurement (for profiling)")
+    ap.add_argument("--others-only", action="store_true",
+                    help="only the per-call timings of the other configurations (for profiling)")
     ap.add_argument("--batched-only", action="store_true",
                     help="only the M >= 16 matrix-core measurement (one JSON object; for profiling that path)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -121,13 +123,18 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.zp_only or args.q4k_only:
+    if args.zp_only or args.q4k_only or args.others_only:
         import torch
         from block_quantized_decode_amd import qmv
         torch.cuda.set_device(0)
         qmv.qmv_device_check()
         stream = torch.cuda.Stream()
-        res = zp_bench(stream) if args.zp_only else q4k_bench(stream, args.q4k_shapes.split(",") if args.q4k_shapes else None)
+        if args.others_only:
+            res = other_workloads_bench(stream)
+        elif args.zp_only:
+            res = zp_bench(stream)
+        else:
+            res = q4k_bench(stream, args.q4k_shapes.split(",") if args.q4k_shapes else None)
         print(json.dumps(res), flush=True)
         return
     if args.batched_only:
@@ -475,13 +482,14 @@ def _graph_us(calls, stream, reps=20):
 def other_workloads_bench(stream):
     """The other configurations, per call and per layer, through the fused
     entry point (M = 1, float32 activation), timed like the step: graphs of
-    prepared calls.  Weights are random normal draws quantized on the GPU
-    and rotated over copies whose total exceeds the 256 MB last-level cache
-    (TinyLlama layer x 20, Qwen2.5-0.5B FFN + lm_head x 4), so each call
-    streams from HBM; the 256 x 512 parity matrix (147 KB) is timed warm.
-    The TinyLlama layer is also timed with the projections concatenated as
-    the forward pass writes them (W_q|W_k|W_v 2560 x 2048, W_gate|W_up
-    11264 x 2048): 4 launches per layer instead of 7."""
+    prepared calls.  Weights are random normal draws quantized on the GPU.
+    Every timed graph cycles through copies of its matrices totalling more
+    than 600 MB (at least 4), more than the 256 MB last-level cache, so each
+    call streams from HBM: per matrix, the copies of that matrix alone; per
+    layer, whole copies of the layer.  The 256 x 512 parity matrix (147 KB)
+    is timed warm.  The TinyLlama layer is also timed with the projections
+    concatenated as the forward pass writes them (W_q|W_k|W_v 2560 x 2048,
+    W_gate|W_up 11264 x 2048): 4 launches per layer instead of 7."""
     import torch
 
     from block_quantized_decode_amd import qmv, synth
@@ -489,12 +497,19 @@ def other_workloads_bench(stream):
     dev = torch.device("cuda:0")
     torch.manual_seed(5)
     out = {}
+    cold = 600 << 20
 
     def quantized(rows, cols, qtype):
         w = torch.randn(rows, cols, device=dev) * 0.02
         q, d = qmv.qmv_quantize_weights(w, qtype)
         del w
         return q, d
+
+    def nbytes(rows, cols, qtype):
+        return rows * cols // 32 * ((16 if qtype == 4 else 32) + 4)
+
+    def copies_for(total):
+        return max(4, -(-cold // total))
 
     def calls_for(mats, qtype, copies):
         """Per copy: [(name, prepared call, weight bytes)] in matrix order."""
@@ -512,6 +527,19 @@ def other_workloads_bench(stream):
             res.append(row)
         return res
 
+    def per_matrix(mats, qtype):
+        """us per call and weight GB/s of each matrix, over its own cold copies."""
+        us, gbs = {}, {}
+        for m in mats:
+            n = copies_for(nbytes(m[1], m[2], qtype))
+            cs = calls_for([m], qtype, n)
+            t = _graph_us([row[0][1] for row in cs], stream) / n
+            us[m[0]] = round(t, 3)
+            gbs[m[0]] = round(cs[0][0][2] / (t * 1e-6) / 1e9, 1)
+            del cs
+            torch.cuda.empty_cache()
+        return us, gbs
+
     # 256 x 512 Q8_0, warm
     wl = synth.WORKLOADS["q8_256x512"]
     cs = calls_for([(m.name, m.rows, m.cols, m.act) for m in wl.matrices], 8, 1)
@@ -522,13 +550,11 @@ def other_workloads_bench(stream):
     # TinyLlama layer, Q4_0: per matrix, per layer, and concatenated
     wl = synth.WORKLOADS["tinyllama_layer_q4"]
     mats = [(m.name, m.rows, m.cols, m.act) for m in wl.matrices]
-    copies = 20
+    per, _ = per_matrix(mats, 4)
+    lbytes = sum(nbytes(r, c, 4) for _, r, c, _ in mats)
+    copies = copies_for(lbytes)
     cs = calls_for(mats, 4, copies)
-    per = {}
-    for i, (name, *_r) in enumerate(mats):
-        per[name] = round(_graph_us([cs[c][i][1] for c in range(copies)], stream) / copies, 3)
     layer_us = _graph_us([call for row in cs for _, call, _ in row], stream) / copies
-    lbytes = sum(b for _, _, b in cs[0])
     del cs
     torch.cuda.empty_cache()
     cat = [("W_qkv", 2560, 2048, "x_attn"), ("W_o", 2048, 2048, "x_o"), ("W_gate_up", 11264, 2048, "x_ffn"),
@@ -541,25 +567,22 @@ def other_workloads_bench(stream):
                     "layer_weight_gb_s": round(lbytes / (layer_us * 1e-6) / 1e9, 1),
                     "layer_concat_us": round(cat_us, 3), "layer_concat_launches": len(cat),
                     "layer_concat_weight_gb_s": round(lbytes / (cat_us * 1e-6) / 1e9, 1),
-                    "copies": copies}
+                    "layer_copies": copies}
 
     # Qwen2.5-0.5B FFN + lm_head, Q8_0
     wl = synth.WORKLOADS["qwen05b_ffn_lmhead_q8"]
     mats = [(m.name, m.rows, m.cols, m.act) for m in wl.matrices]
-    copies = 4
-    cs = calls_for(mats, 8, copies)
-    per, gbs = {}, {}
-    for i, (name, *_r) in enumerate(mats):
-        us = _graph_us([cs[c][i][1] for c in range(copies)], stream) / copies
-        per[name] = round(us, 3)
-        gbs[name] = round(cs[0][i][2] / (us * 1e-6) / 1e9, 1)
-    ffn_us = _graph_us([cs[c][i][1] for c in range(copies) for i in range(3)], stream) / copies
+    per, gbs = per_matrix(mats, 8)
+    ffn = mats[:3]
+    fbytes = sum(nbytes(r, c, 8) for _, r, c, _ in ffn)
+    copies = copies_for(fbytes)
+    cs = calls_for(ffn, 8, copies)
+    ffn_us = _graph_us([call for row in cs for _, call, _ in row], stream) / copies
     del cs
     torch.cuda.empty_cache()
     out[wl.name] = {"per_matrix_us": per, "per_matrix_weight_gb_s": gbs, "ffn_us": round(ffn_us, 3),
-                    "lm_head_pct_hbm_peak": round(100.0 * gbs["lm_head"] / HBM_PEAK_GBS, 2), "copies": copies}
+                    "lm_head_pct_hbm_peak": round(100.0 * gbs["lm_head"] / HBM_PEAK_GBS, 2), "ffn_copies": copies}
     return out
-
 
 def zp_bench(stream):
     """The exported-model format (128-element blocks with a zero point,

@@ -88,6 +88,18 @@ __device__ __forceinline__ v4i mfma16(v2i a, v2i b, v4i c) {
 // byte offset of 16-byte piece q of row r in a 128-byte-per-row LDS image
 __device__ __forceinline__ int img(int r, int q) { return 128 * r + 16 * (q ^ ((r >> 1) & 7)); }
 
+// The 16 x 16 products dw(4 g + v) * dx(l % 16) for lane l = 16 g + ..., in
+// the accumulator layout of v_mfma_i32_16x16x32_i8 (register v: weight row
+// 4 g + v, activation row l % 16), from one v_mfma_f32_4x4x1_16b_f32: its
+// 16 blocks of 4 x 4 outer products put A of lane 4 j + v times B of lane
+// 4 j + i into register v of lane 4 j + i.  So lane l supplies
+// dw(4 (l / 16) + l % 4) as A and dx(l % 16) as B.  One product per output
+// and a zero accumulator: each value is the rounded product dw * dx.
+__device__ __forceinline__ v4f scale_tile(float dw_lane, float dx_lane) {
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(dw_lane, dx_lane, z, 0, 0, 0);
+}
+
 // One stage in registers (this lane's share of the coalesced loads).
 template <int QT, int MT, int RT>
 struct Stage {
@@ -221,6 +233,11 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     };
 
     const int i16 = lane & 15, g = lane >> 4;
+    // one activation tile: the 16 x 16 scale products dw * dx of a block
+    // come from the matrix core (measured 4% faster at M = 16 on the
+    // Llama-7B FFN matrices); four tiles keep the VALU multiply (no gain
+    // there, and packed Q4_0 W_up at M = 64 was 3% slower)
+    constexpr bool SMF = MT == 1;
     float acc[RT][MT][4];
 #pragma unroll
     for (int a = 0; a < RT; ++a)
@@ -259,12 +276,22 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
                 } else {
                     aw = *reinterpret_cast<const v2i *>(reg + Rg::W + img(16 * a + i16, q) + h);
                 }
-                const v4f dw4 = *reinterpret_cast<const v4f *>(reg + Rg::DW + 4 * (64 * u + 16 * a + 4 * g));
+                // SMF: lane l holds the scale of weight row 4 g + l % 4 (the
+                // f32 instruction's A operand); otherwise the 4 rows 4 g + v
+                const float *dwp = reinterpret_cast<const float *>(reg + Rg::DW) + 64 * u + 16 * a + 4 * g;
+                const float dwl = SMF ? dwp[lane & 3] : 0.0f;
+                const v4f dw4 = SMF ? v4f{} : *reinterpret_cast<const v4f *>(dwp);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     const v4i c = mfma16(aw, b[t], c0[t]);
+                    if constexpr (SMF) {
+                        const v4f sc = scale_tile(dwl, dxv[t]);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[a][t][v] = fmaf((float)c[v], dw4[v] * dxv[t], acc[a][t][v]);
+                        for (int v = 0; v < 4; ++v) acc[a][t][v] = fmaf((float)c[v], sc[v], acc[a][t][v]);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[a][t][v] = fmaf((float)c[v], dw4[v] * dxv[t], acc[a][t][v]);
+                    }
                 }
             }
         }
