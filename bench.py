@@ -865,10 +865,12 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5, ceil=None, sclk_mhz=N
         (measured_cold_cap_*: the best int8 matrix-core loop and the
         per-launch streaming read of env.ceilings);
       * warm: min(measured int8 loop, the fp32 epilogue) -- the kernel
-        spends 3 non-packed VALU operations (convert, scale product, fused
-        multiply-add) per output and block against the block's 64 int8
-        operations, and the VALU does 64 lanes x 256 compute units per
-        clock, so the epilogue caps the rate at 64 / 3 x 64 x 256 x clock."""
+        spends E non-packed VALU operations per output and block against
+        the block's 64 int8 operations, and the VALU does 64 lanes x 256
+        compute units per clock, so the epilogue caps the rate at
+        64 / E x 64 x 256 x clock.  E = 3 (convert, scale product, fused
+        multiply-add) for 17 .. 64 rows; E = 2 for up to 16 rows, where the
+        scale products come from the matrix core."""
     import torch
 
     from block_quantized_decode_amd import qmv, synth
@@ -928,7 +930,8 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5, ceil=None, sclk_mhz=N
                 case.update({"warm_us_per_launch": round(wus, 2), "warm_gop_s": round(wgops, 1),
                              "warm_pct_int8_peak": round(100.0 * wgops / (MFMA_I8_PEAK_TOPS * 1e3), 2)})
                 clock = (sclk_mhz or 2400) * 1e6
-                epi_cap = 64.0 / 3.0 * 64 * 256 * clock / 1e9   # GOP/s
+                epi_valu = 2.0 if m <= 16 else 3.0
+                epi_cap = 64.0 / epi_valu * 64 * 256 * clock / 1e9   # GOP/s
                 case["epilogue_cap_gop_s"] = round(epi_cap, 1)
                 if ceil is not None:
                     mfma = ceil["mfma_i8_best_top_s"] * 1e3
@@ -965,8 +968,8 @@ def batched_bench(dev, name="batched_ffn_q4q8", replays=5, ceil=None, sclk_mhz=N
         "bound_note": "cold: HBM-bound for M <= 64: 2M ops per weight element against 0.625 B (Q4_0) or 1.125 B "
                       "(Q8_0) stays below the chip's 625 op/B ridge (hbm_cap_pct_int8_peak per case; "
                       "measured_cold_cap_gop_s with the measured stream and matrix-core ceilings); warm: the fp32 "
-                      "per-block epilogue (3 VALU per output per block against 64 int8 ops, epilogue_cap_gop_s) "
-                      "caps every case at ~17% of the int8 peak",
+                      "per-block epilogue (3 VALU per output per block against 64 int8 ops, 2 for up to 16 rows, "
+                      "epilogue_cap_gop_s) caps every case at ~17% (~25% for up to 16 rows) of the int8 peak",
         "best_warm_gop_s": max(c["warm_gop_s"] for c in cases),
         "best_warm_pct_int8_peak": max(c["warm_pct_int8_peak"] for c in cases),
         "cases": cases,
