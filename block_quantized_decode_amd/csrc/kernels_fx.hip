@@ -56,7 +56,7 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 // Tuning (measured on the Llama-7B FFN shapes): barrier between the
 // activation and weight requests, one pass of weights issued before the
 // quantization, four passes in the ring, one workgroup of 8 wavefronts
-// per compute unit.
+// per compute unit (4 for some shapes of one activation row: launch_m).
 #ifndef QMV_FX_XBAR
 #define QMV_FX_XBAR 1
 #endif
@@ -691,10 +691,9 @@ constexpr int ring_depth() {
     return (QT == 8 && M * NBL > 6) ? 3 : QMV_FX_D;
 }
 
-template <int QT, int M, int AX>
-hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
+template <int QT, int M, int AX, int W>
+hipError_t launch_m_w(const RowsArgs &a, hipStream_t s, const char **name) {
     constexpr bool FX = AX != kActQ8;
-    constexpr int W = QMV_FX_WPB;
     const int nb = a.K / QK;
     const int S = (nb + W - 1) / W;
     const int nrows = a.r1 - a.r0;
@@ -728,6 +727,25 @@ hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
         if constexpr (M <= 2) return launch_t<QT, M, AX, 16, 4, ring_depth<QT, M, 4>(), W>(a, rows_per(4, true), s, name);
     }
     return hipErrorNotSupported;
+}
+
+// Wavefronts per workgroup for one activation row.  Measured on the MI355X
+// (fused launches, weights streamed from HBM, 4 against 8 wavefronts):
+// 4 (one per SIMD) is faster for whole rows per wavefront (Q8_0 4864 x 896
+// 3.58 -> 3.39 us, 151936 x 896 31.1 -> 30.5 us) and for split-K slices of
+// up to 16 Q4_0 blocks (K = 2048: 0.2 - 0.4 us faster at 256 .. 11264 rows)
+// or 48 Q8_0 blocks (896 x 4864 4.93 -> 4.27 us, 11008 x 4096 12.3 ->
+// 11.9 us); 8 is faster for Q4_0 at K = 4096 (11008 x 4096 7.1 against
+// 7.3 us) and the only split-K form for longer rows.  Q4_0 at K = 5632 and
+// Q8_0 at K = 8192 measured the same either way.
+template <int QT, int M, int AX>
+hipError_t launch_m(const RowsArgs &a, hipStream_t s, const char **name) {
+    if constexpr (M == 1) {
+        const int nb = a.K / QK, S4 = (nb + 3) / 4;
+        if (nb <= 32 || (nb >= 64 && S4 <= (QT == 8 ? 48 : 16)))
+            return launch_m_w<QT, M, AX, 4>(a, s, name);
+    }
+    return launch_m_w<QT, M, AX, QMV_FX_WPB>(a, s, name);
 }
 
 template <int QT>
