@@ -9,10 +9,12 @@
 // What is computed is that of kernels_zp.hip and kernels_q4k.hip (the same
 // integer identities, the same activation quantization, bit for bit); only
 // the work layout differs.  The row-streaming kernels there read whole rows
-// per lane group; on rows of 4096 and more elements this kernel reads them
-// the way the fused Q4_0 / Q8_0 matvec does (measured faster for 4-bit codes
-// on the Llama-7B FFN shapes; for 8-bit zero-point codes the row streaming
-// stays ahead, 11.6 against 11.9 us on W_up 11008 x 4096, and keeps them):
+// per lane group; this kernel reads them the way the fused Q4_0 / Q8_0
+// matvec does, where that was measured faster for 4-bit codes: with 8
+// wavefronts on many rows of 4096 and more elements (the Llama-7B FFN
+// shapes), with 4 on fewer rows (launch rule at the end of this file).  For
+// 8-bit zero-point codes the row streaming stays ahead (11.6 against 11.9 us
+// on W_up 11008 x 4096) and keeps them.
 //
 // One workgroup of WPB wavefronts per compute unit owns a run of rw rows
 // (a multiple of 4); its wavefronts split K: wavefront w owns units
@@ -398,72 +400,99 @@ k_gs(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 constexpr int kGsWpb = 8;
 constexpr int kGsRwCap = 512;  // rows per workgroup: slice sums [WPB][rw] in LDS
 
-template <int FMT, int NC>
+template <int FMT, int NC, int W>
 hipError_t launch_gs_t(float *y, const uint8_t *wq, const float *s0, const float *s1, const uint8_t *zp,
                        const uint8_t *sc, const uint8_t *mn, int zdef, int rows, int K, const float *x,
                        int8_t *xq_out, float *xd_out, int r0, int r1, int S, int num_cu, hipStream_t s,
                        const char **name) {
     constexpr int D = QMV_GS_D;
-    auto kern = k_gs<FMT, NC, D, kGsWpb>;
+    auto kern = k_gs<FMT, NC, D, W>;
     static const std::string kname =
-        variant_name("gs_%s_n%d_d%d_w%d", FMT == kGsZp4 ? "zp4" : "q4k", NC, D, kGsWpb);
+        variant_name("gs_%s_n%d_d%d_w%d", FMT == kGsZp4 ? "zp4" : "q4k", NC, D, W);
     const int nrows = r1 - r0;
     int rw = ((nrows + num_cu - 1) / num_cu + 3) / 4 * 4;
     if (rw > kGsRwCap) rw = kGsRwCap;
     const int grid = (nrows + rw - 1) / rw;
-    const size_t lds = (size_t)kGsWpb * rw * 4;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGsWpb), lds, s, y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x,
+    const size_t lds = (size_t)W * rw * 4;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), lds, s, y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x,
                        xq_out, xd_out, r0, r1, rw, S);
     *name = kname.c_str();
     return hipGetLastError();
 }
 
-// Slice of units per wavefront (a multiple of G), or 0 where this kernel
-// does not take the shape: rows shorter than 16 units per wavefront, fewer
-// than 4 passes of rows per workgroup (measured: the row-streaming kernels
-// are faster on the Qwen2.5-0.5B W_down 896 x 4864 and TinyLlama-1.1B
-// W_down 2048 x 5632 shapes), or slices past 64 units.
-int gs_slice(int K, int G, int nrows, int num_cu) {
+// Slice of units per wavefront (a multiple of G) for W wavefronts per
+// workgroup, or 0 where that form does not take the shape: fewer than 16
+// units per wavefront, or slices past 64 units.
+int gs_slice(int K, int G, int W) {
     const int nu = K / 32;
-    const int nbk = nu / G;
-    const int S = (nbk + kGsWpb - 1) / kGsWpb * G;
-    if (nu < 16 * kGsWpb || S > 64 || nrows < 16 * num_cu) return 0;
-    return S;
+    const int S = (nu / G + W - 1) / W * G;
+    return (nu < 16 * W || S > 64) ? 0 : S;
 }
 
-template <int FMT>
+template <int FMT, int W>
 hipError_t launch_gs_f(float *y, const uint8_t *wq, const float *s0, const float *s1, const uint8_t *zp,
                        const uint8_t *sc, const uint8_t *mn, int zdef, int rows, int K, const float *x,
                        int8_t *xq_out, float *xd_out, int r0, int r1, int S, int num_cu, hipStream_t s,
                        const char **name) {
     switch ((S + 15) / 16) {
-        case 1: return launch_gs_t<FMT, 1>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1, S,
-                                           num_cu, s, name);
-        case 2: return launch_gs_t<FMT, 2>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1, S,
-                                           num_cu, s, name);
-        case 3: return launch_gs_t<FMT, 3>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1, S,
-                                           num_cu, s, name);
-        default: return launch_gs_t<FMT, 4>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1, S,
-                                            num_cu, s, name);
+        case 1: return launch_gs_t<FMT, 1, W>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1,
+                                              S, num_cu, s, name);
+        case 2: return launch_gs_t<FMT, 2, W>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1,
+                                              S, num_cu, s, name);
+        case 3: return launch_gs_t<FMT, 3, W>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1,
+                                              S, num_cu, s, name);
+        default: return launch_gs_t<FMT, 4, W>(y, wq, s0, s1, zp, sc, mn, zdef, rows, K, x, xq_out, xd_out, r0, r1,
+                                               S, num_cu, s, name);
     }
 }
 
 }  // namespace
 
+// Which form takes a shape (measured on the MI355X, weights streamed from
+// HBM): 8 wavefronts for at least 16 passes of 4 rows per compute unit;
+// below that, 4 wavefronts where their slices fit (K-quant 256 x 2048
+// 3.35 -> 2.94 us, 2048 x 2048 3.46 -> 3.32 us, 2048 x 5632 5.57 -> 4.52 us;
+// 4-bit zero point 896 x 4864 4.39 -> 3.90 us, all against the
+// row-streaming kernel); otherwise the row-streaming kernels, which stay
+// ahead with 8 wavefronts on fewer rows and with 4 on more (K-quant
+// 5632 x 2048 4.91 against 5.07 us, Llama-7B W_up 7.3 against 7.9 us).
+template <int FMT>
+int gs_form(int K, int nrows, int num_cu, int *S) {
+    constexpr int G = FMT == kGsZp4 ? 4 : 8;
+    if (nrows >= 16 * num_cu) {
+        *S = gs_slice(K, G, kGsWpb);
+        return *S ? kGsWpb : 0;
+    }
+    *S = gs_slice(K, G, 4);
+    return *S ? 4 : 0;
+}
+
 hipError_t launch_gs_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char **name) {
     if (a.bits != 4 || a.K % 128 != 0 || a.r1 - a.r0 < 1) return hipErrorNotSupported;
-    const int S = gs_slice(a.K, 4, a.r1 - a.r0, num_cu);
-    if (S == 0) return hipErrorNotSupported;
-    return launch_gs_f<kGsZp4>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x, a.xq_out,
-                               a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+    int S = 0;
+    switch (gs_form<kGsZp4>(a.K, a.r1 - a.r0, num_cu, &S)) {
+        case 4:
+            return launch_gs_f<kGsZp4, 4>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x,
+                                          a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case kGsWpb:
+            return launch_gs_f<kGsZp4, kGsWpb>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K,
+                                               a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        default: return hipErrorNotSupported;
+    }
 }
 
 hipError_t launch_gs_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char **name) {
     if (a.K % 256 != 0 || a.r1 - a.r0 < 1) return hipErrorNotSupported;
-    const int S = gs_slice(a.K, 8, a.r1 - a.r0, num_cu);
-    if (S == 0) return hipErrorNotSupported;
-    return launch_gs_f<kGsQ4k>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x, a.xq_out,
-                               a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+    int S = 0;
+    switch (gs_form<kGsQ4k>(a.K, a.r1 - a.r0, num_cu, &S)) {
+        case 4:
+            return launch_gs_f<kGsQ4k, 4>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x,
+                                          a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case kGsWpb:
+            return launch_gs_f<kGsQ4k, kGsWpb>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x,
+                                               a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace qmv

@@ -1,6 +1,8 @@
 """The split-K form of the 4-bit zero-point and K-quant products
-(kernels_gs.hip: rows of at least 128 units of 32 elements and at least 16
-rows per compute unit) on the GPU against the oracle.
+(kernels_gs.hip) on the GPU against the oracle: 8 wavefronts per workgroup
+for rows of at least 128 units of 32 elements and at least 16 rows per
+compute unit, 4 wavefronts for fewer rows of at least 64 units (slices of at
+most 64 units either way).
 
 The activation codes and scales must equal the oracle's bit for bit and
 every row must be within the oracle's tolerance, as for the row-streaming
@@ -46,9 +48,9 @@ def _q4k(w, x, r0=None, r1=None, y=None):
     return host(y), host(qo), host(do), qmv.last_kernel()
 
 
-def _nc(k, g):
-    """Units per lane and pass the launcher picks (8 wavefronts, 16 lanes a row)."""
-    s = -(-(k // 32 // g) // 8) * g
+def _nc(k, g, w=8):
+    """Units per lane and pass the launcher picks (w wavefronts, 16 lanes a row)."""
+    s = -(-(k // 32 // g) // w) * g
     return -(-s // 16)
 
 
@@ -185,3 +187,61 @@ def test_gs_q4k_unit_scales_exact():
     # every partial sum is an integer below 2^24: exact in fp32 in any order
     assert np.all((np.abs(s1) + np.abs(s2)).sum(axis=1) < 2 ** 24)
     assert np.array_equal(y.astype(np.int64), (s1 - s2).sum(axis=1)), kname
+
+
+# Fewer than 16 rows per compute unit: 4 wavefronts, 1 .. 4 units per lane and
+# pass (K = 2048: 1; 4096: 2; 4864 and 5632: 3; 8192: 4), a ragged last pass,
+# a workgroup of fewer rows than a pass, and the most rows below the 8-wavefront form.
+W4_SHAPES = [(3, 2048), (256, 2048), (2048, 2048), (4095, 4096), (896, 4864), (2049, 5632), (1000, 8192)]
+
+
+@pytest.mark.parametrize("fmt", ["zp4", "q4k"])
+@pytest.mark.parametrize("rows,k", W4_SHAPES)
+def test_gs_four_wavefronts(fmt, rows, k):
+    announce(f"gs {fmt} four wavefronts {rows}x{k}")
+    rng = np.random.default_rng(7400 + rows + k)
+    x = _x(rng, k)
+    if fmt == "q4k":
+        w = synth.raw_q4k(rng, rows, k)
+        xq, xd = orc.quantize_q8_b256(x)
+        y, qo, do, kname = _q4k(w, x)
+        worst = check_q4k_all(y, w, xq, xd, what=f"gs q4k {rows}x{k}")
+        y2 = _q4k(w, x)[0]
+    else:
+        wq, wd, wzp = synth.raw_zp(rng, 4, rows, k, True)
+        xq, xd = orc.quantize_q8_b128(x)
+        y, qo, do, kname = _zp(4, wq, wd, wzp, x)
+        worst = check_zp_all(4, y, wq, wd, wzp, xq, xd, what=f"gs zp4 {rows}x{k}")
+        y2 = _zp(4, wq, wd, wzp, x)[0]
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert kname == f"gs_{fmt}_n{_nc(k, 8 if fmt == 'q4k' else 4, 4)}_d4_w4", kname
+    assert np.array_equal(qo, xq) and np.array_equal(do.view(np.uint32), xd.view(np.uint32))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "same inputs, same bits"
+    print(f"  {kname}: max |err| / tol = {worst:.4f}")
+
+
+@pytest.mark.parametrize("fmt", ["zp4", "q4k"])
+def test_gs_four_wavefronts_row_ranges(fmt):
+    """Sub-ranges of a 3001-row matrix (the 4-wavefront form) write exactly
+    their rows."""
+    announce(f"gs four wavefronts row ranges {fmt}")
+    rng = np.random.default_rng(7500)
+    rows, k = 3001, 5632
+    x = _x(rng, k)
+    if fmt == "q4k":
+        w = synth.raw_q4k(rng, rows, k)
+        xq, xd = orc.quantize_q8_b256(x)
+    else:
+        wq, wd, wzp = synth.raw_zp(rng, 4, rows, k, True)
+        xq, xd = orc.quantize_q8_b128(x)
+    for r0, r1 in ((0, rows), (1, 2), (5, 1029), (2990, rows)):
+        ydev = torch.full((rows,), float(SENTINEL), dtype=torch.float32, device="cuda:0")
+        if fmt == "q4k":
+            y, _, _, kname = _q4k(w, x, r0, r1, ydev)
+            check_q4k_all(y, w, xq, xd, r0, r1, what=f"[{r0},{r1})")
+        else:
+            y, _, _, kname = _zp(4, wq, wd, wzp, x, r0, r1, ydev)
+            check_zp_all(4, y, wq, wd, wzp, xq, xd, r0, r1, what=f"[{r0},{r1})")
+        if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+            assert kname.endswith("_w4") and kname.startswith("gs_"), kname
+        assert np.all(y[:r0] == SENTINEL) and np.all(y[r1:] == SENTINEL), f"rows outside [{r0},{r1}) written"

@@ -137,10 +137,11 @@ def test_quantize_b128(k):
 #   - one wavefront per row with two windows per row, the accumulator
 #     carried across items (8-bit K = 16384 and 4-bit K = 32768 at 8192 rows);
 #   - the split-K kernel for 4-bit codes (gs_: n units per lane and pass,
-#     ring depth d, w wavefronts) on the Llama-7B shapes.
+#     ring depth d, w wavefronts) on the Llama-7B shapes (8 wavefronts) and
+#     the Qwen2.5-0.5B W_down (4 wavefronts: fewer rows).
 FULL = [
     (4, 4864, 896, "zp4_l32_j1_d4_p1_w8"), (8, 4864, 896, "zp8_l64_j1_d4_p1_w8"),
-    (4, 896, 4864, "zp4_l64_j1_d4_p4_w16"), (8, 896, 4864, "zp8_l64_j2_d4_p4_w16"),
+    (4, 896, 4864, "gs_zp4_n3_d4_w4"), (8, 896, 4864, "zp8_l64_j2_d4_p4_w16"),
     (4, 151936, 896, "zp4_l32_j1_d4_p1_w8"), (8, 151936, 896, "zp8_l64_j1_d4_p1_w8"),
     (4, 11008, 4096, "gs_zp4_n1_d4_w8"), (8, 11008, 4096, "zp8_l64_j4_d2_p1_w16"),
     (4, 4096, 11008, "gs_zp4_n3_d4_w8"), (8, 4096, 11008, "zp8_l64_j3_d2_p4_w16"),
