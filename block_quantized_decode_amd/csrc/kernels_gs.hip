@@ -449,7 +449,7 @@ hipError_t launch_gs_f(float *y, const uint8_t *wq, const float *s0, const float
 }  // namespace
 
 // Which form takes a shape (measured on the MI355X, weights streamed from
-// HBM): 8 wavefronts for at least 16 passes of 4 rows per compute unit;
+// HBM): 8 wavefronts for at least 16 rows (4 passes of 4) per compute unit;
 // below that, 4 wavefronts where their slices fit (K-quant 256 x 2048
 // 3.35 -> 2.94 us, 2048 x 2048 3.46 -> 3.32 us, 2048 x 5632 5.57 -> 4.52 us;
 // 4-bit zero point 896 x 4864 4.39 -> 3.90 us, all against the
