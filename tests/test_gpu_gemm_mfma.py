@@ -182,17 +182,27 @@ def test_gemm_k_limit(qtype):
             _f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd))
 
 
+ROW_TILE_CASES = [(8187, 256, 20, "mt2_rt2_"), (11000, 512, 64, "mt4_rt3_"), (16387, 128, 33, "mt4_rt4_"),
+                  (10000, 8192, 40, "mt4_rt3_w8_d2_t"), (13000, 8192, 64, "mt4_rt4_w8_d2_t")]
+
+
 @pytest.mark.parametrize("qtype", [4, 8])
-@pytest.mark.parametrize("rows,k,m", [(8187, 256, 20), (11000, 512, 64), (16387, 128, 33)])
-def test_gemm_mfma_row_tiles(qtype, rows, k, m):
+@pytest.mark.parametrize("rows,k,m,form", ROW_TILE_CASES, ids=[f"{r}x{k}-m{m}" for r, k, m, _ in ROW_TILE_CASES])
+def test_gemm_mfma_row_tiles(qtype, rows, k, m, form):
     """Weight-row counts that give a workgroup 2, 3 and 4 tiles of 16 rows
-    (more tiles than compute units), with a ragged last tile; the last case
-    also needs more workgroups than compute units."""
+    (more tiles than compute units), with a ragged last tile; 16387 rows
+    also need more workgroups than compute units.  The last two take the
+    stage loop with a guarded tail at 3 and 4 tiles with four activation
+    tiles, the forms whose registers spill to scratch (the 4-tile one for
+    both formats, the 3-tile one for Q8_0)."""
     announce(f"gemm mfma q{qtype} m={m} rows={rows} k={k}")
     rng = np.random.default_rng(rows + k + m + qtype)
     wq, wd = _weights(rng, qtype, rows, k)
     xq, xd = _act(rng, m, k)
     Y = host(_f(qtype)(dev(wq), dev(wd), dev(xq), dev(xd)))
+    kname = qmv.last_kernel()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert kname.startswith(f"mm_q{qtype}_{form}"), kname
     _check_all(qtype, Y, wq, wd, xq, xd, 0, rows, f"q{qtype} {rows}x{k} m={m}")
 
 
