@@ -82,6 +82,9 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #ifndef QMV_FX_D0_SILU
 #define QMV_FX_D0_SILU 1
 #endif
+#ifndef QMV_FX_SQ  // one 16-byte scale load per lane and pass (see k_fx)
+#define QMV_FX_SQ 1
+#endif
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
@@ -94,6 +97,7 @@ struct Pass {
     static constexpr int QW = (QT == 8) ? 2 : 1;  // 16-byte words per block
     v4i w[NBL][QW];
     float dw[NBL];
+    v4i dq;  // the pass's weight scales, 4 consecutive blocks per lane (see k_fx)
 };
 
 // Sum over aligned groups of T lanes (T a power of two, at most 64): an
@@ -137,10 +141,18 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     static_assert(T * NBL <= 64 && (T * NBL) % 16 == 0, "a slice is at most 64 blocks, loaded 16 blocks at a time");
     static_assert(D0 >= 0 && D0 <= D - 1, "passes issued before the quantization");
     static_assert(!FX || M == 1, "the fused form takes one float32 activation row");
-    static_assert(M * WPB * 64 * 40 + (KS ? M * WPB * rw_cap(M) * 4 : 0) <= 163840, "LDS of one compute unit");
+    // SQ: slices of 2 or more blocks per lane fetch a pass's weight scales
+    // with one 16-byte load per lane (lane l: row l / 16 of the pass, blocks
+    // 4 (l % 16) .. + 3 of the slice) instead of one 4-byte load per block,
+    // and redistribute them through a private 1 KiB LDS slot: the same bytes
+    // in a third of the load instructions, where the LDS allows
+    constexpr int LDS0 = M * WPB * 64 * 40 + (KS ? M * WPB * rw_cap(M) * 4 : 0);
+    constexpr bool SQ = QMV_FX_SQ && KS && NBL >= 2 && T == 16 && LDS0 + WPB * 1024 <= 163840;
+    static_assert(LDS0 + (SQ ? WPB * 1024 : 0) <= 163840, "LDS of one compute unit");
     __shared__ v4i s_lo[M][WPB][64], s_hi[M][WPB][64];
     __shared__ float s_dx[M][WPB][64];
     __shared__ int s_sx[M][WPB][64];
+    __shared__ float s_dq[SQ ? WPB : 1][SQ ? 256 : 1];  // SQ: [row of the pass][block of the slice]
     __shared__ float s_bs[AX == kActRms ? 64 * WPB : 1];  // rmsnorm: sums of squares per block
     extern __shared__ float s_red[];           // [M][WPB][rw] slice sums
 
@@ -230,6 +242,7 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
         od[k] = ok ? ((pfirst * PASS + prow) * nb + kb0 + c) * 4 : kOOB;
     }
     const int pq = pstride * PASS * nb * QB, pd = pstride * PASS * nb * 4;  // bytes per pass of this wavefront
+    const int od4 = 4 * (lane % 16) < ns ? ((pfirst * PASS + prow) * nb + kb0 + 4 * (lane % 16)) * 4 : kOOB;
     auto load = [&](Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
         const bool up = GU && j >= nph;
 #pragma unroll
@@ -239,8 +252,12 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
             p.w[k][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a, 0, kNT));
             if constexpr (QT == 8)
                 p.w[k][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a + 16, 0, kNT));
-            p.dw[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, b, 0, kNT));
+            if constexpr (!SQ)
+                p.dw[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, b, 0, kNT));
         }
+        if constexpr (SQ)  // a quad may reach past the slice: the pass loop zeroes those scales
+            p.dq = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rd, od4 + j * pd + (up ? skipd : 0),
+                                                                                 0, kNT));
     };
     Pass<QT, NBL> ring[D];
 #pragma unroll
@@ -378,6 +395,21 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
             const int j = it * D + d;
             load(ring[(d + D - 1) % D], j + D - 1);
             const Pass<QT, NBL> &p = ring[d];
+            float dwk[NBL];
+            if constexpr (SQ) {
+                // lane l's 4 scales go to floats 4 l .. 4 l + 3 of the slot, that is
+                // row l / 16, blocks 4 (l % 16) ..; each lane then reads its own
+                // (a wavefront's LDS operations run in order); scales past the
+                // slice (other slices' or the next row's) are taken as 0, the
+                // value the 4-byte loads' out-of-range offsets return
+                *reinterpret_cast<v4i *>(&s_dq[wid][4 * lane]) = p.dq;
+#pragma unroll
+                for (int k = 0; k < NBL; ++k)
+                    dwk[k] = lane % 16 + 16 * k < ns ? s_dq[wid][64 * prow + lane % 16 + 16 * k] : 0.0f;
+            } else {
+#pragma unroll
+                for (int k = 0; k < NBL; ++k) dwk[k] = p.dw[k];
+            }
             float a[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) a[m] = 0.0f;
@@ -401,7 +433,7 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                         s = dot4(h1, xh[m][k].y, s);
                         s = dot4(h2, xh[m][k].z, s);
                         s = dot4(h3, xh[m][k].w, s);
-                        a[m] = fmaf((float)s, p.dw[k] * dx[m][k], a[m]);
+                        a[m] = fmaf((float)s, dwk[k] * dx[m][k], a[m]);
                     }
                 } else {
 #pragma unroll
@@ -414,7 +446,7 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                         s = dot4(p.w[k][1].y, xh[m][k].y, s);
                         s = dot4(p.w[k][1].z, xh[m][k].z, s);
                         s = dot4(p.w[k][1].w, xh[m][k].w, s);
-                        a[m] = fmaf((float)s, p.dw[k] * dx[m][k], a[m]);
+                        a[m] = fmaf((float)s, dwk[k] * dx[m][k], a[m]);
                     }
                 }
             }
