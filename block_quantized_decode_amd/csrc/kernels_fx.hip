@@ -25,9 +25,10 @@
 // cannot yet accept; so each wavefront first issues its activation loads,
 // then only the first D - 1 passes of weights, prepares the activation
 // while those are in flight, and then runs a software pipeline over passes:
-// issue the loads of pass j + D - 1, then compute pass j.  A wavefront
-// stalled at a load leaves the vector ALU to the others.  Each weight block
-// in registers serves all M activation rows.
+// issue the loads of pass j + D - 1, then compute pass j, and no loads for
+// passes past its last.  A wavefront stalled at a load leaves the vector ALU
+// to the others.  Each weight block in registers serves all M activation
+// rows.
 //
 // A pass is 64 / T rows: lane l takes row l / T of the pass and the blocks
 // c = l % T + T k (k < NBL) of its wavefront's slice, so each group of T
@@ -41,8 +42,8 @@
 // Loads use raw buffer descriptors whose range covers only this
 // workgroup's rows, and every variable part of an address is in the
 // per-lane offset, which the hardware range-checks: rows past r1, blocks
-// past the slice and passes past the last read zeros without touching
-// memory.
+// past the slice and, for wavefronts of fewer than D - 1 passes, the first
+// passes' loads past the last read zeros without touching memory.
 #include "device_common.h"
 #include "launch.h"
 
@@ -52,6 +53,24 @@ namespace {
 constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3: raw 32-bit data
 constexpr int kNT = 2;                 // non-temporal: weights are read once
 constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor range used here
+
+// Calls f(Int<R>{}) for the R in [1, RMAX] equal to the wave-uniform r (no
+// call for r outside): the last passes of a wavefront run as straight-line
+// code specialised on their count, so that loads are issued only for passes
+// that exist and every wait for a pass's loads is exact.
+template <int V>
+struct Int {
+    static constexpr int value = V;
+};
+template <int R, int RMAX, class F>
+__device__ __forceinline__ void with_count(int r, F &&f) {
+    if constexpr (R <= RMAX) {
+        if (r == R)
+            f(Int<R>{});
+        else
+            with_count<R + 1, RMAX>(r, f);
+    }
+}
 
 // Tuning (measured on the Llama-7B FFN shapes): barrier between the
 // activation and weight requests, one pass of weights issued before the
@@ -84,6 +103,9 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #endif
 #ifndef QMV_FX_SQ  // one 16-byte scale load per lane and pass (see k_fx)
 #define QMV_FX_SQ 1
+#endif
+#ifndef QMV_FX_TAIL  // 1: no loads past a wavefront's last pass (see k_fx); 0: whole ring turns
+#define QMV_FX_TAIL 1
 #endif
 
 
@@ -388,81 +410,110 @@ k_fx(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
     for (int d = D0; d < D - 1; ++d) load(ring[d], d);
 
     // 4. passes: loads of pass j + D - 1 in flight while pass j is computed
+    auto step = [&](const Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
+        float dwk[NBL];
+        if constexpr (SQ) {
+            // lane l's 4 scales go to floats 4 l .. 4 l + 3 of the slot, that is
+            // row l / 16, blocks 4 (l % 16) ..; each lane then reads its own
+            // (a wavefront's LDS operations run in order); scales past the
+            // slice (other slices' or the next row's) are taken as 0, the
+            // value the 4-byte loads' out-of-range offsets return
+            *reinterpret_cast<v4i *>(&s_dq[wid][4 * lane]) = p.dq;
+#pragma unroll
+            for (int k = 0; k < NBL; ++k)
+                dwk[k] = lane % 16 + 16 * k < ns ? s_dq[wid][64 * prow + lane % 16 + 16 * k] : 0.0f;
+        } else {
+#pragma unroll
+            for (int k = 0; k < NBL; ++k) dwk[k] = p.dw[k];
+        }
+        float a[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) a[m] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) {
+            if constexpr (QT == 4) {
+                // byte j of the 16: low nibble = element j, high nibble = element j + 16
+                const unsigned mk = 0x0F0F0F0Fu;
+                const v4i w = p.w[k][0];
+                const int l0 = (unsigned)w.x & mk, l1 = (unsigned)w.y & mk;
+                const int l2 = (unsigned)w.z & mk, l3 = (unsigned)w.w & mk;
+                const int h0 = ((unsigned)w.x >> 4) & mk, h1 = ((unsigned)w.y >> 4) & mk;
+                const int h2 = ((unsigned)w.z >> 4) & mk, h3 = ((unsigned)w.w >> 4) & mk;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    int s = dot4(l0, xl[m][k].x, sx[m][k]);  // starts at -8 * sum(qx)
+                    s = dot4(l1, xl[m][k].y, s);
+                    s = dot4(l2, xl[m][k].z, s);
+                    s = dot4(l3, xl[m][k].w, s);
+                    s = dot4(h0, xh[m][k].x, s);
+                    s = dot4(h1, xh[m][k].y, s);
+                    s = dot4(h2, xh[m][k].z, s);
+                    s = dot4(h3, xh[m][k].w, s);
+                    a[m] = fmaf((float)s, dwk[k] * dx[m][k], a[m]);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    int s = dot4(p.w[k][0].x, xl[m][k].x, 0);
+                    s = dot4(p.w[k][0].y, xl[m][k].y, s);
+                    s = dot4(p.w[k][0].z, xl[m][k].z, s);
+                    s = dot4(p.w[k][0].w, xl[m][k].w, s);
+                    s = dot4(p.w[k][1].x, xh[m][k].x, s);
+                    s = dot4(p.w[k][1].y, xh[m][k].y, s);
+                    s = dot4(p.w[k][1].z, xh[m][k].z, s);
+                    s = dot4(p.w[k][1].w, xh[m][k].w, s);
+                    a[m] = fmaf((float)s, dwk[k] * dx[m][k], a[m]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float t = group_sum<T>(a[m]);
+            if constexpr (KS) {
+                const int r = j * PASS + prow;
+                if (lane % T == T - 1 && j < npass && r < rws) s_red[(m * WPB + wid) * rws + r] = t;
+            } else {  // whole rows: store directly
+                const int r = (j * pstride + pfirst) * PASS + prow;
+                if (lane % T == T - 1 && j < npass && r < rows_here) y[(size_t)m * rows + g0 + r] = t;
+            }
+        }
+    };
+#if QMV_FX_TAIL
+    // Ring turns whose loads all fall among the wavefront's passes run as a
+    // loop; the remaining R passes (1 .. 2 D - 2, the first D - 1 of them
+    // already in the ring) run as straight-line code specialised on R that
+    // loads only passes that exist.  Range-checked loads past the last pass
+    // read nothing but still take the per-CU address path, which the
+    // multi-block slices keep full; a per-pass test instead of the
+    // specialisation makes the compiler's waits for the ring inexact.
+    int it = 0;
+    for (; (it + 2) * D - 2 < npass; ++it) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int j = it * D + d;
+            load(ring[(d + D - 1) % D], j + D - 1);
+            step(ring[d], j);
+        }
+    }
+    with_count<1, 2 * D - 2>(npass - it * D, [&](auto rc) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            if (q + D - 1 < R) load(ring[(q + D - 1) % D], it * D + q + D - 1);
+            step(ring[q % D], it * D + q);
+        }
+    });
+#else
     const int nit = (npass + D - 1) / D;
     for (int it = 0; it < nit; ++it) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int j = it * D + d;
             load(ring[(d + D - 1) % D], j + D - 1);
-            const Pass<QT, NBL> &p = ring[d];
-            float dwk[NBL];
-            if constexpr (SQ) {
-                // lane l's 4 scales go to floats 4 l .. 4 l + 3 of the slot, that is
-                // row l / 16, blocks 4 (l % 16) ..; each lane then reads its own
-                // (a wavefront's LDS operations run in order); scales past the
-                // slice (other slices' or the next row's) are taken as 0, the
-                // value the 4-byte loads' out-of-range offsets return
-                *reinterpret_cast<v4i *>(&s_dq[wid][4 * lane]) = p.dq;
-#pragma unroll
-                for (int k = 0; k < NBL; ++k)
-                    dwk[k] = lane % 16 + 16 * k < ns ? s_dq[wid][64 * prow + lane % 16 + 16 * k] : 0.0f;
-            } else {
-#pragma unroll
-                for (int k = 0; k < NBL; ++k) dwk[k] = p.dw[k];
-            }
-            float a[M];
-#pragma unroll
-            for (int m = 0; m < M; ++m) a[m] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NBL; ++k) {
-                if constexpr (QT == 4) {
-                    // byte j of the 16: low nibble = element j, high nibble = element j + 16
-                    const unsigned mk = 0x0F0F0F0Fu;
-                    const v4i w = p.w[k][0];
-                    const int l0 = (unsigned)w.x & mk, l1 = (unsigned)w.y & mk;
-                    const int l2 = (unsigned)w.z & mk, l3 = (unsigned)w.w & mk;
-                    const int h0 = ((unsigned)w.x >> 4) & mk, h1 = ((unsigned)w.y >> 4) & mk;
-                    const int h2 = ((unsigned)w.z >> 4) & mk, h3 = ((unsigned)w.w >> 4) & mk;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        int s = dot4(l0, xl[m][k].x, sx[m][k]);  // starts at -8 * sum(qx)
-                        s = dot4(l1, xl[m][k].y, s);
-                        s = dot4(l2, xl[m][k].z, s);
-                        s = dot4(l3, xl[m][k].w, s);
-                        s = dot4(h0, xh[m][k].x, s);
-                        s = dot4(h1, xh[m][k].y, s);
-                        s = dot4(h2, xh[m][k].z, s);
-                        s = dot4(h3, xh[m][k].w, s);
-                        a[m] = fmaf((float)s, dwk[k] * dx[m][k], a[m]);
-                    }
-                } else {
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        int s = dot4(p.w[k][0].x, xl[m][k].x, 0);
-                        s = dot4(p.w[k][0].y, xl[m][k].y, s);
-                        s = dot4(p.w[k][0].z, xl[m][k].z, s);
-                        s = dot4(p.w[k][0].w, xl[m][k].w, s);
-                        s = dot4(p.w[k][1].x, xh[m][k].x, s);
-                        s = dot4(p.w[k][1].y, xh[m][k].y, s);
-                        s = dot4(p.w[k][1].z, xh[m][k].z, s);
-                        s = dot4(p.w[k][1].w, xh[m][k].w, s);
-                        a[m] = fmaf((float)s, dwk[k] * dx[m][k], a[m]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float t = group_sum<T>(a[m]);
-                if constexpr (KS) {
-                    const int r = j * PASS + prow;
-                    if (lane % T == T - 1 && j < npass && r < rws) s_red[(m * WPB + wid) * rws + r] = t;
-                } else {  // whole rows: store directly
-                    const int r = (j * pstride + pfirst) * PASS + prow;
-                    if (lane % T == T - 1 && j < npass && r < rows_here) y[(size_t)m * rows + g0 + r] = t;
-                }
-            }
+            step(ring[d], j);
         }
     }
+#endif
 
     if constexpr (!KS) return;
     // 5. add the wavefronts' slice sums of each row in wavefront order
@@ -599,59 +650,82 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
 
     // 4. passes: loads of pass j + D - 1 in flight while pass j is computed
     float *red = s_red + (i * WPB + wid) * rw;
+    auto step = [&](const Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
+        v4i acc[NBL];
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) acc[k] = (v4i){sx[k], sx[k], sx[k], sx[k]};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+#pragma unroll
+            for (int k = 0; k < NBL; ++k) {
+                int a;
+                if constexpr (QT == 4) {
+                    // byte j of the 16: low nibble = element j, high nibble = element j + 16
+                    const unsigned w = (unsigned)p.w[k][0][h & 3];
+                    a = (int)((h < 4 ? w : w >> 4) & 0x0F0F0F0Fu);
+                } else {
+                    a = p.w[k][h >> 2][h & 3];
+                }
+                const int b = h < 4 ? xlo[k][h] : xhi[k][h - 4];
+                acc[k] = __builtin_amdgcn_mfma_i32_4x4x4i8(a, b, acc[k], 0, 0, 0);
+            }
+        }
+        float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) {
+            const int dwi = __float_as_int(p.dw[k]);
+            // weight scale of row v of the tile: lane 4 t + v's (quad_perm [v, v, v, v])
+            const float w0 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x00, 0xF, 0xF, false));
+            const float w1 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x55, 0xF, 0xF, false));
+            const float w2 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0xAA, 0xF, 0xF, false));
+            const float w3 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0xFF, 0xF, 0xF, false));
+            f[0] = fmaf((float)acc[k][0], w0 * dx[k], f[0]);
+            f[1] = fmaf((float)acc[k][1], w1 * dx[k], f[1]);
+            f[2] = fmaf((float)acc[k][2], w2 * dx[k], f[2]);
+            f[3] = fmaf((float)acc[k][3], w3 * dx[k], f[3]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            // tiles 4 r .. 4 r + 3 of the 16-lane row r: lanes 12 .. 15 end with the sums
+            f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x114, 0xF, 0xF, false));
+            f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x118, 0xF, 0xF, false));
+            // then the four 16-lane rows: (r0 + r1) + (r2 + r3) in every row
+            f[v] += __shfl_xor(f[v], 16);
+            f[v] += __shfl_xor(f[v], 32);
+        }
+        if (lane >= 12 && lane < 16 && j < npass)
+            *reinterpret_cast<float4 *>(red + 4 * j) = make_float4(f[0], f[1], f[2], f[3]);
+    };
+#if QMV_FX_TAIL
+    // whole ring turns, then the last passes specialised on their count (as in k_fx)
+    int it = 0;
+    for (; (it + 2) * D - 2 < npass; ++it) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int j = it * D + d;
+            load(ring[(d + D - 1) % D], j + D - 1);
+            step(ring[d], j);
+        }
+    }
+    with_count<1, 2 * D - 2>(npass - it * D, [&](auto rc) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            if (q + D - 1 < R) load(ring[(q + D - 1) % D], it * D + q + D - 1);
+            step(ring[q % D], it * D + q);
+        }
+    });
+#else
     const int nit = (npass + D - 1) / D;
     for (int it = 0; it < nit; ++it) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int j = it * D + d;
             load(ring[(d + D - 1) % D], j + D - 1);
-            const Pass<QT, NBL> &p = ring[d];
-            v4i acc[NBL];
-#pragma unroll
-            for (int k = 0; k < NBL; ++k) acc[k] = (v4i){sx[k], sx[k], sx[k], sx[k]};
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-#pragma unroll
-                for (int k = 0; k < NBL; ++k) {
-                    int a;
-                    if constexpr (QT == 4) {
-                        // byte j of the 16: low nibble = element j, high nibble = element j + 16
-                        const unsigned w = (unsigned)p.w[k][0][h & 3];
-                        a = (int)((h < 4 ? w : w >> 4) & 0x0F0F0F0Fu);
-                    } else {
-                        a = p.w[k][h >> 2][h & 3];
-                    }
-                    const int b = h < 4 ? xlo[k][h] : xhi[k][h - 4];
-                    acc[k] = __builtin_amdgcn_mfma_i32_4x4x4i8(a, b, acc[k], 0, 0, 0);
-                }
-            }
-            float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k = 0; k < NBL; ++k) {
-                const int dwi = __float_as_int(p.dw[k]);
-                // weight scale of row v of the tile: lane 4 t + v's (quad_perm [v, v, v, v])
-                const float w0 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x00, 0xF, 0xF, false));
-                const float w1 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x55, 0xF, 0xF, false));
-                const float w2 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0xAA, 0xF, 0xF, false));
-                const float w3 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0xFF, 0xF, 0xF, false));
-                f[0] = fmaf((float)acc[k][0], w0 * dx[k], f[0]);
-                f[1] = fmaf((float)acc[k][1], w1 * dx[k], f[1]);
-                f[2] = fmaf((float)acc[k][2], w2 * dx[k], f[2]);
-                f[3] = fmaf((float)acc[k][3], w3 * dx[k], f[3]);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                // tiles 4 r .. 4 r + 3 of the 16-lane row r: lanes 12 .. 15 end with the sums
-                f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x114, 0xF, 0xF, false));
-                f[v] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[v]), 0x118, 0xF, 0xF, false));
-                // then the four 16-lane rows: (r0 + r1) + (r2 + r3) in every row
-                f[v] += __shfl_xor(f[v], 16);
-                f[v] += __shfl_xor(f[v], 32);
-            }
-            if (lane >= 12 && lane < 16 && j < npass)
-                *reinterpret_cast<float4 *>(red + 4 * j) = make_float4(f[0], f[1], f[2], f[3]);
+            step(ring[d], j);
         }
     }
+#endif
 
     // 5. add the wavefronts' sums of each (activation row, weight row) in
     //    wavefront order, one pair per thread
