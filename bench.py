@@ -92,7 +92,7 @@ def copy_calibration():
 
 # The sources the timed kernel (the split-K fused matvec) is compiled from:
 # the kernel file and every header it includes.
-TIMED_KERNEL_SOURCES = ("device_common.h", "launch.h", "kernels_fx.hip")
+TIMED_KERNEL_SOURCES = ("count.h", "device_common.h", "launch.h", "kernels_fx.hip")
 
 
 def kernel_source_sha() -> str:

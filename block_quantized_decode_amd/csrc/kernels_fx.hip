@@ -44,6 +44,7 @@
 // per-lane offset, which the hardware range-checks: rows past r1, blocks
 // past the slice and, for wavefronts of fewer than D - 1 passes, the first
 // passes' loads past the last read zeros without touching memory.
+#include "count.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -53,24 +54,6 @@ namespace {
 constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3: raw 32-bit data
 constexpr int kNT = 2;                 // non-temporal: weights are read once
 constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor range used here
-
-// Calls f(Int<R>{}) for the R in [1, RMAX] equal to the wave-uniform r (no
-// call for r outside): the last passes of a wavefront run as straight-line
-// code specialised on their count, so that loads are issued only for passes
-// that exist and every wait for a pass's loads is exact.
-template <int V>
-struct Int {
-    static constexpr int value = V;
-};
-template <int R, int RMAX, class F>
-__device__ __forceinline__ void with_count(int r, F &&f) {
-    if constexpr (R <= RMAX) {
-        if (r == R)
-            f(Int<R>{});
-        else
-            with_count<R + 1, RMAX>(r, f);
-    }
-}
 
 // Tuning (measured on the Llama-7B FFN shapes): barrier between the
 // activation and weight requests, one pass of weights issued before the

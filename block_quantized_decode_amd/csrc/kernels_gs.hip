@@ -44,6 +44,7 @@
 // Loads use raw buffer descriptors covering this workgroup's rows only; every
 // variable part of an address is in the range-checked offset, so rows past
 // r1, units past the slice and passes past the last read zeros.
+#include "count.h"
 #include "launch.h"
 #include "rowstream.h"
 
@@ -57,6 +58,9 @@ using rs::v4i;
 #endif
 #ifndef QMV_GS_D0  // passes issued before the activation work
 #define QMV_GS_D0 1
+#endif
+#ifndef QMV_GS_TAIL  // 1: the last passes specialised on their count; 0: tested per pass
+#define QMV_GS_TAIL 1
 #endif
 
 constexpr int kOff = 0x40000000;  // an offset beyond every range here, with room for pass strides
@@ -374,15 +378,32 @@ k_gs(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             compute(ring[d], mcur, j, d);
         }
     }
-    for (; it * D < npass; ++it) {
-        mcur = mnxt;
+    // The remaining R passes (1 .. 2 D - 2, the first D - 1 of them in the
+    // ring; at most two turns' scales): as code specialised on R, which keeps
+    // the waits for the ring exact, where that measured faster (8 wavefronts,
+    // and 4-bit zero-point codes); else one or two turns testing each pass.
+    if constexpr (QMV_GS_TAIL && (WPB == 8 || FMT == kGsZp4)) {
+        with_count<1, 2 * D - 2>(npass - it * D, [&](auto rc) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int j = it * D + d;
-            if (j < npass) {  // (wave-uniform)
-                if (j + D - 1 < npass) load(ring[(d + D - 1) % D], j + D - 1);
-                if (d == 1 && (it + 1) * D < npass) load_meta(mnxt, it + 1);
-                compute(ring[d], mcur, j, d);
+            for (int q = 0; q < R; ++q) {
+                if (q % D == 0) mcur = mnxt;
+                if (q + D - 1 < R) load(ring[(q + D - 1) % D], it * D + q + D - 1);
+                if (q == 1 && R > D) load_meta(mnxt, it + 1);
+                compute(ring[q % D], mcur, it * D + q, q % D);
+            }
+        });
+    } else {
+        for (; it * D < npass; ++it) {
+            mcur = mnxt;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int j = it * D + d;
+                if (j < npass) {  // (wave-uniform)
+                    if (j + D - 1 < npass) load(ring[(d + D - 1) % D], j + D - 1);
+                    if (d == 1 && (it + 1) * D < npass) load_meta(mnxt, it + 1);
+                    compute(ring[d], mcur, j, d);
+                }
             }
         }
     }
