@@ -47,6 +47,7 @@
 #include <stdio.h>
 
 #include "launch.h"
+#include "count.h"
 #include "rowstream.h"
 
 namespace qmv {
@@ -266,6 +267,37 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 
     // ---- phase B: the rows
     const int items = map.items;
+#if QMV_RS_TAIL
+    // whole ring turns while every load of the turn is one of this
+    // wavefront's items, then the remaining R items (1 .. 2 D - 2) as code
+    // specialised on R: no loads past the last item, exact waits
+    int t0 = 0;
+    for (; t0 + 2 * D - 2 < items; t0 += D) {
+        if constexpr (IB) {
+            cur = nxt;
+            nxt = load_sc(t0 + D);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load(ring[(d + D - 1) % D], t0 + d + D - 1);
+            compute(ring[d], t0 + d, cur, d);
+        }
+    }
+    with_count<1, 2 * D - 2>(items - t0, [&](auto rc) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            if constexpr (IB) {
+                if (q % D == 0) {
+                    cur = nxt;
+                    if (q + D < R) nxt = load_sc(t0 + q + D);
+                }
+            }
+            if (q + D - 1 < R) load(ring[(q + D - 1) % D], t0 + q + D - 1);
+            compute(ring[q % D], t0 + q, cur, q % D);
+        }
+    });
+#else
     for (int t0 = 0; t0 < items; t0 += D) {
         if constexpr (IB) {
             cur = nxt;
@@ -280,6 +312,7 @@ k_zp(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
             }
         }
     }
+#endif
     if constexpr (P > 1) {
         __syncthreads();
         for (int li = threadIdx.x; li < map.rows_here; li += 64 * WPB) {

@@ -20,6 +20,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef QMV_RS_TAIL  // 1: the last items specialised on their count; 0: whole ring turns, tested per item
+#define QMV_RS_TAIL 1
+#endif
+
 namespace qmv {
 namespace rs {
 
