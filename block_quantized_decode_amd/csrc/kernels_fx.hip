@@ -71,6 +71,9 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #ifndef QMV_FX_D
 #define QMV_FX_D 4
 #endif
+#ifndef QMV_FX_D3_NBL  // slices of at least this many blocks per lane take a ring of 3
+#define QMV_FX_D3_NBL 2
+#endif
 #ifndef QMV_FX_WG_PER_CU
 #define QMV_FX_WG_PER_CU 1
 #endif
@@ -743,12 +746,13 @@ hipError_t launch_mq_t(const RowsArgs &a, hipStream_t s, const char **name) {
 
 template <int QT>
 hipError_t launch_mq(const RowsArgs &a, hipStream_t s, const char **name) {
-    constexpr int W = QMV_FX_WPB, D = QMV_FX_D;
+    // ring depth as ring_depth: 4 for one block per lane, 3 for more
+    constexpr int W = QMV_FX_WPB, D = QMV_FX_D, DN = QMV_FX_D3_NBL <= 2 ? 3 : D;
     const int S = (a.K / QK + W - 1) / W;
     if (S <= 16) return launch_mq_t<QT, 1, D, W>(a, s, name);
-    if (S <= 32) return launch_mq_t<QT, 2, D, W>(a, s, name);
-    if (S <= 48) return launch_mq_t<QT, 3, D, W>(a, s, name);
-    return launch_mq_t<QT, 4, D, W>(a, s, name);
+    if (S <= 32) return launch_mq_t<QT, 2, DN, W>(a, s, name);
+    if (S <= 48) return launch_mq_t<QT, 3, DN, W>(a, s, name);
+    return launch_mq_t<QT, 4, DN, W>(a, s, name);
 }
 
 template <int QT, int M, int AX, int T, int NBL, int D, int WPB, bool KS = true, bool GU = false>
@@ -773,11 +777,14 @@ hipError_t launch_t(const RowsArgs &a, int rw, hipStream_t s, const char **name)
     return hipGetLastError();
 }
 
-// Ring depth: four passes in flight, three where the activation registers
-// of several rows leave no room for a fourth (Q8_0 with M * NBL > 6).
+// Ring depth: four passes in flight for slices of one block per lane, three
+// for slices of several blocks per lane (measured faster there: Llama-7B
+// W_down 9.45 -> 9.30 us, TinyLlama W_down 3.94 -> 3.73 us; each of their
+// passes already carries 2 - 4 loads per lane) and where the activation
+// registers of several rows leave no room for a fourth (Q8_0 with M * NBL > 6).
 template <int QT, int M, int NBL>
 constexpr int ring_depth() {
-    return (QT == 8 && M * NBL > 6) ? 3 : QMV_FX_D;
+    return (NBL >= QMV_FX_D3_NBL || (QT == 8 && M * NBL > 6)) ? 3 : QMV_FX_D;
 }
 
 template <int QT, int M, int AX, int W>
