@@ -56,6 +56,9 @@ using rs::v4i;
 #ifndef QMV_GS_D  // ring depth (passes in registers)
 #define QMV_GS_D 4
 #endif
+#ifndef QMV_GS_D3_NC  // K-quant units per lane from which the ring is 3 deep
+#define QMV_GS_D3_NC 2
+#endif
 #ifndef QMV_GS_D0  // passes issued before the activation work
 #define QMV_GS_D0 1
 #endif
@@ -426,7 +429,11 @@ hipError_t launch_gs_t(float *y, const uint8_t *wq, const float *s0, const float
                        const uint8_t *sc, const uint8_t *mn, int zdef, int rows, int K, const float *x,
                        int8_t *xq_out, float *xd_out, int r0, int r1, int S, int num_cu, hipStream_t s,
                        const char **name) {
-    constexpr int D = QMV_GS_D;
+    // 3 passes in flight for K-quant slices of several units per lane (each
+    // unit of a pass also loads its scale and minimum bytes), 4 otherwise:
+    // measured K-quant Llama W_down 8.03 -> 7.69 us, TinyLlama W_down
+    // 4.49 -> 4.37 us; 4-bit zero points kept 4 (equal or 0.4% slower with 3)
+    constexpr int D = (FMT == kGsQ4k && NC >= QMV_GS_D3_NC) ? 3 : QMV_GS_D;
     auto kern = k_gs<FMT, NC, D, W>;
     static const std::string kname =
         variant_name("gs_%s_n%d_d%d_w%d", FMT == kGsZp4 ? "zp4" : "q4k", NC, D, W);

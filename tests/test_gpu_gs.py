@@ -214,7 +214,8 @@ def test_gs_four_wavefronts(fmt, rows, k):
         worst = check_zp_all(4, y, wq, wd, wzp, xq, xd, what=f"gs zp4 {rows}x{k}")
         y2 = _zp(4, wq, wd, wzp, x)[0]
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert kname == f"gs_{fmt}_n{_nc(k, 8 if fmt == 'q4k' else 4, 4)}_d4_w4", kname
+        nc = _nc(k, 8 if fmt == 'q4k' else 4, 4)
+        assert kname == f"gs_{fmt}_n{nc}_d{3 if fmt == 'q4k' and nc >= 2 else 4}_w4", kname
     assert np.array_equal(qo, xq) and np.array_equal(do.view(np.uint32), xd.view(np.uint32))
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "same inputs, same bits"
     print(f"  {kname}: max |err| / tol = {worst:.4f}")
