@@ -90,6 +90,9 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #ifndef QMV_FX_SQ  // one 16-byte scale load per lane and pass (see k_fx)
 #define QMV_FX_SQ 1
 #endif
+#ifndef QMV_MQ_SQ  // the same in k_mq
+#define QMV_MQ_SQ 1
+#endif
 #ifndef QMV_FX_TAIL  // 1: no loads past a wavefront's last pass (see k_fx); 0: whole ring turns
 #define QMV_FX_TAIL 1
 #endif
@@ -555,7 +558,10 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
      int32_t M, const int8_t *__restrict__ xq, const float *__restrict__ xd, int32_t r0, int32_t r1, int32_t rw) {
     constexpr int QB = (QT == 8) ? 32 : 16;    // quant bytes per block
     static_assert(D0 >= 0 && D0 <= D - 1, "passes issued before the activation sums");
+    // SQ: a pass's weight scales in one 16-byte load per lane, as in k_fx
+    constexpr bool SQ = QMV_MQ_SQ && NBL >= 2;
     extern __shared__ float s_red[];           // [activation row][wavefront][rw] partial sums
+    __shared__ float s_dq[SQ ? WPB : 1][SQ ? 256 : 1];  // SQ: [row of the pass][block of the slice]
 
     const int nb = K >> 5;
     const int lane = threadIdx.x & 63;
@@ -603,6 +609,8 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
         od[k] = ok ? (i * nb + kb0 + c) * 4 : kOOB;
     }
     const int pq = 4 * nb * QB, pd = 4 * nb * 4;  // bytes per pass
+    // SQ: lane l reads row l / 16 of the pass, blocks 4 (l % 16) .. + 3
+    const int od4 = 4 * (lane % 16) < ns ? ((lane >> 4) * nb + kb0 + 4 * (lane % 16)) * 4 : kOOB;
     auto load = [&](Pass<QT, NBL> &p, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NBL; ++k) {
@@ -610,8 +618,11 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
             p.w[k][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a, 0, kNT));
             if constexpr (QT == 8)
                 p.w[k][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, a + 16, 0, kNT));
-            p.dw[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, b, 0, kNT));
+            if constexpr (!SQ)
+                p.dw[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, b, 0, kNT));
         }
+        if constexpr (SQ)
+            p.dq = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rd, od4 + j * pd, 0, kNT));
     };
     Pass<QT, NBL> ring[D];
 #pragma unroll
@@ -656,10 +667,22 @@ k_mq(float *__restrict__ y, const int8_t *__restrict__ wq, const float *__restri
                 acc[k] = __builtin_amdgcn_mfma_i32_4x4x4i8(a, b, acc[k], 0, 0, 0);
             }
         }
+        float dwk[NBL];
+        if constexpr (SQ) {
+            // lane l's quad goes to floats 4 l .. 4 l + 3 of the slot; lane
+            // (t, i) then reads row i's scale of block t + 16 k (0 past the
+            // slice, as the 4-byte loads' out-of-range offsets give)
+            *reinterpret_cast<v4i *>(&s_dq[wid][4 * lane]) = p.dq;
+#pragma unroll
+            for (int k = 0; k < NBL; ++k) dwk[k] = t + 16 * k < ns ? s_dq[wid][64 * i + t + 16 * k] : 0.0f;
+        } else {
+#pragma unroll
+            for (int k = 0; k < NBL; ++k) dwk[k] = p.dw[k];
+        }
         float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < NBL; ++k) {
-            const int dwi = __float_as_int(p.dw[k]);
+            const int dwi = __float_as_int(dwk[k]);
             // weight scale of row v of the tile: lane 4 t + v's (quad_perm [v, v, v, v])
             const float w0 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x00, 0xF, 0xF, false));
             const float w1 = __int_as_float(__builtin_amdgcn_mov_dpp(dwi, 0x55, 0xF, 0xF, false));
