@@ -837,10 +837,18 @@ hipError_t launch_m_w(const RowsArgs &a, hipStream_t s, const char **name) {
     }
     if (nb <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(4 * W, false), s, name);
     if (nb <= 32) return launch_t<QT, M, AX, 32, 1, ring_depth<QT, M, 1>(), W, false>(a, rows_per(2 * W, false), s, name);
-    // split K: the fused matvec, and pre-quantized Q8_0 weights with 2 .. 4
-    // activation rows (elsewhere the row-streaming kernel is as fast or faster)
-    if constexpr (FX || (QT == 8 && M >= 2)) {
-        if (S <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W>(a, rows_per(4, true), s, name);
+    // split K: the fused matvec; pre-quantized Q8_0 weights with 2 .. 4
+    // activation rows; pre-quantized Q4_0 weights with 2 or 3 rows and
+    // slices of more than 16 blocks (Llama-7B W_down 4096 x 11008: 9.15 ->
+    // 8.33 us at 2 rows, 10.38 -> 9.29 us at 3).  Elsewhere the
+    // row-streaming kernel is as fast or faster (one row; W_up 11008 x 4096
+    // at 1 - 3 rows: 6.63 / 7.1 / 7.74 against 6.8 / 7.25 / 7.98 us).
+    constexpr bool PX4 = !FX && QT == 4 && M >= 2;
+    if constexpr (FX || (QT == 8 && M >= 2) || PX4) {
+        if (S <= 16) {
+            if constexpr (PX4) return hipErrorNotSupported;
+            else return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W>(a, rows_per(4, true), s, name);
+        }
         if (S <= 32) return launch_t<QT, M, AX, 16, 2, ring_depth<QT, M, 2>(), W>(a, rows_per(4, true), s, name);
         if (S <= 48) return launch_t<QT, M, AX, 16, 3, ring_depth<QT, M, 3>(), W>(a, rows_per(4, true), s, name);
         if constexpr (M <= 2) return launch_t<QT, M, AX, 16, 4, ring_depth<QT, M, 4>(), W>(a, rows_per(4, true), s, name);

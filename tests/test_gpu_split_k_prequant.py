@@ -130,13 +130,17 @@ def test_prequant_kernel_choice():
     """Pre-quantized calls: K / 32 <= 32 runs the split-K kernel's
     whole-row mode (M = 1 .. 4); for K / 32 in [64, 512] the matrix-core
     form takes 4 rows of Q4_0 and 3 or 4 rows with slices of more than 48
-    blocks (K / 32 > 384), the dot-product form 2 .. 4 rows of Q8_0, and the
-    row-streaming kernel one row and 2 or 3 rows of Q4_0 (measured as fast
-    or faster there); other K, and more rows, the row-streaming kernel."""
+    blocks (K / 32 > 384), the dot-product form 2 .. 4 rows of Q8_0 and 2 or
+    3 rows of Q4_0 with slices of more than 16 blocks (K / 32 > 128), and
+    the row-streaming kernel one row and 2 or 3 rows of Q4_0 with shorter
+    slices (measured as fast or faster there); other K, and more rows, the
+    row-streaming kernel."""
     announce("split-K pre-quantized kernel choice")
     rng = np.random.default_rng(1900)
     cases = [(4, 1, 32, "px_"), (4, 1, 1024, "px_"), (4, 1, 1056, "rows_"), (4, 1, 2048, "rows_"),
-             (4, 1, 16384, "rows_"), (4, 2, 16384, "rows_"), (4, 3, 12288, "rows_"), (4, 3, 12320, "mq_"),
+             (4, 1, 16384, "rows_"), (4, 2, 16384, "px_"), (4, 3, 12288, "px_"), (4, 3, 12320, "mq_"),
+             (4, 2, 4096, "rows_"), (4, 2, 4128, "px_"), (4, 3, 4096, "rows_"), (4, 3, 11008, "px_"),
+             (4, 1, 11008, "rows_"),
              (4, 4, 2048, "mq_"), (4, 4, 11008, "mq_"), (4, 4, 16384, "mq_"), (4, 4, 16416, "rows_"),
              (4, 4, 896, "px_"), (4, 5, 2048, "rows_"), (4, 8, 4096, "rows_"),
              (8, 1, 2048, "rows_"), (8, 2, 2048, "px_"), (8, 3, 2048, "px_"), (8, 4, 11008, "px_"),

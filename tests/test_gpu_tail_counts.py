@@ -73,10 +73,10 @@ def test_whole_rows_every_tail(qtype, p):
                    what=f"fx whole rows q{qtype} {rows}x{k}")
 
 
-# (qtype, M, K): Q8_0 with 2 and 3 pre-quantized rows (the fused kernel's
-# pre-quantized form; 3 rows of 3 blocks per lane take a ring of 3), Q4_0
+# (qtype, M, K): Q8_0 and Q4_0 with 2 and 3 pre-quantized rows (the fused
+# kernel's pre-quantized form, 3 blocks per lane and a ring of 3), Q4_0
 # with 4 rows (the 4 x 4 matrix-core form)
-PREQ = [(8, 2, 11008), (8, 3, 11008), (4, 4, 4096), (4, 4, 11008)]
+PREQ = [(8, 2, 11008), (8, 3, 11008), (4, 2, 11008), (4, 3, 11008), (4, 4, 4096), (4, 4, 11008)]
 
 
 @pytest.mark.parametrize("qtype,m,k", PREQ)
