@@ -43,6 +43,7 @@
 // RT weight tiles.
 #include <stdio.h>
 
+#include "count.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -51,6 +52,9 @@ namespace {
 
 constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3: raw 32-bit data
 constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor range used here
+#ifndef QMV_MM_CTAIL  // 1: the many-stage form's last stages specialised on their count; 0: tested per stage
+#define QMV_MM_CTAIL 1
+#endif
 constexpr int kNT = 2;                 // non-temporal: weights are read once
 constexpr int KU = 4;                  // blocks per stage
 constexpr int kMinus8 = (int)0xF8F8F8F8;
@@ -314,7 +318,8 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
         // among this wavefront's stages run unguarded (exact wait counts),
         // and the last one or two load and compute only stages that exist
         // (measured: Q4_0 W_down 4096 x 11008 at M = 16, 11 stages,
-        // 14.3 -> 12.9 us)
+        // 14.3 -> 12.9 us), as code specialised on their count, which keeps
+        // those waits exact too (12.9 -> 12.7 us; packed and M = 64 0 - 1.5%)
         int it = 0;
         for (; (it + 2) * D - 2 < nst; ++it) {
 #pragma unroll
@@ -325,6 +330,17 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+#if QMV_MM_CTAIL
+        with_count<1, 2 * D - 2>(nst - it * D, [&](auto rc) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                if (q + D - 1 < R) load(ring[(q + D - 1) % D], it * D + q + D - 1);
+                step(q % D, it * D + q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+#else
         for (; it * D < nst; ++it) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
@@ -336,6 +352,7 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+#endif
     } else {
         // few stages: whole turns (stages past the last load nothing and
         // compute zeros); a guarded tail would be half of the loop here and
