@@ -55,7 +55,7 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #ifndef QMV_MM_CTAIL  // 1: the many-stage form's last stages specialised on their count; 0: tested per stage
 #define QMV_MM_CTAIL 1
 #endif
-#ifndef QMV_MM_PARTPAD  // 1: the partial tiles' LDS rows padded to 65 floats
+#ifndef QMV_MM_PARTPAD  // 1: the partial tiles' LDS layout padded against bank conflicts (see k_mm)
 #define QMV_MM_PARTPAD 1
 #endif
 constexpr int kNT = 2;                 // non-temporal: weights are read once
@@ -376,24 +376,26 @@ k_mm(float *__restrict__ Y, const int8_t *__restrict__ wq, const float *__restri
     // partial tiles of the wavefronts -> LDS (over the staging regions),
     // then a fixed-order sum per output
     __syncthreads();
-    // [wavefront][RT][MT][4][PS]: rows of 64 lanes padded to PS floats, so the
-    // sum below (consecutive threads on consecutive accumulator registers v)
-    // reads distinct banks
-    constexpr int PS = QMV_MM_PARTPAD ? 65 : 64;
+    // [wavefront][RT][MT] blocks of BS floats, each [4][PS]: the rows of 64
+    // lanes padded to 65 floats and each block to 4 * 65 + 1, so the sum
+    // below (consecutive threads on consecutive accumulator registers v, then
+    // on the next weight tile) reads distinct banks: measured bank conflicts
+    // of packed W_up, M = 64, 55% -> 23% -> 9% of LDS-active cycles
+    constexpr int PS = QMV_MM_PARTPAD ? 65 : 64, BS = QMV_MM_PARTPAD ? 4 * 65 + 1 : 4 * 64;
     float *part = reinterpret_cast<float *>(smem);
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) part[(((wid * RT + a) * MT + t) * 4 + v) * PS + lane] = acc[a][t][v];
+            for (int v = 0; v < 4; ++v) part[((wid * RT + a) * MT + t) * BS + v * PS + lane] = acc[a][t][v];
     __syncthreads();
     for (int e = threadIdx.x; e < 16 * RT * 16 * MT; e += 64 * WPB) {
         const int nl = e % (16 * RT), m = e / (16 * RT);  // weight row within the range, activation row
         const int a = nl >> 4, gv = nl & 15, t = m >> 4;
         const int l = 16 * (gv >> 2) + (m & 15), v = gv & 3;
         float s = 0.0f;
-        for (int w = 0; w < WPB; ++w) s += part[(((w * RT + a) * MT + t) * 4 + v) * PS + l];
+        for (int w = 0; w < WPB; ++w) s += part[((w * RT + a) * MT + t) * BS + v * PS + l];
         if (m < M && nl < nrow) Y[(size_t)m * rows + g0 + nl] = s;
     }
 }
@@ -405,7 +407,7 @@ hipError_t launch_cfg_t(const GemmArgs &a, hipStream_t s, const char **name) {
     // gain in flight; four tiles leave no room for a third stage)
     constexpr int WPB = (PK && MT == 1) ? QMV_MM_W1 : 8, D = MT == 1 ? QMV_MM_D1 : MT == 2 ? QMV_MM_D2 : QMV_MM_D4;
     typedef Region<MT, RT, PK> Rg;
-    constexpr int lds_stage = WPB * Rg::BYTES, lds_part = WPB * RT * MT * 4 * (QMV_MM_PARTPAD ? 65 : 64) * 4;
+    constexpr int lds_stage = WPB * Rg::BYTES, lds_part = WPB * RT * MT * (QMV_MM_PARTPAD ? 4 * 65 + 1 : 4 * 64) * 4;
     constexpr int lds = lds_stage > lds_part ? lds_stage : lds_part;
     static_assert(lds <= 160 * 1024, "LDS budget");
     static const std::string kname =
