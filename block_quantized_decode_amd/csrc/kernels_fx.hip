@@ -71,6 +71,9 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 #ifndef QMV_FX_D
 #define QMV_FX_D 4
 #endif
+#ifndef QMV_FX_W2  // 1: one float32 row of Q4_0 with 257 .. 384 blocks on 9 .. 12 wavefronts (launch_m_w)
+#define QMV_FX_W2 1
+#endif
 #ifndef QMV_FX_D3_NBL  // slices of at least this many blocks per lane take a ring of 3
 #define QMV_FX_D3_NBL 2
 #endif
@@ -810,6 +813,31 @@ constexpr int ring_depth() {
     return (NBL >= QMV_FX_D3_NBL || (QT == 8 && M * NBL > 6)) ? 3 : QMV_FX_D;
 }
 
+// One float32 row of Q4_0 with 257 .. 384 blocks: 2 blocks per lane over
+// nb / 32 wavefronts (9 .. 12) instead of 3 over 8, where that leaves at most
+// 5% of the lanes' block slots empty (returns that wavefront count, else 0).
+// A load instruction costs the same whether its lanes read or fall past the
+// slice.  Measured per launch (4096 rows, graphs of launches streaming from
+// HBM, alternating on one box): K = 9216 6.70 - 6.74 -> 6.25 us, 10240
+// 6.90 -> 6.68 - 6.69, 11008 7.58 - 7.62 -> 7.11 - 7.15, 12288 7.51 - 7.56 ->
+// 7.42 - 7.46.  12 wavefronts at K = 11008 (the same 89.6% slot use as 3
+// blocks over 8) were no faster than 8.
+inline int wide_slices(int nb) {
+    const int w2 = (nb + 31) / 32;
+    return (nb > 256 && w2 <= 12 && 20 * nb >= 19 * 32 * w2) ? w2 : 0;
+}
+
+template <int QT, int M, int AX, bool GU>
+hipError_t launch_w2(const RowsArgs &a, int rw, int w2, hipStream_t s, const char **name) {
+    constexpr int D2 = ring_depth<QT, M, 2>();
+    switch (w2) {
+        case 9: return launch_t<QT, M, AX, 16, 2, D2, 9, true, GU>(a, rw, s, name);
+        case 10: return launch_t<QT, M, AX, 16, 2, D2, 10, true, GU>(a, rw, s, name);
+        case 11: return launch_t<QT, M, AX, 16, 2, D2, 11, true, GU>(a, rw, s, name);
+        default: return launch_t<QT, M, AX, 16, 2, D2, 12, true, GU>(a, rw, s, name);
+    }
+}
+
 template <int QT, int M, int AX, int W>
 hipError_t launch_m_w(const RowsArgs &a, hipStream_t s, const char **name) {
     constexpr bool FX = AX != kActQ8;
@@ -828,6 +856,12 @@ hipError_t launch_m_w(const RowsArgs &a, hipStream_t s, const char **name) {
         if constexpr (FX && M == 1) {
             const int want = ((nrows + groups - 1) / groups + 3) / 4 * 4;
             const int rwp = min(rw_cap(M) / 2, want);
+#if QMV_FX_W2
+            if constexpr (QT == 4 && W == 8) {  // the plain product's split, so that y keeps its bits
+                const int w2 = wide_slices(nb);
+                if (w2) return launch_w2<QT, M, AX, true>(a, rwp, w2, s, name);
+            }
+#endif
             if (nb >= 64 && S <= 16) return launch_t<QT, M, AX, 16, 1, ring_depth<QT, M, 1>(), W, true, true>(a, rwp, s, name);
             if (nb >= 64 && S <= 32) return launch_t<QT, M, AX, 16, 2, ring_depth<QT, M, 2>(), W, true, true>(a, rwp, s, name);
             if (nb >= 64 && S <= 48) return launch_t<QT, M, AX, 16, 3, ring_depth<QT, M, 3>(), W, true, true>(a, rwp, s, name);
@@ -844,6 +878,12 @@ hipError_t launch_m_w(const RowsArgs &a, hipStream_t s, const char **name) {
     // row-streaming kernel is as fast or faster (one row; W_up 11008 x 4096
     // at 1 - 3 rows: 6.63 / 7.1 / 7.74 against 6.8 / 7.25 / 7.98 us).
     constexpr bool PX4 = !FX && QT == 4 && M >= 2;
+#if QMV_FX_W2  // more wavefronts of 2 blocks per lane (wide_slices)
+    if constexpr (FX && M == 1 && QT == 4 && W == 8) {
+        const int w2 = wide_slices(nb);
+        if (w2) return launch_w2<QT, M, AX, false>(a, rows_per(4, true), w2, s, name);
+    }
+#endif
     if constexpr (FX || (QT == 8 && M >= 2) || PX4) {
         if (S <= 16) {
             if constexpr (PX4) return hipErrorNotSupported;

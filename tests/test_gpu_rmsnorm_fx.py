@@ -55,7 +55,7 @@ def _run(qtype, wq, wd, x, wn, eps, r0=None, r1=None, y=None):
 # smallest split), 65 (ragged slices, block count not a power of two), 128,
 # 160 (Llama-13B hidden), 344, 512 (the largest)
 SHAPES = [(3, 32), (33, 512), (301, 896), (77, 1024), (5, 2048), (257, 2080), (1031, 4096), (19, 5120),
-          (37, 11008), (130, 16384)]
+          (37, 11008), (45, 9216), (130, 16384)]
 
 
 @pytest.mark.parametrize("qtype", [4, 8])

@@ -60,7 +60,7 @@ def _check_activation(a_ref, qo, do):
 
 
 SHAPES = [(3, 32), (33, 512), (301, 896), (77, 1024), (5, 2048), (257, 2080), (1031, 4096), (64, 5504),
-          (37, 11008), (130, 16384)]
+          (37, 11008), (45, 12288), (130, 16384)]
 
 
 @pytest.mark.parametrize("qtype", [4, 8])

@@ -7,7 +7,7 @@ the turn falls among a wavefront's passes; the remaining R passes (1 .. 2 D
 - 2) run as code specialised on R.  Rows are spread over one workgroup per
 compute unit in whole 4-row passes, so rows = 4 p x (compute units) gives
 every wavefront p passes, and p = 1 .. 7 and 10 reach every R for D = 4
-(R = p up to 6, then 3 and 6); rows 3 short of that leave the last
+(R = p up to 6, then 3 and 6) and for D = 3; rows 3 short of that leave the last
 workgroup a shorter count.  The whole-row form (K / 32 <= 32) takes every
 4th pass of 2-row passes, so there rows = 8 p x (compute units).  Each case
 is compared with the oracle on every output."""
@@ -39,8 +39,15 @@ def _x(rng, k):
     return x
 
 
-@pytest.mark.parametrize("qtype", [4, 8])
-@pytest.mark.parametrize("k", [4096, 11008])
+# Q4_0 with 257 .. 384 blocks per row runs 2 blocks per lane on K / 1024
+# wavefronts where at most 5% of the block slots stay empty (K = 9216,
+# 10240, 11008 and 12288 on 9, 10, 11 and 12), else 3 blocks on 8 (K = 8448)
+FX_Q4_NAME = {4096: "fx_q4_t16_n1_d4_w8", 8448: "fx_q4_t16_n3_d3_w8", 9216: "fx_q4_t16_n2_d3_w9",
+              10240: "fx_q4_t16_n2_d3_w10", 11008: "fx_q4_t16_n2_d3_w11", 12288: "fx_q4_t16_n2_d3_w12"}
+
+
+@pytest.mark.parametrize("qtype,k", [(q, k) for q in (4, 8) for k in (4096, 11008)] +
+                         [(4, k) for k in (8448, 9216, 10240, 12288)])
 @pytest.mark.parametrize("p", PASSES)
 def test_fused_every_tail(qtype, k, p):
     rows = _rows(p, short=3 if p in (2, 5) else 0)
@@ -52,6 +59,8 @@ def test_fused_every_tail(qtype, k, p):
     f = qmv.qmv_matvec_q4_fx if qtype == 4 else qmv.qmv_matvec_q8_fx
     y = host(f(dev(wq), dev(wd), dev(x)))
     assert qmv.last_kernel().startswith("fx_"), qmv.last_kernel()
+    if qtype == 4:
+        assert qmv.last_kernel() == FX_Q4_NAME[k], qmv.last_kernel()
     check_gemm_all(qtype, y.reshape(1, -1), wq, wd, xq.reshape(1, -1), xd.reshape(1, -1),
                    what=f"fx q{qtype} {rows}x{k}")
 
