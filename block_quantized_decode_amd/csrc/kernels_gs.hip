@@ -385,7 +385,7 @@ k_gs(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
     // ring; at most two turns' scales): as code specialised on R, which keeps
     // the waits for the ring exact, where that measured faster (8 wavefronts,
     // and 4-bit zero-point codes); else one or two turns testing each pass.
-    if constexpr (QMV_GS_TAIL && (WPB == 8 || FMT == kGsZp4)) {
+    if constexpr (QMV_GS_TAIL && (WPB >= 8 || FMT == kGsZp4)) {
         with_count<1, 2 * D - 2>(npass - it * D, [&](auto rc) __attribute__((always_inline)) {
             constexpr int R = decltype(rc)::value;
 #pragma unroll
@@ -422,6 +422,9 @@ k_gs(float *__restrict__ y, const uint8_t *__restrict__ wq, const float *__restr
 }
 
 constexpr int kGsWpb = 8;
+#ifndef QMV_GS_W2  // 1: rows of 257 .. 384 units on 9 .. 12 wavefronts of 2 units per lane (gs_form)
+#define QMV_GS_W2 1
+#endif
 constexpr int kGsRwCap = 512;  // rows per workgroup: slice sums [WPB][rw] in LDS
 
 template <int FMT, int NC, int W>
@@ -484,11 +487,24 @@ hipError_t launch_gs_f(float *y, const uint8_t *wq, const float *s0, const float
 // row-streaming kernel); otherwise the row-streaming kernels, which stay
 // ahead with 8 wavefronts on fewer rows and with 4 on more (K-quant
 // 5632 x 2048 4.91 against 5.07 us, Llama-7B W_up 7.3 against 7.9 us).
+//
+// With 8 wavefronts, rows of 257 .. 384 units take 3 units per lane; where
+// nu / 32 wavefronts (9 .. 12) of 2 units per lane leave at most 5% of the
+// slots empty, those are taken instead (a load instruction costs the same
+// whether its lanes read or fall past the slice; the fused Q4_0 matvec
+// measured the same split faster on every such K).
 template <int FMT>
 int gs_form(int K, int nrows, int num_cu, int *S) {
     constexpr int G = FMT == kGsZp4 ? 4 : 8;
     if (nrows >= 16 * num_cu) {
         *S = gs_slice(K, G, kGsWpb);
+#if QMV_GS_W2
+        const int nu = K / 32, w2 = (nu + 31) / 32;
+        if (*S > 32 && w2 >= 9 && w2 <= 12 && 20 * nu >= 19 * 32 * w2 && gs_slice(K, G, w2) == 32) {
+            *S = 32;
+            return w2;
+        }
+#endif
         return *S ? kGsWpb : 0;
     }
     *S = gs_slice(K, G, 4);
@@ -502,6 +518,12 @@ hipError_t launch_gs_zp(const ZpArgs &a, int num_cu, hipStream_t s, const char *
         case 4:
             return launch_gs_f<kGsZp4, 4>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x,
                                           a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+#if QMV_GS_W2
+        case 9: return launch_gs_t<kGsZp4, 2, 9>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case 10: return launch_gs_t<kGsZp4, 2, 10>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case 11: return launch_gs_t<kGsZp4, 2, 11>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case 12: return launch_gs_t<kGsZp4, 2, 12>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+#endif
         case kGsWpb:
             return launch_gs_f<kGsZp4, kGsWpb>(a.y, a.wq, a.wd, nullptr, a.wzp, nullptr, nullptr, 8, a.rows, a.K,
                                                a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
@@ -516,6 +538,12 @@ hipError_t launch_gs_q4k(const Q4kArgs &a, int num_cu, hipStream_t s, const char
         case 4:
             return launch_gs_f<kGsQ4k, 4>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x,
                                           a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+#if QMV_GS_W2
+        case 9: return launch_gs_t<kGsQ4k, 2, 9>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case 10: return launch_gs_t<kGsQ4k, 2, 10>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case 11: return launch_gs_t<kGsQ4k, 2, 11>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+        case 12: return launch_gs_t<kGsQ4k, 2, 12>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x, a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);
+#endif
         case kGsWpb:
             return launch_gs_f<kGsQ4k, kGsWpb>(a.y, a.wq, a.d, a.dmin, nullptr, a.sc, a.mn, 0, a.rows, a.K, a.x,
                                                a.xq_out, a.xd_out, a.r0, a.r1, S, num_cu, s, name);

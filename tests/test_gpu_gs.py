@@ -7,7 +7,8 @@ most 64 units either way).
 The activation codes and scales must equal the oracle's bit for bit and
 every row must be within the oracle's tolerance, as for the row-streaming
 kernels.  The cases cover each units-per-lane count (K = 4096: 1 unit per
-lane and pass, 8192: 2, 12288 and 11008: 3, 16384: 4), with and without
+lane and pass, 8192: 2 on 8 wavefronts, 12288 and 11008: 2 on 12 and 11,
+16384: 4), with and without
 zero points, K-quant super-blocks, row counts that leave a
 ragged last pass and a short last workgroup, row sub-ranges, repeated calls
 (same bits) and unit scales (the exact integer sums).  8-bit zero-point
@@ -49,8 +50,15 @@ def _q4k(w, x, r0=None, r1=None, y=None):
 
 
 def _nc(k, g, w=8):
-    """Units per lane and pass the launcher picks (w wavefronts, 16 lanes a row)."""
-    s = -(-(k // 32 // g) // w) * g
+    """Units per lane and pass the launcher picks (w wavefronts, 16 lanes a row).
+    With 8 wavefronts, rows of 257 .. 384 units whose nu / 32 wavefronts
+    (9 .. 12) hold 2 units per lane with at most 5% of the slots empty take
+    those instead (K = 11008 on 11, 12288 on 12)."""
+    nu = k // 32
+    w2 = -(-nu // 32)
+    if w == 8 and 256 < nu and w2 <= 12 and 20 * nu >= 19 * 32 * w2 and -(-(nu // g) // w2) * g == 32:
+        return 2
+    s = -(-(nu // g) // w) * g
     return -(-s // 16)
 
 

@@ -144,7 +144,7 @@ FULL = [
     (4, 896, 4864, "gs_zp4_n3_d4_w4"), (8, 896, 4864, "zp8_l64_j2_d3_p4_w16"),
     (4, 151936, 896, "zp4_l32_j1_d3_p1_w8"), (8, 151936, 896, "zp8_l64_j1_d3_p1_w8"),
     (4, 11008, 4096, "gs_zp4_n1_d4_w8"), (8, 11008, 4096, "zp8_l64_j4_d2_p1_w16"),
-    (4, 4096, 11008, "gs_zp4_n3_d4_w8"), (8, 4096, 11008, "zp8_l64_j3_d2_p4_w16"),
+    (4, 4096, 11008, "gs_zp4_n2_d4_w11"), (8, 4096, 11008, "zp8_l64_j3_d2_p4_w16"),
     (4, 2048, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 2048, 11008, "zp8_l64_j3_d2_p4_w16"),
     (4, 3001, 11008, "zp4_l64_j2_d2_p4_w16"), (8, 3001, 11008, "zp8_l64_j3_d2_p4_w16"),
     (8, 8192, 16384, "zp8_l64_j8_d2_p1_w16"), (4, 8192, 32768, "zp4_l64_j8_d2_p1_w16"),
