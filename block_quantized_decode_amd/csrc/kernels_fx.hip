@@ -58,7 +58,8 @@ constexpr int kOOB = 0x40000000;       // an offset beyond every descriptor rang
 // Tuning (measured on the Llama-7B FFN shapes): barrier between the
 // activation and weight requests, one pass of weights issued before the
 // quantization, four passes in the ring, one workgroup of 8 wavefronts
-// per compute unit (4 for some shapes of one activation row: launch_m).
+// per compute unit (4 for some shapes of one activation row: launch_m;
+// 9 - 12 for some longer Q4_0 rows: wide_slices).
 #ifndef QMV_FX_XBAR
 #define QMV_FX_XBAR 1
 #endif
